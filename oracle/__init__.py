@@ -1,0 +1,227 @@
+"""The CPU oracle (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s cpu_baseline
+leg may import this package. It wraps ``oracle.c`` (plain C, built with gcc
+``-O2 -ffp-contract=off -fno-fast-math``) through ctypes and numpy; it shares
+no code with the HIP library and never imports it.
+
+Functions take and return numpy arrays in the pages' wire formats (see
+``workloads``). Parity pins: ``tests/test_oracle_*.py``. The C header comment
+of ``oracle.c`` cites the passage each function follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+CFLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC",
+          "-shared", "-std=c11", "-Wall", "-Wextra"]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile oracle.c into liboracle.so (gcc; CPU only)."""
+    tmp = _LIB + ".tmp"
+    cmd = ["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("oracle build failed:\n" + res.stdout + res.stderr)
+    if verbose and res.stderr:
+        print(res.stderr)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        _lib = ctypes.CDLL(_LIB)
+        _declare(_lib)
+    return _lib
+
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_INT = ctypes.c_int
+_F32 = ctypes.c_float
+
+
+def _declare(L):
+    L.gdo_max_threads.restype = _INT
+    L.gdo_f16_to_f32.argtypes = [ctypes.c_uint16]
+    L.gdo_f16_to_f32.restype = _F32
+    L.gdo_q1_q8_gemv_aos.argtypes = [_P, _P, _P, _I64, _I64, _I64, _INT]
+    L.gdo_pack_q1_p1.argtypes = [_P, _I64, _I64, _P, _P]
+    L.gdo_pack_q8_p1.argtypes = [_P, _I64, _I64, _P, _P]
+    L.gdo_q1_q8_gemv_p1packed.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _INT]
+    L.gdo_q1_planes.argtypes = [_P, _I64, _I64, _P, _P]
+    L.gdo_sign_gemm_f64.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _INT]
+    L.gdo_sign_gemm_f32.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _INT]
+    L.gdo_blockq8_f32.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _INT]
+    L.gdo_ternary_dot_direct.argtypes = [_P, _P, _P, _P, _I64, _I64]
+    L.gdo_ternary_gemv.argtypes = [_P, _P, _F32, _P, _F32, _P, _P, _I64, _I64, _INT]
+    for name in ("gdo_q1_q8_gemv_aos", "gdo_pack_q1_p1", "gdo_pack_q8_p1",
+                 "gdo_q1_q8_gemv_p1packed", "gdo_q1_planes", "gdo_sign_gemm_f64",
+                 "gdo_sign_gemm_f32", "gdo_blockq8_f32", "gdo_ternary_dot_direct",
+                 "gdo_ternary_gemv"):
+        getattr(L, name).restype = None
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a, a.ctypes.data
+
+
+def max_threads() -> int:
+    return int(lib().gdo_max_threads())
+
+
+def f16_to_f32(h: int) -> np.float32:
+    return np.float32(lib().gdo_f16_to_f32(int(h) & 0xFFFF))
+
+
+# ----------------------------------------------------------------- Q1_0.q8_0
+
+def q1_q8_gemv_aos(w_aos, a_aos, rows: int, K: int, n_act: int = 1, nthreads: int = 1):
+    """F1: y f32 [n_act, rows] from AoS weight bytes and AoS activation bytes."""
+    w, wp = _c(w_aos, np.uint8)
+    a, ap = _c(a_aos, np.uint8)
+    _check_q1(w, a, rows, K, n_act)
+    y = np.empty((n_act, rows), dtype=np.float32)
+    lib().gdo_q1_q8_gemv_aos(wp, ap, y.ctypes.data, rows, K, n_act, nthreads)
+    return y
+
+
+def pack_q1_p1(w_aos, rows: int, K: int):
+    w, wp = _c(w_aos, np.uint8)
+    nb = K // 128
+    d = np.empty(rows * nb, dtype=np.float32)
+    b = np.empty(rows * nb * 4, dtype=np.uint32)
+    lib().gdo_pack_q1_p1(wp, rows, K, d.ctypes.data, b.ctypes.data)
+    return d, b
+
+
+def pack_q8_p1(a_aos, n_act: int, K: int):
+    a, ap = _c(a_aos, np.uint8)
+    nb8 = K // 32
+    d = np.empty(n_act * nb8, dtype=np.float32)
+    q = np.empty(n_act * nb8 * 8, dtype=np.uint32)
+    lib().gdo_pack_q8_p1(ap, n_act, K, d.ctypes.data, q.ctypes.data)
+    return d, q
+
+
+def q1_q8_gemv_p1packed(w_aos, a_aos, rows: int, K: int, n_act: int = 1, nthreads: int = 1):
+    """F2: P1's packQ1/packQ8 layouts, one chain per (row, lane)."""
+    wd, wb = pack_q1_p1(w_aos, rows, K)
+    ad, aq = pack_q8_p1(a_aos, n_act, K)
+    y = np.empty((n_act, rows), dtype=np.float32)
+    lib().gdo_q1_q8_gemv_p1packed(wd.ctypes.data, wb.ctypes.data, ad.ctypes.data,
+                                  aq.ctypes.data, y.ctypes.data, rows, K, n_act, nthreads)
+    return y
+
+
+def q1_plane_shapes(rows: int, K: int):
+    nb = K // 128
+    nb8 = (nb + 7) // 8 * 8
+    r64 = (rows + 63) // 64 * 64
+    return (r64 * nb * 4,), (r64 * nb8,)
+
+
+def q1_planes(w_aos, rows: int, K: int):
+    """The library's documented Q1 plane layout: (bits u32[...], scales u16[...])."""
+    w, wp = _c(w_aos, np.uint8)
+    bshape, sshape = q1_plane_shapes(rows, K)
+    bits = np.empty(bshape, dtype=np.uint32)
+    scales = np.empty(sshape, dtype=np.uint16)
+    lib().gdo_q1_planes(wp, rows, K, bits.ctypes.data, scales.ctypes.data)
+    return bits, scales
+
+
+def _check_q1(w, a, rows, K, n_act):
+    if K % 128 or rows < 0 or n_act < 1:
+        raise ValueError("bad Q1 shape")
+    if w.size != rows * (K // 128) * 18:
+        raise ValueError("weight bytes do not match rows x K")
+    if a.size != n_act * (K // 32) * 34:
+        raise ValueError("activation bytes do not match n_act x K")
+
+
+# ------------------------------------------------------------ sign-bit GEMM
+
+def sign_gemm_f64(x, bits, scales, nthreads: int = 1):
+    x, xp = _c(x, np.float32)
+    bits, bp = _c(bits, np.uint32)
+    scales, sp = _c(scales, np.float32)
+    M, K = x.shape
+    N = bits.shape[0]
+    if bits.shape != (N, K // 32) or scales.shape != (N, K // 32) or K % 32:
+        raise ValueError("bad sign GEMM shapes")
+    y = np.empty((M, N), dtype=np.float32)
+    lib().gdo_sign_gemm_f64(xp, bp, sp, y.ctypes.data, M, N, K, nthreads)
+    return y
+
+
+def sign_gemm_f32(x, bits, scales, nthreads: int = 1):
+    x, xp = _c(x, np.float32)
+    bits, bp = _c(bits, np.uint32)
+    scales, sp = _c(scales, np.float32)
+    M, K = x.shape
+    N = bits.shape[0]
+    y = np.empty((M, N), dtype=np.float32)
+    lib().gdo_sign_gemm_f32(xp, bp, sp, y.ctypes.data, M, N, K, nthreads)
+    return y
+
+
+# ----------------------------------------------------------- block-Q8 nt
+
+def blockq8_f32(x, quants, scales, nthreads: int = 1):
+    x, xp = _c(x, np.float32)
+    quants, qp = _c(quants, np.uint32)
+    scales, sp = _c(scales, np.float32)
+    m, k = x.shape
+    n = quants.shape[0]
+    if quants.shape != (n, k // 4) or scales.shape != (n, k // 32) or k % 32:
+        raise ValueError("bad block-Q8 shapes")
+    y = np.empty((m, n), dtype=np.float32)
+    lib().gdo_blockq8_f32(xp, qp, sp, y.ctypes.data, m, k, n, nthreads)
+    return y
+
+
+# ------------------------------------------------------------------ ternary
+
+def ternary_dot_direct(P, N, x_q):
+    P, pp = _c(P, np.uint32)
+    N, np_ = _c(N, np.uint32)
+    x, xp = _c(x_q, np.int8)
+    rows, W = P.shape
+    K = W * 32
+    dot = np.empty(rows, dtype=np.int64)
+    lib().gdo_ternary_dot_direct(pp, np_, xp, dot.ctypes.data, rows, K)
+    return dot
+
+
+def ternary_gemv(P, N, w_scale, x_q, x_scale, nthreads: int = 1):
+    """T2 (popcount identity): returns (y f32 [rows], dot int32 [rows])."""
+    P, pp = _c(P, np.uint32)
+    N, np_ = _c(N, np.uint32)
+    x, xp = _c(x_q, np.int8)
+    rows, W = P.shape
+    K = W * 32
+    if N.shape != P.shape or x.size != K:
+        raise ValueError("bad ternary shapes")
+    y = np.empty(rows, dtype=np.float32)
+    dot = np.empty(rows, dtype=np.int32)
+    lib().gdo_ternary_gemv(pp, np_, float(w_scale), xp, float(x_scale), y.ctypes.data,
+                           dot.ctypes.data, rows, K, nthreads)
+    return y, dot

@@ -1,0 +1,404 @@
+/*
+ * oracle.c -- the CPU oracle for the block-quantized weight x activation
+ * products. TEST INFRASTRUCTURE ONLY: it is loaded by tests/, by
+ * __graft_entry__.smoke() and by bench.py's cpu_baseline leg, and by nothing
+ * else. It shares no source, header, table or helper with the HIP library
+ * (gemm_decode_amd/csrc); the two meet only on input bytes.
+ *
+ * Plain, slow, obviously correct: every function is a direct loop nest in the
+ * order the pages state, with no blocking, fusion or reordering. Compiled with
+ * -O2 -ffp-contract=off -fno-fast-math and the default x86-64 SSE rounding
+ * (round to nearest even, no flush-to-zero), so every float operation written
+ * here is exactly one IEEE operation. Threads (OpenMP) only split independent
+ * outputs; each output's arithmetic is the same sequence on any thread count.
+ *
+ * Sources (page title, then section):
+ *   [P1] "browseml-gpu.js" (browseML on the GPU, exactly): header comment
+ *        "The arithmetic, as the reference does it", Q1_DOT_WGSL, Q1_MM_WGSL,
+ *        packQ1, packQ8.
+ *   [P2] "block_q8_matmul_nt.wgsl" (kopitiam-gpu): PACKING, ACCUMULATION
+ *        ORDER, quant_at, main.
+ *   [P3] "BonsaiのWebGPUカーネルを読み解く" (habakan blog): the ternary
+ *        popcount identity in the section on Bonsai; the figure on PrismML's
+ *        decode/prefill kernels (q1_bits / q1_scales, q1_signs4_unit).
+ *   [P4] "web-xpu-ops": "The reference is the point" (f64 reference).
+ *
+ * Parity pins live in tests/test_oracle_*.py; every function below is pinned
+ * by at least one of them (closed forms, integer-exact special cases,
+ * brute force in f64/int64 via numpy, invariants).
+ */
+
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+#include <omp.h>
+
+#define QK1 128
+#define QK8 32
+#define Q1_BYTES 18
+#define Q8_BYTES 34
+
+int gdo_max_threads(void) { return omp_get_max_threads(); }
+
+/* ------------------------------------------------------------------------
+ * f16 -> f32, exactly. [P1] decodes f16 scales with integer operations,
+ * subnormals included: value = (-1)^s * m * 2^-24 for exponent field 0,
+ * (-1)^s * (1024 + m) * 2^(e - 25) for 1 <= e <= 30, and Inf/NaN for e = 31
+ * (NaN keeps the mantissa in the top of the f32 mantissa). Every f16 value is
+ * exactly representable in f32 and ldexp of a small integer is exact.
+ * ------------------------------------------------------------------------ */
+float gdo_f16_to_f32(uint16_t h)
+{
+    uint32_t s = (h >> 15) & 1u, e = (h >> 10) & 0x1fu, m = h & 0x3ffu;
+    float v;
+    if (e == 31u) {
+        uint32_t bits = (s << 31) | 0x7f800000u | (m << 13);
+        memcpy(&v, &bits, 4);
+        return v;
+    }
+    if (e == 0u)
+        v = ldexpf((float)m, -24);
+    else
+        v = ldexpf((float)(1024u + m), (int)e - 25);
+    return s ? -v : v;
+}
+
+/* The int8 negation [P1] uses when a sign bit is 0: two's-complement
+ * wrapping, so -(-128) stays -128 (Q1_DOT_WGSL, "the reference negates as an
+ * i8 (wrapping)"). */
+static int32_t neg_i8_wrapping(int32_t q)
+{
+    return q == -128 ? -128 : -q;
+}
+
+/* ------------------------------------------------------------------------
+ * Q1_0 . q8_0, form F1: walks the array-of-structs bytes like Q1_DOT_WGSL.
+ *
+ * [P1] header comment: per 128 weights a f16 d0 and 128 sign bits; per 32
+ * activations a f16 d1 and 32 int8. For block i and accumulation lane l=0..7:
+ *   s      = sum over e=4l..4l+3 of (bit(32k+e) ? q_e : neg_i8_wrapping(q_e))
+ *   ab[l]  = d1*s            (k = 0)     -- exact in f32 (11 + 10 bits)
+ *   ab[l]  = ab[l] + d1*s    (k = 1..3)  -- one rounding per add
+ *   acc[l] = fma(d0, ab[l], acc[l])      -- correctly rounded fused op
+ * and finally ((a0+a4)+(a2+a6)) + ((a1+a5)+(a3+a7)).
+ * Activation column c's block b is at a + (c*(K/32) + b)*34; output is
+ * y[c*rows + r] (Q1_MM_WGSL's O[col*rows + row]).
+ * ------------------------------------------------------------------------ */
+void gdo_q1_q8_gemv_aos(const uint8_t *w, const uint8_t *a, float *y,
+                        int64_t rows, int64_t K, int64_t n_act, int nthreads)
+{
+    const int64_t nb = K / QK1;
+    const int64_t nb8 = K / QK8;
+    if (nthreads < 1) nthreads = 1;
+#pragma omp parallel for num_threads(nthreads) schedule(static) collapse(2)
+    for (int64_t c = 0; c < n_act; c++) {
+        for (int64_t r = 0; r < rows; r++) {
+            const uint8_t *act = a + c * nb8 * Q8_BYTES;
+            float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            for (int64_t i = 0; i < nb; i++) {
+                const uint8_t *wb = w + (r * nb + i) * Q1_BYTES;
+                float d0 = gdo_f16_to_f32((uint16_t)(wb[0] | (wb[1] << 8)));
+                float ab[8];
+                for (int k = 0; k < 4; k++) {
+                    const uint8_t *ab8 = act + (i * 4 + k) * Q8_BYTES;
+                    float d1 = gdo_f16_to_f32((uint16_t)(ab8[0] | (ab8[1] << 8)));
+                    for (int l = 0; l < 8; l++) {
+                        int32_t s = 0;
+                        for (int e = 4 * l; e < 4 * l + 4; e++) {
+                            int32_t q = (int32_t)(int8_t)ab8[2 + e];
+                            int bit = (wb[2 + k * 4 + e / 8] >> (e % 8)) & 1;
+                            s += bit ? q : neg_i8_wrapping(q);
+                        }
+                        float prod = d1 * (float)s;
+                        ab[l] = (k == 0) ? prod : ab[l] + prod;
+                    }
+                }
+                for (int l = 0; l < 8; l++)
+                    acc[l] = fmaf(d0, ab[l], acc[l]);
+            }
+            float h = ((acc[0] + acc[4]) + (acc[2] + acc[6])) +
+                      ((acc[1] + acc[5]) + (acc[3] + acc[7]));
+            y[c * rows + r] = h;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------
+ * [P1] packQ1: per weight block its scale as f32 (exact) and its 128 bits as
+ * four little-endian u32 taken from bytes 2+4k..5+4k.
+ * ------------------------------------------------------------------------ */
+void gdo_pack_q1_p1(const uint8_t *w, int64_t rows, int64_t K, float *d, uint32_t *b)
+{
+    const int64_t nb = K / QK1;
+    for (int64_t i = 0; i < rows * nb; i++) {
+        const uint8_t *o = w + i * Q1_BYTES;
+        d[i] = gdo_f16_to_f32((uint16_t)(o[0] | (o[1] << 8)));
+        for (int k = 0; k < 4; k++) {
+            const uint8_t *p = o + 2 + 4 * k;
+            b[i * 4 + k] = (uint32_t)p[0] | ((uint32_t)p[1] << 8) |
+                           ((uint32_t)p[2] << 16) | ((uint32_t)p[3] << 24);
+        }
+    }
+}
+
+/* [P1] packQ8: per activation block its scale as f32 and its quants four to
+ * a little-endian u32; column c's block b at index c*(K/32) + b. */
+void gdo_pack_q8_p1(const uint8_t *a, int64_t n_act, int64_t K, float *d, uint32_t *q)
+{
+    const int64_t nb8 = K / QK8;
+    for (int64_t c = 0; c < n_act; c++) {
+        for (int64_t b = 0; b < nb8; b++) {
+            const uint8_t *o = a + (c * nb8 + b) * Q8_BYTES;
+            d[c * nb8 + b] = gdo_f16_to_f32((uint16_t)(o[0] | (o[1] << 8)));
+            for (int w = 0; w < 8; w++) {
+                const uint8_t *p = o + 2 + 4 * w;
+                q[(c * nb8 + b) * 8 + w] = (uint32_t)p[0] | ((uint32_t)p[1] << 8) |
+                                           ((uint32_t)p[2] << 16) | ((uint32_t)p[3] << 24);
+            }
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------
+ * Q1_0 . q8_0, form F2: the same arithmetic on [P1]'s packed layouts, one
+ * chain per (row, lane l) as Q1_MM_WGSL runs it: lane l reads the nibble
+ * (word_k >> 4l) & 0xf and the l-th quant word of each activation block;
+ * the eight chains are then added in the fixed tree. Must equal F1 bit for
+ * bit, which pins the packing and the lane <-> element mapping.
+ * ------------------------------------------------------------------------ */
+void gdo_q1_q8_gemv_p1packed(const float *wd, const uint32_t *wb,
+                             const float *ad, const uint32_t *aq, float *y,
+                             int64_t rows, int64_t K, int64_t n_act, int nthreads)
+{
+    const int64_t nb = K / QK1;
+    if (nthreads < 1) nthreads = 1;
+#pragma omp parallel for num_threads(nthreads) schedule(static) collapse(2)
+    for (int64_t c = 0; c < n_act; c++) {
+        for (int64_t r = 0; r < rows; r++) {
+            float part[8];
+            for (int l = 0; l < 8; l++) {
+                float acc = 0.f;
+                for (int64_t i = 0; i < nb; i++) {
+                    float d0 = wd[r * nb + i];
+                    float ab = 0.f;
+                    for (int k = 0; k < 4; k++) {
+                        int64_t b = i * 4 + k;
+                        float d1 = ad[c * nb * 4 + b];
+                        uint32_t bits = (wb[(r * nb + i) * 4 + k] >> (4 * l)) & 0xfu;
+                        uint32_t qw = aq[(c * nb * 4 + b) * 8 + l];
+                        int32_t s = 0;
+                        for (int j = 0; j < 4; j++) {
+                            int32_t q = (int32_t)(int8_t)(uint8_t)(qw >> (8 * j));
+                            s += ((bits >> j) & 1u) ? q : neg_i8_wrapping(q);
+                        }
+                        float prod = d1 * (float)s;
+                        ab = (k == 0) ? prod : prod + ab;
+                    }
+                    acc = fmaf(d0, ab, acc);
+                }
+                part[l] = acc;
+            }
+            y[c * rows + r] = ((part[0] + part[4]) + (part[2] + part[6])) +
+                              ((part[1] + part[5]) + (part[3] + part[7]));
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------
+ * The library's Q1 plane layout, written from its published definition
+ * (include/gemm_decode.h, "Q1 planes"). Integer byte moves only.
+ *   R64 = rows rounded up to 64, nb = K/128, nb8 = nb rounded up to 8.
+ *   bits  : u32 [R64/64][nb][64][4]; word k of (row r, block i) holds the
+ *           sign bits of elements 32k..32k+31, element 32k+4l+j at bit
+ *           (8*(l%4) + 2 + 4*(l/4) + j) mod 32.
+ *   scales: u16 [R64/64][nb8/8][64][8]; entry (r, i) = the f16 bits of d0.
+ *   Padding rows and padding blocks are zero.
+ * ------------------------------------------------------------------------ */
+void gdo_q1_planes(const uint8_t *w, int64_t rows, int64_t K,
+                   uint32_t *bits, uint16_t *scales)
+{
+    const int64_t nb = K / QK1;
+    const int64_t nb8 = (nb + 7) / 8 * 8;
+    const int64_t R64 = (rows + 63) / 64 * 64;
+    memset(bits, 0, (size_t)(R64 * nb * 4) * sizeof(uint32_t));
+    memset(scales, 0, (size_t)(R64 * nb8) * sizeof(uint16_t));
+    for (int64_t r = 0; r < rows; r++) {
+        int64_t t = r / 64, lane = r % 64;
+        for (int64_t i = 0; i < nb; i++) {
+            const uint8_t *o = w + (r * nb + i) * Q1_BYTES;
+            scales[((t * (nb8 / 8) + i / 8) * 64 + lane) * 8 + (i % 8)] =
+                (uint16_t)(o[0] | (o[1] << 8));
+            for (int k = 0; k < 4; k++) {
+                uint32_t word = 0;
+                for (int l = 0; l < 8; l++) {
+                    for (int j = 0; j < 4; j++) {
+                        int e = 32 * k + 4 * l + j;          /* element in block */
+                        int bit = (o[2 + e / 8] >> (e % 8)) & 1;
+                        int pos = (8 * (l % 4) + 2 + 4 * (l / 4) + j) % 32;
+                        word |= (uint32_t)bit << pos;
+                    }
+                }
+                bits[((t * nb + i) * 64 + lane) * 4 + k] = word;
+            }
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------
+ * Sign-bit GEMM y = x @ w^T, plain definition in f64 ([P4], "The reference is
+ * the point": accumulate in f64). [P3]'s packed format: bit j of u32
+ * bits[n][g] is weight 32g+j of row n, bit 1 -> +1, bit 0 -> -1, and
+ * scales[n][g] multiplies the 32 weights of group g:
+ *   y[m][n] = sum_g scales[n][g] * sum_j x[m][32g+j] * sign(n, 32g+j),
+ * rounded to f32 once.
+ * ------------------------------------------------------------------------ */
+void gdo_sign_gemm_f64(const float *x, const uint32_t *bits, const float *scales,
+                       float *y, int64_t M, int64_t N, int64_t K, int nthreads)
+{
+    const int64_t G = K / 32;
+    if (nthreads < 1) nthreads = 1;
+#pragma omp parallel for num_threads(nthreads) schedule(static) collapse(2)
+    for (int64_t m = 0; m < M; m++) {
+        for (int64_t n = 0; n < N; n++) {
+            double acc = 0.0;
+            for (int64_t g = 0; g < G; g++) {
+                uint32_t word = bits[n * G + g];
+                double sub = 0.0;
+                for (int j = 0; j < 32; j++) {
+                    double xv = (double)x[m * K + 32 * g + j];
+                    sub += ((word >> j) & 1u) ? xv : -xv;
+                }
+                acc += (double)scales[n * G + g] * sub;
+            }
+            y[m * N + n] = (float)acc;
+        }
+    }
+}
+
+/* The same product with f32 arithmetic in group order (sub-total of the 32
+ * signed activations in sequence, then acc = acc + scale*sub): one of the
+ * orders the page's fragments allow, kept to size the tolerance. */
+void gdo_sign_gemm_f32(const float *x, const uint32_t *bits, const float *scales,
+                       float *y, int64_t M, int64_t N, int64_t K, int nthreads)
+{
+    const int64_t G = K / 32;
+    if (nthreads < 1) nthreads = 1;
+#pragma omp parallel for num_threads(nthreads) schedule(static) collapse(2)
+    for (int64_t m = 0; m < M; m++) {
+        for (int64_t n = 0; n < N; n++) {
+            float acc = 0.f;
+            for (int64_t g = 0; g < G; g++) {
+                uint32_t word = bits[n * G + g];
+                float sub = 0.f;
+                for (int j = 0; j < 32; j++) {
+                    float xv = x[m * K + 32 * g + j];
+                    sub = sub + (((word >> j) & 1u) ? xv : -xv);
+                }
+                float t = scales[n * G + g] * sub;
+                acc = acc + t;
+            }
+            y[m * N + n] = acc;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------
+ * Block-Q8 matmul_nt y = x @ w^T, [P2] main in its stated order, in f32 with
+ * every product and add rounded separately (the reading recorded for the
+ * unstated contraction): for each (row, col) acc = 0; per block b of 32,
+ * block_sum = 0; block_sum = block_sum + x*quant for t = 0..31 in order;
+ * acc = acc + scales[col][b]*block_sum. quant_at: byte t%4 of word t/4,
+ * sign-extended ([P2], PACKING).
+ * ------------------------------------------------------------------------ */
+static float quant_at(const uint32_t *quants, int64_t index)
+{
+    uint32_t word = quants[index / 4];
+    uint32_t byte = (word >> ((index % 4) * 8)) & 0xffu;
+    return (float)(int32_t)(int8_t)(uint8_t)byte;
+}
+
+void gdo_blockq8_f32(const float *x, const uint32_t *quants, const float *scales,
+                     float *y, int64_t m, int64_t k, int64_t n, int nthreads)
+{
+    const int64_t bpr = k / 32;
+    if (nthreads < 1) nthreads = 1;
+#pragma omp parallel for num_threads(nthreads) schedule(static) collapse(2)
+    for (int64_t row = 0; row < m; row++) {
+        for (int64_t col = 0; col < n; col++) {
+            float acc = 0.f;
+            for (int64_t b = 0; b < bpr; b++) {
+                float block_sum = 0.f;
+                for (int t = 0; t < 32; t++) {
+                    float p = x[row * k + b * 32 + t] * quant_at(quants, col * k + b * 32 + t);
+                    block_sum = block_sum + p;
+                }
+                float sb = scales[col * bpr + b] * block_sum;
+                acc = acc + sb;
+            }
+            y[row * n + col] = acc;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------
+ * Ternary bitplane GEMV ([P3], section on Bonsai). Weights w in {-1,0,+1} as
+ * P (w=+1) and N (w=-1) planes, u32 [rows][K/32], element 32m+j at bit j.
+ *
+ * T1: the direct integer sum dot = sum_k w_k * x_k (int64), brute force.
+ *
+ * T2: the page's identity, dot = 2(pc(P&X) - pc(N&X)) - pc(P) + pc(N), for a
+ * binary plane X. For int8 x it is applied to the eight bit planes X_b of the
+ * offset-binary code u = x + 128 (u = sum_b 2^b X_b): each plane gives
+ * D_b = sum_k w_k (2 X_bk - 1), so sum_b 2^b D_b = sum_k w_k (2u_k - 255)
+ * = 2 dot + pc(P) - pc(N), i.e. dot = (sum_b 2^b D_b - pc(P) + pc(N)) / 2.
+ * The output is y = (float)dot * s with s = w_scale * x_scale rounded once.
+ * ------------------------------------------------------------------------ */
+void gdo_ternary_dot_direct(const uint32_t *P, const uint32_t *N, const int8_t *x,
+                            int64_t *dot, int64_t rows, int64_t K)
+{
+    const int64_t W = K / 32;
+    for (int64_t r = 0; r < rows; r++) {
+        int64_t acc = 0;
+        for (int64_t kk = 0; kk < K; kk++) {
+            int p = (P[r * W + kk / 32] >> (kk % 32)) & 1;
+            int q = (N[r * W + kk / 32] >> (kk % 32)) & 1;
+            int w = p - q;
+            acc += (int64_t)w * (int64_t)x[kk];
+        }
+        dot[r] = acc;
+    }
+}
+
+void gdo_ternary_gemv(const uint32_t *P, const uint32_t *N, float w_scale,
+                      const int8_t *x, float x_scale, float *y, int32_t *dot32,
+                      int64_t rows, int64_t K, int nthreads)
+{
+    const int64_t W = K / 32;
+    if (nthreads < 1) nthreads = 1;
+    const float s = w_scale * x_scale;
+#pragma omp parallel for num_threads(nthreads) schedule(static)
+    for (int64_t r = 0; r < rows; r++) {
+        int64_t sum = 0;       /* sum_b 2^b D_b */
+        int64_t pcP = 0, pcN = 0;
+        for (int64_t m = 0; m < W; m++) {
+            uint32_t p = P[r * W + m], n = N[r * W + m];
+            pcP += __builtin_popcount(p);
+            pcN += __builtin_popcount(n);
+            for (int b = 0; b < 8; b++) {
+                uint32_t X = 0;
+                for (int j = 0; j < 32; j++) {
+                    uint32_t u = (uint32_t)((int32_t)x[m * 32 + j] + 128);
+                    X |= ((u >> b) & 1u) << j;
+                }
+                int64_t D = 2 * ((int64_t)__builtin_popcount(p & X) -
+                                 (int64_t)__builtin_popcount(n & X)) -
+                            __builtin_popcount(p) + __builtin_popcount(n);
+                sum += D * ((int64_t)1 << b);
+            }
+        }
+        int64_t twice = sum - pcP + pcN;
+        int64_t dot = twice / 2;
+        if (dot32) dot32[r] = (int32_t)dot;
+        y[r] = (float)dot * s;
+    }
+}
