@@ -1,0 +1,207 @@
+// ternary.hip -- ternary bitplane GEMV on gfx950 (page "BonsaiのWebGPU
+// カーネルを読み解く", section on Bonsai: P/N bitplanes and the popcount
+// identity dot = 2(pc(P&X) - pc(N&X)) - pc(P) + pc(N) for a binary plane X).
+//
+// int8 activations enter as their eight two's-complement bit planes B_b
+// (x = sum_{b<7} 2^b B_b - 128 B_7). Per plane the identity's difference
+// pc(P&B) - pc(N&B) equals pc((P&B) | (N&~B)) - pc(N) when P&N = 0, and
+// (P&B) | (N&~B) is one v_bfi_b32; summing c_b = 2^b (b<7), c_7 = -128 over
+// planes (sum c_b = -1) gives
+//     dot = sum_b c_b * pc(bfi(B_b, P, N)) + pc(N),
+// i.e. one bit-select and one popcount-accumulate per plane per 32 weights.
+// An element with P and N both set contributes 0 here, as in w = P - N.
+//
+// Mapping. Eight lanes share a row and split its K range in 16-byte pieces
+// (integer sums are associative, so the split is exact); a wave covers eight
+// rows and reads 128 contiguous bytes of each. The activation planes are
+// copied once per workgroup into LDS, where the eight lanes of a row read
+// eight consecutive 16-byte pieces and the eight rows of a wave read the same
+// addresses (broadcast).
+#include "gd_internal.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kLanesPerRow = 8;
+constexpr int kRowsPerPass = kThreads / kLanesPerRow;   // 32
+constexpr int kPasses = 4;                              // rows per WG = 128
+constexpr int kRowsPerWG = kRowsPerPass * kPasses;
+
+// ------------------------------------------------------------ bit planes
+// One thread per (vector, 32-element word): plane b word m = bit b of the
+// bytes x[32m .. 32m+31], element 32m+j at bit j.
+__global__ void act_bitplanes_kernel(const int8_t *__restrict__ x, uint32_t *__restrict__ planes, int64_t count,
+                                     int64_t W) {
+    const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (gid >= count * W) return;
+    const int64_t v = gid / W, m = gid % W;
+    const uint4 *src = reinterpret_cast<const uint4 *>(x + (v * W + m) * 32);
+    const uint4 lo = src[0], hi = src[1];
+    const uint32_t bytes[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    uint32_t out[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int q = 0; q < 8; q++) {
+#pragma unroll
+        for (int by = 0; by < 4; by++) {
+            const uint32_t val = (bytes[q] >> (8 * by)) & 0xffu;
+            const int j = 4 * q + by;
+#pragma unroll
+            for (int b = 0; b < 8; b++) out[b] |= ((val >> b) & 1u) << j;
+        }
+    }
+    uint32_t *dst = planes + v * 8 * W + m;
+#pragma unroll
+    for (int b = 0; b < 8; b++) dst[b * W] = out[b];
+}
+
+// --------------------------------------------------------------- GEMV
+struct TernArgs {
+    const uint32_t *P, *N, *X;
+    float *y;
+    int32_t *dot;
+    float w_scale, x_scale;
+};
+
+// Per-lane partial counts over words [w0, w0+4): cnt[b] += pc(bfi(B_b, P, N)),
+// cn += pc(N).
+__device__ __forceinline__ void count4(const uint4 &p4, const uint4 &n4, const uint32_t *xl, int64_t W4,
+                                       int64_t w0, uint32_t cnt[8], uint32_t &cn) {
+    const uint32_t p[4] = {p4.x, p4.y, p4.z, p4.w};
+    const uint32_t n[4] = {n4.x, n4.y, n4.z, n4.w};
+#pragma unroll
+    for (int b = 0; b < 8; b++) {
+        const uint4 x4 = *reinterpret_cast<const uint4 *>(xl + b * W4 + w0);
+        const uint32_t xb[4] = {x4.x, x4.y, x4.z, x4.w};
+#pragma unroll
+        for (int q = 0; q < 4; q++) cnt[b] += __builtin_popcount((p[q] & xb[q]) | (n[q] & ~xb[q]));
+    }
+#pragma unroll
+    for (int q = 0; q < 4; q++) cn += __builtin_popcount(n[q]);
+}
+
+__device__ __forceinline__ void ternary_body(const TernArgs &a, uint32_t *xl, int64_t rows, int64_t W) {
+    const int64_t W4 = (W + 3) / 4 * 4;
+    // stage the planes (zero-padded to a multiple of 4 words) into LDS
+    for (int64_t i = threadIdx.x; i < 8 * W4; i += kThreads) {
+        const int64_t b = i / W4, m = i % W4;
+        xl[i] = (m < W) ? a.X[b * W + m] : 0u;
+    }
+    __syncthreads();
+    const int lane = threadIdx.x % kLanesPerRow;
+    const int rsub = threadIdx.x / kLanesPerRow;
+    const bool vec = (W % 4) == 0;
+    for (int pass = 0; pass < kPasses; pass++) {
+        const int64_t r = static_cast<int64_t>(blockIdx.x) * kRowsPerWG + pass * kRowsPerPass + rsub;
+        uint32_t cnt[8] = {0, 0, 0, 0, 0, 0, 0, 0}, cn = 0;
+        if (r < rows) {
+            const uint32_t *Pr = a.P + r * W, *Nr = a.N + r * W;
+            if (vec) {
+                for (int64_t w0 = 4 * lane; w0 < W; w0 += 4 * kLanesPerRow) {
+                    const uint4 p4 = *reinterpret_cast<const uint4 *>(Pr + w0);
+                    const uint4 n4 = *reinterpret_cast<const uint4 *>(Nr + w0);
+                    count4(p4, n4, xl, W4, w0, cnt, cn);
+                }
+            } else {
+                for (int64_t w0 = 4 * lane; w0 < W; w0 += 4 * kLanesPerRow) {
+                    uint32_t pw[4], nw[4];
+                    for (int q = 0; q < 4; q++) {
+                        pw[q] = (w0 + q < W) ? Pr[w0 + q] : 0u;
+                        nw[q] = (w0 + q < W) ? Nr[w0 + q] : 0u;
+                    }
+                    count4(make_uint4(pw[0], pw[1], pw[2], pw[3]), make_uint4(nw[0], nw[1], nw[2], nw[3]), xl, W4,
+                           w0, cnt, cn);
+                }
+            }
+        }
+        int32_t part = static_cast<int32_t>(cn) - 128 * static_cast<int32_t>(cnt[7]);
+#pragma unroll
+        for (int b = 0; b < 7; b++) part += static_cast<int32_t>(cnt[b]) << b;
+        // sum over the 8 lanes of the row (exact integer adds)
+        part += __shfl_xor(part, 1, kLanesPerRow);
+        part += __shfl_xor(part, 2, kLanesPerRow);
+        part += __shfl_xor(part, 4, kLanesPerRow);
+        if (lane == 0 && r < rows) {
+            const float s = a.w_scale * a.x_scale;
+            a.y[r] = static_cast<float>(part) * s;
+            if (a.dot) a.dot[r] = part;
+        }
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void ternary_gemv_kernel(TernArgs a, int64_t rows, int64_t W) {
+    extern __shared__ uint32_t xl[];
+    ternary_body(a, xl, rows, W);
+}
+
+__global__ __launch_bounds__(kThreads) void ternary_gemv_grouped_kernel(const gd_ternary_problem *probs,
+                                                                        int64_t rows, int64_t W) {
+    extern __shared__ uint32_t xl[];
+    const gd_ternary_problem pr = probs[blockIdx.y];
+    TernArgs a{pr.w_pos, pr.w_neg, pr.x_planes, pr.y, pr.dot_out, pr.w_scale, pr.x_scale};
+    ternary_body(a, xl, rows, W);
+}
+
+int check_shape(int64_t rows, int64_t K) {
+    GD_REQUIRE(rows >= 1 && K >= 1, GD_EINVAL, "rows (%lld) and K (%lld) must be >= 1", (long long)rows,
+               (long long)K);
+    GD_REQUIRE(K % 32 == 0, GD_ESHAPE, "K (%lld) must be a multiple of 32", (long long)K);
+    GD_REQUIRE(K <= (INT64_C(1) << 17), GD_ERANGE, "K (%lld) above 2^17 (|dot| must stay below 2^24)",
+               (long long)K);
+    GD_REQUIRE(rows <= INT64_C(1) << 31, GD_ERANGE, "rows (%lld) above 2^31", (long long)rows);
+    return GD_OK;
+}
+
+size_t lds_bytes(int64_t K) { return static_cast<size_t>(8 * ((K / 32 + 3) / 4 * 4) * 4); }
+
+}  // namespace
+
+using namespace gd;
+
+extern "C" int ternary_act_bitplanes(const int8_t *x_q, int64_t count, int64_t K, uint32_t *planes,
+                                     void *stream) {
+    GD_REQUIRE(x_q && planes, GD_EINVAL, "ternary_act_bitplanes: null pointer");
+    GD_REQUIRE(count >= 1 && K >= 1, GD_EINVAL, "ternary_act_bitplanes: count and K must be >= 1");
+    GD_REQUIRE(K % 32 == 0, GD_ESHAPE, "ternary_act_bitplanes: K (%lld) must be a multiple of 32", (long long)K);
+    GD_REQUIRE(count <= 65535 && K <= (INT64_C(1) << 17), GD_ERANGE, "ternary_act_bitplanes: count or K too large");
+    GD_REQUIRE(aligned(x_q, 16) && aligned(planes, 16), GD_EALIGN,
+               "ternary_act_bitplanes: x_q and planes must be 16-byte aligned");
+    const int64_t W = K / 32, n = count * W;
+    hipLaunchKernelGGL(act_bitplanes_kernel, dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256), 0,
+                       as_stream(stream), x_q, planes, count, W);
+    return check_launch("ternary_act_bitplanes");
+}
+
+extern "C" int ternary_gemv(const uint32_t *w_pos, const uint32_t *w_neg, float w_scale, const uint32_t *x_planes,
+                            float x_scale, float *y, int32_t *dot_out, int64_t rows, int64_t K, void *stream) {
+    GD_REQUIRE(w_pos && w_neg && x_planes && y, GD_EINVAL, "ternary_gemv: null pointer");
+    int st = check_shape(rows, K);
+    if (st) return st;
+    GD_REQUIRE(aligned(w_pos, 16) && aligned(w_neg, 16) && aligned(x_planes, 16), GD_EALIGN,
+               "ternary_gemv: w_pos, w_neg and x_planes must be 16-byte aligned");
+    GD_REQUIRE(aligned(y, 4) && aligned(dot_out, 4), GD_EALIGN, "ternary_gemv: y/dot_out must be 4-byte aligned");
+    const int64_t W = K / 32;
+    const size_t lds = lds_bytes(K);
+    GD_REQUIRE(lds <= 64 * 1024, GD_ERANGE, "ternary_gemv: K too large for the LDS plane stage");
+    TernArgs a{w_pos, w_neg, x_planes, y, dot_out, w_scale, x_scale};
+    const int64_t gx = (rows + kRowsPerWG - 1) / kRowsPerWG;
+    hipLaunchKernelGGL(ternary_gemv_kernel, dim3(static_cast<uint32_t>(gx)), dim3(kThreads), lds,
+                       as_stream(stream), a, rows, W);
+    return check_launch("ternary_gemv");
+}
+
+extern "C" int ternary_gemv_grouped(const gd_ternary_problem *problems, int64_t count, int64_t rows, int64_t K,
+                                    void *stream) {
+    GD_REQUIRE(problems, GD_EINVAL, "ternary_gemv_grouped: null problems array");
+    int st = check_shape(rows, K);
+    if (st) return st;
+    GD_REQUIRE(count >= 1, GD_EINVAL, "ternary_gemv_grouped: count (%lld) must be >= 1", (long long)count);
+    GD_REQUIRE(count <= 65535, GD_ERANGE, "ternary_gemv_grouped: count (%lld) above 65535", (long long)count);
+    GD_REQUIRE(aligned(problems, 8), GD_EALIGN, "ternary_gemv_grouped: problems must be 8-byte aligned");
+    const int64_t W = K / 32;
+    const size_t lds = lds_bytes(K);
+    GD_REQUIRE(lds <= 64 * 1024, GD_ERANGE, "ternary_gemv_grouped: K too large for the LDS plane stage");
+    const int64_t gx = (rows + kRowsPerWG - 1) / kRowsPerWG;
+    hipLaunchKernelGGL(ternary_gemv_grouped_kernel, dim3(static_cast<uint32_t>(gx), static_cast<uint32_t>(count)),
+                       dim3(kThreads), lds, as_stream(stream), problems, rows, W);
+    return check_launch("ternary_gemv_grouped");
+}

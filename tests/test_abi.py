@@ -1,0 +1,103 @@
+"""The C ABI on a host without a GPU: the library loads, exports every
+function include/gemm_decode.h declares, and rejects bad arguments with the
+documented status before any HIP call (no compute is launched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gemm_decode.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)) - {"defined"})
+
+
+@pytest.fixture(scope="module")
+def gd():
+    import gemm_decode_amd
+    return gemm_decode_amd
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ["q1_planes_bytes", "q1_repack", "q1_q8_gemv", "q1_q8_gemv_grouped", "q1_sign_gemm",
+              "blockq8_matmul_nt", "ternary_act_bitplanes", "ternary_gemv", "ternary_gemv_grouped",
+              "gemm_decode_status_string", "gemm_decode_last_error", "gemm_decode_abi_version",
+              "gemm_decode_fill", "gemm_decode_stream_read"]:
+        assert n in names, n
+
+
+def test_library_exports_every_declared_symbol(gd):
+    lib = ctypes.CDLL(gd.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    assert lib.gemm_decode_abi_version() == 1
+
+
+def test_status_strings(gd):
+    L = gd.lib()
+    for code, name in [(0, "GD_OK"), (-1, "GD_EINVAL"), (-2, "GD_ESHAPE"), (-3, "GD_EALIGN"),
+                       (-4, "GD_EHIP"), (-5, "GD_ERANGE"), (7, "GD_UNKNOWN")]:
+        assert L.gemm_decode_status_string(code).decode() == name
+
+
+def test_plane_sizes(gd):
+    assert gd.q1_planes_bytes(256, 1024) == (256 * 8 * 16, 256 * 8 * 2)
+    assert gd.q1_planes_bytes(65, 128) == (128 * 16, 128 * 8 * 2)
+    assert gd.q1_planes_bytes(14336, 4096) == (14336 * 32 * 16, 14336 * 32 * 2)
+    with pytest.raises(gd.GemmDecodeError, match="GD_ESHAPE"):
+        gd.q1_planes_bytes(4, 100)
+    with pytest.raises(gd.GemmDecodeError, match="GD_EINVAL"):
+        gd.q1_planes_bytes(0, 128)
+
+
+FAKE = 0x100000   # an aligned address that is never dereferenced: validation fails first
+
+
+def st(fn, *args):
+    return fn(*args)
+
+
+def test_validation_without_gpu(gd):
+    L = gd.lib()
+    E = dict(inval=-1, shape=-2, align=-3, range=-5)
+    # Q1
+    assert L.q1_repack(None, 4, 128, FAKE, FAKE, None) == E["inval"]
+    assert L.q1_repack(FAKE + 1, 4, 128, FAKE, FAKE, None) == E["align"]
+    assert L.q1_repack(FAKE, 4, 100, FAKE, FAKE, None) == E["shape"]
+    assert L.q1_repack(FAKE, 4, 128, FAKE + 8, FAKE, None) == E["align"]
+    assert "16-byte" in L.gemm_decode_last_error().decode()
+    assert L.q1_q8_gemv(FAKE, FAKE, FAKE, FAKE, 0, 128, 1, None) == E["inval"]
+    assert L.q1_q8_gemv(FAKE, FAKE, FAKE, FAKE, 4, 128, 0, None) == E["inval"]
+    assert L.q1_q8_gemv(FAKE, FAKE, FAKE, FAKE, 4, 128, 70000, None) == E["range"]
+    assert L.q1_q8_gemv(FAKE, FAKE, FAKE + 1, FAKE, 4, 128, 1, None) == E["align"]
+    assert L.q1_q8_gemv(FAKE, FAKE, FAKE, FAKE + 2, 4, 128, 1, None) == E["align"]
+    assert L.q1_q8_gemv_grouped(None, 1, 4, 128, None) == E["inval"]
+    assert L.q1_q8_gemv_grouped(FAKE, 0, 4, 128, None) == E["inval"]
+    assert L.q1_q8_gemv_grouped(FAKE, 65536, 4, 128, None) == E["range"]
+    assert L.q1_q8_gemv_grouped(FAKE + 4, 1, 4, 128, None) == E["align"]
+    # sign-bit GEMM
+    assert L.q1_sign_gemm(FAKE, FAKE, FAKE, FAKE, 4, 4, 100, None) == E["shape"]
+    assert L.q1_sign_gemm(None, FAKE, FAKE, FAKE, 4, 4, 128, None) == E["inval"]
+    assert L.q1_sign_gemm(FAKE + 4, FAKE, FAKE, FAKE, 4, 4, 128, None) == E["align"]
+    assert L.q1_sign_gemm(FAKE, FAKE, FAKE, FAKE, 0, 4, 128, None) == E["inval"]
+    # block-Q8
+    assert L.blockq8_matmul_nt(FAKE, FAKE, FAKE, FAKE, 1, 100, 4, None) == E["shape"]
+    assert L.blockq8_matmul_nt(FAKE, FAKE, FAKE, FAKE, 1, 960, 0, None) == E["inval"]
+    assert L.blockq8_matmul_nt(FAKE, FAKE + 4, FAKE, FAKE, 1, 960, 4, None) == E["align"]
+    assert L.blockq8_matmul_nt(FAKE, FAKE, FAKE, FAKE, 65, 960, 4, None) == E["range"]
+    # ternary
+    assert L.ternary_act_bitplanes(FAKE, 1, 100, FAKE, None) == E["shape"]
+    assert L.ternary_act_bitplanes(FAKE, 1, 128, FAKE + 4, None) == E["align"]
+    assert L.ternary_gemv(FAKE, FAKE, 1.0, FAKE, 1.0, FAKE, None, 4, 100, None) == E["shape"]
+    assert L.ternary_gemv(FAKE, None, 1.0, FAKE, 1.0, FAKE, None, 4, 128, None) == E["inval"]
+    assert L.ternary_gemv(FAKE, FAKE, 1.0, FAKE, 1.0, FAKE, None, 4, 1 << 20, None) == E["range"]
+    assert L.ternary_gemv_grouped(FAKE, 0, 4, 128, None) == E["inval"]
+    # measurement
+    assert L.gemm_decode_fill(FAKE, 100, 1, None) == E["shape"]
+    assert L.gemm_decode_stream_read(FAKE, 160, 0, FAKE, 1, None) == E["inval"]

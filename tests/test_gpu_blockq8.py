@@ -1,0 +1,86 @@
+"""GPU parity for block-scaled int8 matmul_nt, through the C ABI.
+
+Bar: max|y_gpu - y_oracle| / ||y_oracle||_inf <= 1e-5, the oracle being the
+page "block_q8_matmul_nt.wgsl" order in f32; plus an integer-exact case that
+must match bit for bit (every f32 step exact in any order).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+TOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def gd():
+    if not torch.cuda.is_available():
+        pytest.fail("a GPU test ran without a visible HIP device")
+    import gemm_decode_amd
+    return gemm_decode_amd
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def run(gd, x, quants, scales):
+    m, k = x.shape
+    n = quants.shape[0]
+    y = torch.full((m * n,), float("nan"), device="cuda")
+    gd.blockq8_matmul_nt(dev(x), dev(quants.view(np.int32)), dev(scales), y, m, k, n)
+    torch.cuda.synchronize()
+    return y.cpu().numpy().reshape(m, n)
+
+
+def rel_err(got, want):
+    return float(np.max(np.abs(got.astype(np.float64) - want)) / np.max(np.abs(want)))
+
+
+@pytest.mark.parametrize("m", [1, 16])
+def test_lm_head_shape_sampled(gd, m):
+    """k=960, n=49152 (the output-projection shape) at full size; the oracle
+    checks a sample of 2048 output features spread over the whole range plus
+    the first and last 64."""
+    cfg = wl.BLOCKQ8_LMHEAD
+    k, n = cfg["k"], cfg["n"]
+    x, quants, scales = wl.blockq8_inputs(m, k, n, cfg["seed"])
+    y = run(gd, x, quants, scales)
+    rng = np.random.default_rng(m)
+    cols = np.unique(np.concatenate([np.arange(64), np.arange(n - 64, n), rng.choice(n, 2048, replace=False)]))
+    want = oracle.blockq8_f32(x, quants[cols], scales[cols], nthreads=8)
+    assert rel_err(y[:, cols], want) <= TOL
+    assert np.all(np.isfinite(y))
+
+
+@pytest.mark.parametrize("m,k,n", [(1, 32, 1), (3, 64, 130), (5, 992, 77), (16, 960, 300), (2, 2048, 257)])
+def test_small_shapes_full(gd, m, k, n):
+    x, quants, scales = wl.blockq8_inputs(m, k, n, seed=m * 1000 + k + n)
+    y = run(gd, x, quants, scales)
+    assert rel_err(y, oracle.blockq8_f32(x, quants, scales)) <= TOL
+
+
+def test_integer_exact_bitwise(gd):
+    m, k, n = 4, 960, 512
+    rng = np.random.default_rng(11)
+    x = rng.integers(-4, 5, size=(m, k)).astype(np.float32)
+    q = rng.integers(-128, 128, size=(n, k)).astype(np.int8)
+    quants = q.view("<u4").reshape(n, k // 4)
+    scales = (2.0 ** rng.integers(-8, -3, size=(n, k // 32))).astype(np.float32)
+    y = run(gd, x, quants, scales)
+    assert np.array_equal(y, oracle.blockq8_f32(x, quants, scales))
+
+
+def test_sign_extension(gd):
+    """Quant bytes 0xFF and 0x80 read as -1 and -128."""
+    k, n = 32, 2
+    q = np.zeros((n, k), dtype=np.uint8)
+    q[0, 3] = 0xFF
+    q[1, 17] = 0x80
+    quants = q.view("<u4").reshape(n, k // 4)
+    x = np.ones((1, k), dtype=np.float32)
+    y = run(gd, x, quants, np.ones((n, 1), dtype=np.float32))
+    assert y.tolist() == [[-1.0, -128.0]]

@@ -1,0 +1,168 @@
+"""GPU parity for the Q1_0 . q8_0 path (repack + GEMV), through the C ABI.
+
+Bar: bit-exact. The planes must equal the oracle's plane writer byte for
+byte; every output's f32 bits must equal the oracle's (form F1, the page
+"browseml-gpu.js" arithmetic). Inputs are seeded and synthetic; -128 quants
+and random f16 exponents come from the page's randomCase generator.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def gd():
+    if not torch.cuda.is_available():
+        pytest.fail("a GPU test ran without a visible HIP device")
+    import gemm_decode_amd
+    return gemm_decode_amd
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def planes_on_gpu(gd, W, rows, K):
+    b, s = gd.q1_alloc_planes(rows, K)
+    b.fill_(0xA5)
+    s.fill_(0x5A)   # the repack must overwrite every byte, padding included
+    gd.q1_repack(dev(W.reshape(-1)), rows, K, b, s)
+    return b, s
+
+
+def run_gemv(gd, W, A, rows, K, n_act=1):
+    b, s = planes_on_gpu(gd, W, rows, K)
+    y = torch.full((n_act * rows,), float("nan"), dtype=torch.float32, device="cuda")
+    gd.q1_q8_gemv(b, s, dev(A.reshape(-1)), y, rows, K, n_act)
+    torch.cuda.synchronize()
+    return y.cpu().numpy().reshape(n_act, rows)
+
+
+def assert_bits_equal(got, want, what=""):
+    g = np.ascontiguousarray(got, dtype=np.float32).view(np.uint32)
+    w = np.ascontiguousarray(want, dtype=np.float32).view(np.uint32)
+    bad = np.flatnonzero(g.reshape(-1) != w.reshape(-1))
+    assert bad.size == 0, (f"{what}: {bad.size} outputs differ; first: "
+                           + ", ".join(f"[{i}] gpu={g.reshape(-1)[i]:#010x} ref={w.reshape(-1)[i]:#010x}"
+                                       for i in bad[:16]))
+
+
+@pytest.mark.parametrize("rows,K", [(1, 128), (63, 256), (65, 1024), (256, 1024), (300, 1152), (1000, 4224)])
+def test_repack_matches_oracle_planes(gd, rows, K):
+    W = wl.q1_weights_aos(rows, K, seed=rows * 7 + K)
+    b, s = planes_on_gpu(gd, W, rows, K)
+    torch.cuda.synchronize()
+    ob, os_ = oracle.q1_planes(W, rows, K)
+    assert np.array_equal(b.cpu().numpy().view(np.uint32), ob)
+    assert np.array_equal(s.cpu().numpy().view(np.uint16), os_)
+
+
+def test_gemv_small_config_bit_exact(gd):
+    """Q1_0.q8_0 GEMV, rows=256, K=1024, batch 1 (the correctness-sized case)."""
+    cfg = wl.Q1_SMALL
+    W = wl.q1_weights_aos(cfg.rows, cfg.K, cfg.weight_seed)
+    A = wl.q8_acts_aos(cfg.K, cfg.act_seeds[0])
+    y = run_gemv(gd, W, A, cfg.rows, cfg.K)
+    assert_bits_equal(y, oracle.q1_q8_gemv_aos(W, A, cfg.rows, cfg.K), "rows=256 K=1024")
+
+
+def test_page_exact_protocol(gd):
+    """The page's exact() protocol: randomCase(256, 2048, seed 1) row by row,
+    then five activations (one partial tile of four) through the multi-column
+    path, each column against its own oracle result."""
+    rows, n = 256, 2048
+    W, A = wl.random_case(rows, n, 1)
+    As = np.concatenate([A] + [wl.random_case(1, n, 100 + k)[1] for k in range(1, 5)])
+    y1 = run_gemv(gd, W, A, rows, n)
+    assert_bits_equal(y1, oracle.q1_q8_gemv_aos(W, A, rows, n), "randomCase single")
+    y5 = run_gemv(gd, W, As, rows, n, n_act=5)
+    assert_bits_equal(y5, oracle.q1_q8_gemv_aos(W, As, rows, n, n_act=5, nthreads=8), "randomCase x5")
+
+
+@pytest.mark.parametrize("rows,K,seed", [(1, 128, 1), (63, 128, 2), (65, 384, 3), (257, 1024, 4),
+                                         (1000, 4224, 5), (130, 8192, 6)])
+def test_ragged_and_chunked_shapes(gd, rows, K, seed):
+    """Rows off the 64/256 tiles, one-block rows (K=128), and K past one LDS
+    table chunk of 32 blocks (K=4224, 8192)."""
+    W, A = wl.random_case(rows, K, seed)
+    y = run_gemv(gd, W, A, rows, K)
+    assert_bits_equal(y, oracle.q1_q8_gemv_aos(W, A, rows, K, nthreads=8), f"rows={rows} K={K}")
+
+
+def test_special_scales_and_bits(gd):
+    """Subnormal, zero and large d0/d1, all-ones and all-zeros sign bits."""
+    rows, K = 128, 1024
+    W, A = wl.random_case(rows, K, 42)
+    W = W.reshape(rows, K // 128, 18).copy()
+    sub = np.array([0x0001, 0x03FF, 0x8001, 0x0000, 0x8000, 0x7BFF, 0x0400], dtype=np.uint16)
+    W[:, :, 0:2] = sub[np.arange(rows * (K // 128)) % sub.size].reshape(rows, K // 128, 1).view(np.uint8)
+    W[0, :, 2:] = 0xFF
+    W[1, :, 2:] = 0x00
+    A = A.reshape(K // 32, 34).copy()
+    A[::3, 0:2] = np.array([0x0001], dtype=np.uint16).view(np.uint8)
+    A[1::5, 0:2] = np.array([0x7800], dtype=np.uint16).view(np.uint8)
+    y = run_gemv(gd, W, A, rows, K)
+    assert_bits_equal(y, oracle.q1_q8_gemv_aos(W, A, rows, K), "special scales")
+
+
+def _decode_set(rows, K, n_vec, seed_w, seeds_a):
+    W = wl.q1_weights_aos(rows, K, seed_w)
+    A = np.concatenate([wl.q8_acts_aos(K, s) for s in seeds_a[:n_vec]])
+    return W, A
+
+
+@pytest.mark.parametrize("idx", [0, 1])
+def test_decode_shapes_grouped_full(gd, idx):
+    """The decode shapes (4096x4096 and 14336x4096, 32 activation vectors),
+    run as one grouped launch of 32 batch-1 problems over distinct plane
+    copies, every output compared with the oracle."""
+    cfg = wl.Q1_DECODE[idx]
+    rows, K, n = cfg.rows, cfg.K, len(cfg.act_seeds)
+    W, A = _decode_set(rows, K, n, cfg.weight_seed, cfg.act_seeds)
+    b, s = planes_on_gpu(gd, W, rows, K)
+    copies = [(b.clone(), s.clone()) for _ in range(n)]
+    a_dev = [dev(A[c]) for c in range(n)]
+    ys = [torch.full((rows,), float("nan"), device="cuda") for _ in range(n)]
+    probs = gd.make_q1_problems([(copies[c][0], copies[c][1], a_dev[c], ys[c]) for c in range(n)])
+    gd.q1_q8_gemv_grouped(probs, n, rows, K)
+    torch.cuda.synchronize()
+    got = np.stack([y.cpu().numpy() for y in ys])
+    want = oracle.q1_q8_gemv_aos(W, A, rows, K, n_act=n, nthreads=oracle.max_threads())
+    assert_bits_equal(got, want, f"decode {rows}x{K} grouped")
+    # the multi-column entry point on the same inputs gives the same bits
+    y = torch.empty(n * rows, device="cuda")
+    gd.q1_q8_gemv(b, s, dev(A.reshape(-1)), y, rows, K, n)
+    torch.cuda.synchronize()
+    assert_bits_equal(y.cpu().numpy().reshape(n, rows), want, "n_act=32")
+
+
+def test_deterministic_repeat(gd):
+    rows, K = 4096, 4096
+    W = wl.q1_weights_aos(rows, K, 1)
+    A = wl.q8_acts_aos(K, 1000)
+    b, s = planes_on_gpu(gd, W, rows, K)
+    a = dev(A.reshape(-1))
+    outs = []
+    for _ in range(3):
+        y = torch.empty(rows, device="cuda")
+        gd.q1_q8_gemv(b, s, a, y, rows, K, 1)
+        torch.cuda.synchronize()
+        outs.append(y.cpu().numpy())
+    assert_bits_equal(outs[1], outs[0], "repeat 1")
+    assert_bits_equal(outs[2], outs[0], "repeat 2")
+
+
+def test_validation_errors_raise(gd):
+    b, s = gd.q1_alloc_planes(64, 128)
+    y = torch.empty(64, device="cuda")
+    a = torch.zeros(4 * 34, dtype=torch.uint8, device="cuda")
+    with pytest.raises(gd.GemmDecodeError, match="GD_ESHAPE"):
+        gd._check(gd.lib().q1_q8_gemv(b.data_ptr(), s.data_ptr(), a.data_ptr(), y.data_ptr(), 64, 100, 1, None))
+    with pytest.raises(gd.GemmDecodeError, match="GD_EALIGN"):
+        gd._check(gd.lib().q1_q8_gemv(b.data_ptr() + 4, s.data_ptr(), a.data_ptr(), y.data_ptr(), 64, 128, 1,
+                                      None))

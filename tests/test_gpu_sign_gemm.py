@@ -1,0 +1,80 @@
+"""GPU parity for the sign-bit prefill GEMM (matrix-core path), via the C ABI.
+
+Bar: max|y_gpu - y_oracle| / ||y_oracle||_inf <= 1e-5 against the f64 oracle
+of the plain definition; an integer-valued case must match bit for bit (hi/lo
+split exact, every f32 accumulation exact), which pins the MFMA tiling.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+TOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def gd():
+    if not torch.cuda.is_available():
+        pytest.fail("a GPU test ran without a visible HIP device")
+    import gemm_decode_amd
+    return gemm_decode_amd
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def run(gd, x, bits, scales):
+    M, K = x.shape
+    N = bits.shape[0]
+    y = torch.full((M * N,), float("nan"), device="cuda")
+    gd.q1_sign_gemm(dev(x), dev(bits.view(np.int32)), dev(scales), y, M, N, K)
+    torch.cuda.synchronize()
+    return y.cpu().numpy().reshape(M, N)
+
+
+def rel_err(got, want):
+    return float(np.max(np.abs(got.astype(np.float64) - want)) / np.max(np.abs(want)))
+
+
+def test_integer_exact_pins_tiling(gd):
+    M, N, K = 144, 160, 256
+    rng = np.random.default_rng(5)
+    x = rng.integers(-8, 9, size=(M, K)).astype(np.float32)
+    bits = rng.integers(0, 2 ** 32, size=(N, K // 32), dtype=np.uint64).astype(np.uint32)
+    scales = (2.0 ** rng.integers(-6, -1, size=(N, K // 32))).astype(np.float32)
+    y = run(gd, x, bits, scales)
+    assert np.array_equal(y, oracle.sign_gemm_f64(x, bits, scales))
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 32), (16, 16, 32), (17, 33, 96), (130, 129, 512), (64, 256, 4096)])
+def test_ragged_shapes(gd, M, N, K):
+    x, bits, scales = wl.sign_gemm_inputs(M, N, K, seed=M + N + K)
+    y = run(gd, x, bits, scales)
+    assert rel_err(y, oracle.sign_gemm_f64(x, bits, scales, nthreads=8)) <= TOL
+
+
+def test_prefill_shape_sampled(gd):
+    """M=512 tokens, N=4096, K=4096 at full size: all 512 rows against the
+    oracle on a sample of 96 output columns (first, last and random)."""
+    cfg = wl.SIGN_PREFILL
+    M, N, K = cfg["M"], cfg["N"], cfg["K"]
+    x, bits, scales = wl.sign_gemm_inputs(M, N, K, cfg["seed"])
+    y = run(gd, x, bits, scales)
+    rng = np.random.default_rng(0)
+    cols = np.unique(np.concatenate([np.arange(16), np.arange(N - 16, N), rng.choice(N, 64, replace=False)]))
+    want = oracle.sign_gemm_f64(x, bits[cols], scales[cols], nthreads=8)
+    assert rel_err(y[:, cols], want) <= TOL
+    assert np.all(np.isfinite(y))
+
+
+def test_all_ones_row_sums(gd):
+    M, N, K = 32, 48, 1024
+    x, _, _ = wl.sign_gemm_inputs(M, N, K, 1)
+    bits = np.full((N, K // 32), 0xFFFFFFFF, dtype=np.uint32)
+    y = run(gd, x, bits, np.ones((N, K // 32), dtype=np.float32))
+    want = x.astype(np.float64).sum(axis=1)
+    assert np.max(np.abs(y - want[:, None])) <= 1e-5 * np.max(np.abs(want))
