@@ -136,13 +136,15 @@ def bench_q1(args, gd, torch):
     # parity spot check (untimed): every output of the first ring slot
     step(0)
     torch.cuda.synchronize()
-    import oracle
-    mism = 0
-    for si, (s, W) in enumerate(zip(shapes, Ws)):
-        got = np.stack([ys[si][c].cpu().numpy() for c in range(n_vec)])
-        want = oracle.q1_q8_gemv_aos(W, A, s.rows, s.K, n_act=n_vec, nthreads=cpu_cores())
-        mism += int((got.view(np.uint32) != want.view(np.uint32)).sum())
-    log(f"[bench] q1: parity vs oracle: {mism} mismatching outputs")
+    mism = None
+    if args.parity:
+        import oracle
+        mism = 0
+        for si, (s, W) in enumerate(zip(shapes, Ws)):
+            got = np.stack([ys[si][c].cpu().numpy() for c in range(n_vec)])
+            want = oracle.q1_q8_gemv_aos(W, A, s.rows, s.K, n_act=n_vec, nthreads=cpu_cores())
+            mism += int((got.view(np.uint32) != want.view(np.uint32)).sum())
+        log(f"[bench] q1: parity vs oracle: {mism} mismatching outputs")
 
     for w in range(args.warmup):
         step(w % ring)
@@ -195,11 +197,12 @@ def bench_q1(args, gd, torch):
                   "us_per_gemv": round(ser_s / (args.serial_steps * 2 * n_vec) * 1e6, 3),
                   "launches": args.serial_steps * 2 * n_vec}
 
-    ceiling = measured_read_ceiling(gd, torch) if args.ceiling else None
+    ceiling = (measured_read_ceiling(gd, torch, gib=args.ceiling_gib, passes=args.ceiling_passes,
+                                     reps=args.ceiling_reps) if args.ceiling else None)
 
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline_q1(Ws[0], A, shapes[0], budget_s=args.cpu_seconds)
+        cpu = cpu_baseline_q1(Ws, A, shapes, budget_s=args.cpu_seconds)
 
     out = {
         "metric": METRIC,
@@ -241,24 +244,28 @@ def bench_q1(args, gd, torch):
     return out
 
 
-def cpu_baseline_q1(W, A, shape, budget_s: float):
-    """The oracle (form F1) on the host: whole batch-1 GEMVs of the 4096x4096
-    weight on successive activation vectors until ~budget_s elapses."""
+def cpu_baseline_q1(Ws, A, shapes, budget_s: float):
+    """The oracle (form F1) on the host, on the same workload: the step's
+    batch-1 GEMVs in order (vector c against each weight shape), cycling until
+    about budget_s of CPU time has been spent."""
     import oracle
     threads = cpu_cores()
     oracle.lib()
-    n_done, t_used = 0, 0.0
-    per = q1_gemv_bytes(shape.rows, shape.K)
-    while t_used < budget_s and n_done < A.shape[0]:
+    done_bytes, t_used, n_gemv = 0, 0.0, 0
+    n_vec = A.shape[0]
+    order = [(c, si) for c in range(n_vec) for si in range(len(shapes))]
+    while t_used < budget_s:
+        c, si = order[n_gemv % len(order)]
+        s = shapes[si]
         t = time.perf_counter()
-        oracle.q1_q8_gemv_aos(W, A[n_done], shape.rows, shape.K, 1, nthreads=threads)
+        oracle.q1_q8_gemv_aos(Ws[si], A[c], s.rows, s.K, 1, nthreads=threads)
         t_used += time.perf_counter() - t
-        n_done += 1
-    return {"value": round(per * n_done / t_used / 1e9, 4), "unit": "GB/s", "cores": threads,
+        done_bytes += q1_gemv_bytes(s.rows, s.K)
+        n_gemv += 1
+    return {"value": round(done_bytes / t_used / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{n_done} batch-1 GEMVs of {shape.rows}x{shape.K} (activation seeds "
-                      f"{shape.act_seeds[0]}..{shape.act_seeds[n_done - 1]}), {t_used:.2f} s, "
-                      f"OpenMP over rows, {cpu_model()}"}
+            "sample": f"{n_gemv} batch-1 GEMVs of the step (vectors x {{4096x4096, 14336x4096}}, in order, "
+                      f"cycling), {t_used:.2f} s of oracle time, OpenMP over rows, {cpu_model()}"}
 
 
 # --------------------------------------------------------------------- main
@@ -274,6 +281,11 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-ceiling", dest="ceiling", action="store_false")
+    ap.add_argument("--ceiling-gib", type=float, default=2.0)
+    ap.add_argument("--ceiling-passes", type=int, default=8)
+    ap.add_argument("--ceiling-reps", type=int, default=5)
+    ap.add_argument("--no-parity", dest="parity", action="store_false",
+                    help="skip the untimed oracle comparison (profiling runs)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:

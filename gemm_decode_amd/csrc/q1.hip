@@ -2,48 +2,64 @@
 // bit-exact batch-1 GEMV (page "browseml-gpu.js": header comment "The
 // arithmetic, as the reference does it", Q1_DOT_WGSL, Q1_MM_WGSL, packQ1).
 //
-// Mapping. One thread owns one weight row and all eight accumulation lanes
-// of that row, so every lane's chain (ab over the four sub-blocks, then the
-// fused acc step per block) and the final tree run in registers in exactly
-// the stated order. A wave is 64 consecutive rows; the Q1 planes store a
-// 64-row tile block-major so one 16-byte load per lane per block is a fully
-// coalesced 1 KiB wave load.
+// Arithmetic. For each row the eight accumulation lanes l = 0..7 run in the
+// stated order: ab_l = T0 + T1 + T2 + T3 over the sub-blocks (T_k the exact
+// product d1_k * s_{k,l}), then acc_l = fma(d0, ab_l, acc_l) per block, and
+// finally ((a0+a4)+(a2+a6)) + ((a1+a5)+(a3+a7)). Every step is one IEEE
+// operation in that order, so the result is bit-exact.
 //
 // Activation staging. The q8_0 vector is shared by every row, so each
 // workgroup turns it into product tables in LDS: for block i, sub-block k
-// and lane l, T[i][k][l][n] = d1_k * s(n), where n is a 4-bit sign group and
-// s(n) the wrapped integer sum of its four quants. |s| <= 512 and d1 has 11
+// and lane l, T[i][k][l][n] = d1_k * s(n), n a 4-bit sign group and s(n) the
+// wrapped integer sum of its four quants. |s| <= 512 and d1 has 11
 // significant bits, so every entry is the exact f32 product the stated
-// arithmetic forms; a row then needs one table read per 4-bit group instead
-// of four selects, three integer adds, a conversion and a multiply. All 64
-// lanes of a wave read the same 16-entry table at a time, so a read touches
-// at most 16 distinct LDS words in 16 distinct banks.
+// arithmetic forms, and a row needs one table read per 4-bit group.
+//
+// Mapping. A 64-row tile is served by two waves: the "low" wave runs lanes
+// 0-3 of all 64 rows, the "high" wave lanes 4-7. Each wave reads its own
+// 8 bytes per row and block (the planes store the two halves apart, so a
+// wave load is 512 contiguous bytes), pulls 16 table offsets out of them
+// with one v_and_b32 (SDWA byte select) each, and reads the tables at
+// immediate LDS offsets. All 64 lanes of a wave read the same 16-entry table
+// per instruction: at most 16 distinct dwords in 16 distinct banks. The two
+// halves meet once per row, through LDS, for the final tree.
 #include "gd_internal.h"
 
 namespace {
 
-constexpr int kRowsPerWG = 256;           // one row per thread
+constexpr int kThreads = 512;             // 8 waves: 4 tiles x 2 halves
+constexpr int kRowsPerWG = 256;
 constexpr int kChunkBlocks = 32;          // blocks whose tables fit in LDS
 constexpr int kTableFloats = kChunkBlocks * 32 * 16;   // 64 KiB
+constexpr int kGroupsPerThread = kChunkBlocks * 32 / kThreads;   // 2
 
-// Exact f16 -> f32 (the hardware conversion is exact for every f16 value,
-// subnormals included, with the default denormal mode).
+// Pointers into device global memory (address space 1), so weight loads are
+// global_load (counted by vmcnt only), not flat loads that also hold lgkmcnt.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef const u32x2 __attribute__((address_space(1))) *gptr_u2;
+typedef const u32x4 __attribute__((address_space(1))) *gptr_u4;
+
+
+// Exact f16 -> f32 (the conversion is exact for every f16 value, subnormals
+// included, under the default denormal mode).
 __device__ __forceinline__ float f16_to_f32(uint16_t h) {
     return static_cast<float>(__builtin_bit_cast(_Float16, h));
 }
 
-// Bit position of element 32k + 4l + j inside word k of the bits plane.
-__host__ __device__ constexpr int plane_bit(int l, int j) {
-    return (8 * (l % 4) + 2 + 4 * (l / 4) + j) % 32;
+// ------------------------------------------------------------------ repack
+// Nibble of lane l in sub-block k of a block, from the page's LSB-first
+// words (element 32k + e at bit e of word k).
+__device__ __forceinline__ uint32_t nib_of(const uint32_t (&in)[4], int k, int l) {
+    return (in[k] >> (4 * l)) & 0xfu;
 }
 
-// ------------------------------------------------------------------ repack
-// One thread per (padded row, block slot). Reads the 18-byte AoS block (nine
-// 16-bit loads), writes its four permuted bit words and its scale; padding
-// rows and padding blocks are written as zero.
+// One thread per (padded row, block slot): reads the 18-byte AoS block (nine
+// 16-bit loads), writes its two 8-byte halves and its scale; padding rows and
+// blocks are written as zero.
 __global__ void q1_repack_kernel(const uint16_t *__restrict__ w_aos, uint32_t *__restrict__ bits,
-                                 uint16_t *__restrict__ scales, int64_t rows, int64_t nb,
-                                 int64_t nb8, int64_t r64) {
+                                 uint16_t *__restrict__ scales, int64_t rows, int64_t nb, int64_t nb8,
+                                 int64_t r64) {
     const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (gid >= r64 * nb8) return;
     const int64_t r = gid / nb8;
@@ -60,149 +76,317 @@ __global__ void q1_repack_kernel(const uint16_t *__restrict__ w_aos, uint32_t *_
     }
     scales[((t * (nb8 / 8) + i / 8) * 64 + lane) * 8 + i % 8] = d0;
     if (i < nb) {
-        uint4 out;
-        uint32_t *ow = reinterpret_cast<uint32_t *>(&out);
-        for (int k = 0; k < 4; k++) {
-            uint32_t word = 0;
-            for (int l = 0; l < 8; l++) {
-                const uint32_t nib = (in[k] >> (4 * l)) & 0xfu;
-                word |= __builtin_amdgcn_alignbit(nib, nib, (32 - plane_bit(l, 0)) % 32);
+        for (int h = 0; h < 2; h++) {
+            uint32_t out[2];
+            for (int m = 0; m < 2; m++) {
+                uint32_t word = 0;
+                for (int jj = 0; jj < 4; jj++)
+                    for (int kk = 0; kk < 2; kk++) {
+                        const uint32_t nib = nib_of(in, 2 * m + kk, 4 * h + jj);
+                        const int pos = (8 * jj + 2 + 4 * kk) % 32;
+                        word |= __builtin_amdgcn_alignbit(nib, nib, (32 - pos) % 32);   // rotate left by pos
+                    }
+                out[m] = word;
             }
-            ow[k] = word;
+            *reinterpret_cast<uint2 *>(bits + (((t * nb + i) * 2 + h) * 64 + lane) * 2) = make_uint2(out[0], out[1]);
         }
-        *reinterpret_cast<uint4 *>(bits + ((t * nb + i) * 64 + lane) * 4) = out;
     }
 }
 
-// -------------------------------------------------------------------- GEMV
+// ------------------------------------------------------------ tables (a2)
+// Group g = (i_local*4 + k)*8 + l of a chunk holds 16 floats. Each thread
+// owns two groups (g = tid + 512j). The build is split so its activation
+// loads can be issued ahead of the weight prefetch (the load counter is in
+// order: waiting for loads issued after the prefetch would drain it).
+struct TableRaw {
+    uint32_t d[kGroupsPerThread], q01[kGroupsPerThread], q23[kGroupsPerThread];
+};
+
+__device__ __forceinline__ void table_loads(TableRaw &raw, const uint16_t *a_generic, int64_t c0, int cb) {
+    // C-style cast: an address-space cast from the generic pointer
+    const auto a = (const uint16_t __attribute__((address_space(1))) *)a_generic;
+    const int ng = cb * 32;
+#pragma unroll
+    for (int j = 0; j < kGroupsPerThread; j++) {
+        int g = threadIdx.x + kThreads * j;
+        g = g < ng ? g : ng - 1;                  // clamped: computed, never stored
+        const int il = g >> 5, k = (g >> 3) & 3, l = g & 7;
+        const auto blk = a + ((c0 + il) * 4 + k) * 17;   // 34 bytes = 17 halves
+        raw.d[j] = blk[0];
+        raw.q01[j] = blk[1 + 2 * l];
+        raw.q23[j] = blk[2 + 2 * l];
+    }
+}
+
+// Entries: T[0] = d1*s(0) and T[n] = T[n without its lowest set bit] +
+// d1*delta(lowest bit). Every partial value is d1 times an integer of
+// magnitude <= 512, so each add is exact and T[n] = d1*s(n) bit for bit.
+__device__ __forceinline__ void table_store(float *tab, const TableRaw &raw, int cb) {
+    const int ng = cb * 32;
+#pragma unroll
+    for (int j = 0; j < kGroupsPerThread; j++) {
+        const int g = threadIdx.x + kThreads * j;
+        const float d1 = f16_to_f32(static_cast<uint16_t>(raw.d[j]));
+        const int32_t q[4] = {static_cast<int8_t>(raw.q01[j] & 0xff), static_cast<int8_t>(raw.q01[j] >> 8),
+                              static_cast<int8_t>(raw.q23[j] & 0xff), static_cast<int8_t>(raw.q23[j] >> 8)};
+        int32_t base = 0;
+        float dlt[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++) {
+            const int32_t neg = (q[jj] == -128) ? -128 : -q[jj];   // int8 wrapping negation
+            base += neg;
+            dlt[jj] = d1 * static_cast<float>(q[jj] - neg);         // exact: |q - neg| <= 255
+        }
+        float v[16];
+        v[0] = d1 * static_cast<float>(base);                        // exact: |base| <= 512
+#pragma unroll
+        for (int n = 1; n < 16; n++) {
+            const int low = __builtin_ctz(n);
+            v[n] = v[n & (n - 1)] + dlt[low];
+        }
+        if (g < ng) {
+            float4 *dst = reinterpret_cast<float4 *>(tab + g * 16);
+#pragma unroll
+            for (int m = 0; m < 4; m++) dst[m] = make_float4(v[4 * m], v[4 * m + 1], v[4 * m + 2], v[4 * m + 3]);
+        }
+    }
+}
+
+// ------------------------------------------------------------------ GEMV
 struct Q1Args {
-    const uint4 *bits;        // bits plane
+    const uint32_t *bits;     // bits plane
     const uint4 *scales;      // scale plane, 8 f16 per 16 bytes
     const uint16_t *a;        // q8_0 AoS activation (one column)
     float *y;                 // output column
 };
 
-// Builds the product tables of blocks [c0, c0 + cb) into `tab`: group
-// g = (i_local*4 + k)*8 + l holds 16 floats. One thread per group per pass.
-__device__ __forceinline__ void build_tables(float *tab, const uint16_t *__restrict__ a,
-                                             int64_t c0, int cb) {
-    for (int g = threadIdx.x; g < cb * 32; g += kRowsPerWG) {
-        const int il = g >> 5, k = (g >> 3) & 3, l = g & 7;
-        const uint16_t *blk = a + ((c0 + il) * 4 + k) * 17;   // 34 bytes = 17 halves
-        const float d1 = f16_to_f32(blk[0]);
-        const uint32_t q01 = blk[1 + 2 * l], q23 = blk[2 + 2 * l];
-        int32_t q[4] = {static_cast<int8_t>(q01 & 0xff), static_cast<int8_t>(q01 >> 8),
-                        static_cast<int8_t>(q23 & 0xff), static_cast<int8_t>(q23 >> 8)};
-        int32_t base = 0, delta[4];
-        for (int j = 0; j < 4; j++) {
-            const int32_t neg = (q[j] == -128) ? -128 : -q[j];   // int8 wrapping negation
-            base += neg;
-            delta[j] = q[j] - neg;
-        }
-        float v[16];
-        for (int n = 0; n < 16; n++) {
-            int32_t s = base;
-            for (int j = 0; j < 4; j++)
-                if ((n >> j) & 1) s += delta[j];
-            v[n] = d1 * static_cast<float>(s);    // exact: |s| <= 512
-        }
-        float4 *dst = reinterpret_cast<float4 *>(tab + g * 16);
-        for (int m = 0; m < 4; m++) dst[m] = make_float4(v[4 * m], v[4 * m + 1], v[4 * m + 2], v[4 * m + 3]);
+// Table offset of the 4-bit group held in byte B of w, pre-shifted by 2:
+// (byte B of w) & 0x3c as one v_and_b32 with an SDWA byte select.
+template <int B>
+__device__ __forceinline__ uint32_t grp(uint32_t w) {
+    static_assert(B >= 0 && B < 4, "byte select");
+    uint32_t r;
+    const uint32_t mask = 0x3cu;
+    if constexpr (B == 0)
+        asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0 src1_sel:DWORD"
+            : "=v"(r) : "v"(w), "v"(mask));
+    else if constexpr (B == 1)
+        asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1 src1_sel:DWORD"
+            : "=v"(r) : "v"(w), "v"(mask));
+    else if constexpr (B == 2)
+        asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2 src1_sel:DWORD"
+            : "=v"(r) : "v"(w), "v"(mask));
+    else
+        asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3 src1_sel:DWORD"
+            : "=v"(r) : "v"(w), "v"(mask));
+    return r;
+}
+
+template <int U>
+__device__ __forceinline__ float d0_half(const u32x4 &s8) {
+    const uint32_t word = (U < 2) ? s8.x : (U < 4) ? s8.y : (U < 6) ? s8.z : s8.w;
+    return f16_to_f32(static_cast<uint16_t>((U & 1) ? (word >> 16) : (word & 0xffffu)));
+}
+
+// The 16 table reads of half H of block U of the chunk: word m covers
+// sub-blocks 2m (bytes' bits 2..5) and 2m+1 (the word rotated by 4); byte jj
+// is lane 4H + jj. Table (U, k, l) starts at byte U*2048 + k*512 + l*64.
+template <int H, int U>
+__device__ __forceinline__ void half_reads(const char *tab, const u32x2 &wb, float (&v)[16]) {
+    const uint32_t wm[2] = {wb.x, wb.y};
+#pragma unroll
+    for (int m = 0; m < 2; m++) {
+        const uint32_t w = wm[m];
+        const uint32_t wr = __builtin_amdgcn_alignbit(w, w, 4);
+        const char *t0 = tab + U * 2048 + (2 * m) * 512 + (4 * H) * 64;
+        const char *t1 = t0 + 512;
+        v[8 * m + 0] = *reinterpret_cast<const float *>(t0 + 0 * 64 + grp<0>(w));
+        v[8 * m + 1] = *reinterpret_cast<const float *>(t0 + 1 * 64 + grp<1>(w));
+        v[8 * m + 2] = *reinterpret_cast<const float *>(t0 + 2 * 64 + grp<2>(w));
+        v[8 * m + 3] = *reinterpret_cast<const float *>(t0 + 3 * 64 + grp<3>(w));
+        v[8 * m + 4] = *reinterpret_cast<const float *>(t1 + 0 * 64 + grp<0>(wr));
+        v[8 * m + 5] = *reinterpret_cast<const float *>(t1 + 1 * 64 + grp<1>(wr));
+        v[8 * m + 6] = *reinterpret_cast<const float *>(t1 + 2 * 64 + grp<2>(wr));
+        v[8 * m + 7] = *reinterpret_cast<const float *>(t1 + 3 * 64 + grp<3>(wr));
     }
 }
 
-// Table entry for the 4-bit group of lane l held in word w (see plane_bit):
-// lanes 0-3 sit at bits 8l+2.., lanes 4-7 at bits 8(l-4)+6.. (mod 32), so the
-// group pre-shifted by 2 is ((w or w rotated right by 4) >> 8(l%4)) & 0x3c.
-template <int L>
-__device__ __forceinline__ float lookup(const char *tabg, uint32_t w, uint32_t w_r4) {
-    const uint32_t src = (L < 4) ? w : w_r4;
-    const uint32_t off = (src >> (8 * (L % 4))) & 0x3cu;
-    return *reinterpret_cast<const float *>(tabg + L * 64 + off);
+// ab_jj = T_{k=0} + T_{k=1} + T_{k=2} + T_{k=3} in order, then the fused step.
+// v[8m + jj] is sub-block 2m, v[8m + 4 + jj] sub-block 2m+1.
+__device__ __forceinline__ void half_math(const float (&v)[16], float d0, float (&acc)[4]) {
+#pragma unroll
+    for (int jj = 0; jj < 4; jj++) {
+        float ab = v[jj];
+        ab = ab + v[4 + jj];
+        ab = ab + v[8 + jj];
+        ab = ab + v[12 + jj];
+        acc[jj] = __builtin_fmaf(d0, ab, acc[jj]);
+    }
 }
 
-__device__ __forceinline__ float d0_of(const uint4 &s8, int idx) {
+// Eight blocks U0..U0+7 of the chunk: table reads of block u+1 are issued
+// before the arithmetic of block u consumes its own.
+template <int H, int U0>
+__device__ __forceinline__ void group8(const char *tab, const u32x2 (&wb)[8], const u32x4 &s8, float (&acc)[4]) {
+    float va[16], vb[16];
+    half_reads<H, U0 + 0>(tab, wb[0], va);
+    half_reads<H, U0 + 1>(tab, wb[1], vb);
+    half_math(va, d0_half<0>(s8), acc);
+    half_reads<H, U0 + 2>(tab, wb[2], va);
+    half_math(vb, d0_half<1>(s8), acc);
+    half_reads<H, U0 + 3>(tab, wb[3], vb);
+    half_math(va, d0_half<2>(s8), acc);
+    half_reads<H, U0 + 4>(tab, wb[4], va);
+    half_math(vb, d0_half<3>(s8), acc);
+    half_reads<H, U0 + 5>(tab, wb[5], vb);
+    half_math(va, d0_half<4>(s8), acc);
+    half_reads<H, U0 + 6>(tab, wb[6], va);
+    half_math(vb, d0_half<5>(s8), acc);
+    half_reads<H, U0 + 7>(tab, wb[7], vb);
+    half_math(va, d0_half<6>(s8), acc);
+    half_math(vb, d0_half<7>(s8), acc);
+}
+
+struct RowPtrs {
+    gptr_u2 bits;          // this wave's half of block 0 of this row; + i*128 per block
+    gptr_u4 sc;            // scales of blocks 0..7 of this row; + (i/8)*64
+};
+
+__device__ __forceinline__ void load_group(const RowPtrs &rp, int64_t g, u32x2 (&wb)[8], u32x4 &s8) {
+#pragma unroll
+    for (int u = 0; u < 8; u++) wb[u] = rp.bits[(8 * g + u) * 128];
+    s8 = rp.sc[g * 64];
+}
+
+// One chunk of up to 32 blocks starting at group g0 (n4 full groups), with
+// the chunk's tables built in LDS. Straight-line code: three register
+// buffers, each group's loads issued two groups before it is consumed
+// (group indices clamped to the last full group, so every load is issued).
+template <int H>
+__device__ __forceinline__ void chunk(float *tab, const Q1Args &p, const RowPtrs &rp, int64_t g0, int64_t n4,
+                                      int64_t ng, int64_t nb, float (&acc)[4]) {
+    const char *tabc = reinterpret_cast<const char *>(tab);
+    const int64_t gl = ng - 1;
+    const int64_t i0 = 8 * g0;
+    const int cb = static_cast<int>((nb - i0) < kChunkBlocks ? (nb - i0) : kChunkBlocks);
+    TableRaw raw;
+    table_loads(raw, p.a, i0, cb);
+    asm volatile("" ::: "memory");   // keep the table loads ahead of the prefetch
+    u32x2 w0[8], w1[8], w2[8];
+    u32x4 s0, s1, s2;
+    load_group(rp, g0, w0, s0);
+    load_group(rp, (g0 + 1 < gl) ? g0 + 1 : gl, w1, s1);
+    load_group(rp, (g0 + 2 < gl) ? g0 + 2 : gl, w2, s2);
+    if (g0 > 0) __syncthreads();
+    table_store(tab, raw, cb);
+    __syncthreads();
+    group8<H, 0>(tabc, w0, s0, acc);
+    load_group(rp, (g0 + 3 < gl) ? g0 + 3 : gl, w0, s0);
+    if (n4 > 1) group8<H, 8>(tabc, w1, s1, acc);
+    if (n4 > 2) group8<H, 16>(tabc, w2, s2, acc);
+    if (n4 > 3) group8<H, 24>(tabc, w0, s0, acc);
+}
+
+// One block of half H at a run-time position (tail blocks past the last full
+// group of eight): same reads, same arithmetic, run-time table offsets.
+template <int H>
+__device__ __forceinline__ void tail_block(const char *tabb, const u32x2 &wb, float d0, float (&acc)[4]) {
+    const uint32_t wm[2] = {wb.x, wb.y};
+    float v[16];
+#pragma unroll
+    for (int m = 0; m < 2; m++) {
+        const uint32_t w = wm[m];
+        const uint32_t wr = __builtin_amdgcn_alignbit(w, w, 4);
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++) {
+            const char *t0 = tabb + (2 * m) * 512 + (4 * H + jj) * 64;
+            v[8 * m + jj] = *reinterpret_cast<const float *>(t0 + ((w >> (8 * jj)) & 0x3cu));
+            v[8 * m + 4 + jj] = *reinterpret_cast<const float *>(t0 + 512 + ((wr >> (8 * jj)) & 0x3cu));
+        }
+    }
+    half_math(v, d0, acc);
+}
+
+__device__ __forceinline__ float d0_of(const u32x4 &s8, int idx) {
     const uint32_t word = (idx < 2) ? s8.x : (idx < 4) ? s8.y : (idx < 6) ? s8.z : s8.w;
-    const uint16_t h = (idx & 1) ? static_cast<uint16_t>(word >> 16) : static_cast<uint16_t>(word & 0xffff);
-    return f16_to_f32(h);
+    return f16_to_f32(static_cast<uint16_t>((idx & 1) ? (word >> 16) : (word & 0xffffu)));
 }
 
-__device__ __forceinline__ void q1_gemv_body(const Q1Args &p, float *tab, int64_t rows, int64_t nb,
-                                             int64_t nb8) {
-    const int64_t r = static_cast<int64_t>(blockIdx.x) * kRowsPerWG + threadIdx.x;
-    const int64_t r64 = (rows + 63) / 64 * 64;
-    const bool live = r < r64;
-    const int64_t t = r / 64, lane = r % 64;
-    const uint4 *bits_row = p.bits + t * nb * 64 + lane;           // + i*64 per block
-    const uint4 *sc_row = p.scales + t * (nb8 / 8) * 64 + lane;     // + (i/8)*64
-
-    float acc[8];
-#pragma unroll
-    for (int l = 0; l < 8; l++) acc[l] = 0.0f;
-
-    for (int64_t c0 = 0; c0 < nb; c0 += kChunkBlocks) {
-        const int cb = static_cast<int>((nb - c0) < kChunkBlocks ? (nb - c0) : kChunkBlocks);
-        if (c0 > 0) __syncthreads();
-        build_tables(tab, p.a, c0, cb);
-        __syncthreads();
-        if (live) {
-            uint4 s8 = make_uint4(0, 0, 0, 0);
-            for (int il = 0; il < cb; il++) {
-                const int64_t i = c0 + il;
-                if ((i & 7) == 0 || il == 0) s8 = sc_row[(i >> 3) * 64];
-                const float d0 = d0_of(s8, static_cast<int>(i & 7));
-                const uint4 wb = bits_row[i * 64];
-                const uint32_t wk[4] = {wb.x, wb.y, wb.z, wb.w};
-                float ab[8];
-#pragma unroll
-                for (int k = 0; k < 4; k++) {
-                    const char *tabg = reinterpret_cast<const char *>(tab) + ((il * 4 + k) * 8) * 64;
-                    const uint32_t w = wk[k];
-                    const uint32_t w_r4 = __builtin_amdgcn_alignbit(w, w, 4);
-                    float v[8];
-                    v[0] = lookup<0>(tabg, w, w_r4);
-                    v[1] = lookup<1>(tabg, w, w_r4);
-                    v[2] = lookup<2>(tabg, w, w_r4);
-                    v[3] = lookup<3>(tabg, w, w_r4);
-                    v[4] = lookup<4>(tabg, w, w_r4);
-                    v[5] = lookup<5>(tabg, w, w_r4);
-                    v[6] = lookup<6>(tabg, w, w_r4);
-                    v[7] = lookup<7>(tabg, w, w_r4);
-#pragma unroll
-                    for (int l = 0; l < 8; l++) ab[l] = (k == 0) ? v[l] : ab[l] + v[l];
-                }
-#pragma unroll
-                for (int l = 0; l < 8; l++) acc[l] = __builtin_fmaf(d0, ab[l], acc[l]);
-            }
+template <int H>
+__device__ __forceinline__ void half_row(float *tab, const Q1Args &p, const RowPtrs &rp, int64_t nb, float (&acc)[4]) {
+    const int64_t ng = nb / 8;
+    constexpr int kGroupsPerChunk = kChunkBlocks / 8;
+    for (int64_t g0 = 0; g0 < ng; g0 += kGroupsPerChunk) {
+        const int64_t n4 = (ng - g0) < kGroupsPerChunk ? (ng - g0) : kGroupsPerChunk;
+        chunk<H>(tab, p, rp, g0, n4, ng, nb, acc);
+    }
+    const int64_t it0 = ng * 8;
+    if (it0 < nb) {   // tail: the last nb % 8 blocks
+        const int64_t c0 = it0 / kChunkBlocks * kChunkBlocks;
+        if (it0 % kChunkBlocks == 0) {
+            if (ng > 0) __syncthreads();
+            TableRaw raw;
+            table_loads(raw, p.a, it0, static_cast<int>(nb - it0));
+            table_store(tab, raw, static_cast<int>(nb - it0));
+            __syncthreads();
+        }
+        const u32x4 s8 = rp.sc[(it0 >> 3) * 64];
+        const char *tabc = reinterpret_cast<const char *>(tab);
+        for (int64_t i = it0; i < nb; i++) {
+            const u32x2 wbv = rp.bits[i * 128];
+            tail_block<H>(tabc + (i - c0) * 2048, wbv, d0_of(s8, static_cast<int>(i & 7)), acc);
         }
     }
-    if (r < rows)
-        p.y[r] = ((acc[0] + acc[4]) + (acc[2] + acc[6])) + ((acc[1] + acc[5]) + (acc[3] + acc[7]));
 }
 
-__global__ __launch_bounds__(kRowsPerWG) void q1_gemv_kernel(const uint4 *bits, const uint4 *scales,
-                                                             const uint16_t *a, float *y, int64_t rows,
-                                                             int64_t nb, int64_t nb8) {
+__device__ __forceinline__ void q1_gemv_body(const Q1Args &p, float *tab, int64_t rows, int64_t nb, int64_t nb8) {
+    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+    const int tl = wave >> 1, h = wave & 1;
+    const int64_t r = static_cast<int64_t>(blockIdx.x) * kRowsPerWG + tl * 64 + lane;
+    const int64_t r64 = (rows + 63) / 64 * 64;
+    // Rows past the padded rows read the last padded row (never stored), so
+    // every thread runs the same loads and barriers.
+    const int64_t rl = r < r64 ? r : r64 - 1;
+    const int64_t t = rl / 64, ln = rl % 64;
+    RowPtrs rp{(gptr_u2)p.bits + ((t * nb) * 2 + h) * 64 + ln, (gptr_u4)p.scales + t * (nb8 / 8) * 64 + ln};
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (h == 0)
+        half_row<0>(tab, p, rp, nb, acc);
+    else
+        half_row<1>(tab, p, rp, nb, acc);
+    // The high half hands lanes 4..7 to the low half through LDS.
+    __syncthreads();
+    float4 *xch = reinterpret_cast<float4 *>(tab) + tl * 64 + lane;
+    if (h == 1) *xch = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    __syncthreads();
+    if (h == 0 && r < rows) {
+        const float4 hi = *xch;
+        p.y[r] = ((acc[0] + hi.x) + (acc[2] + hi.z)) + ((acc[1] + hi.y) + (acc[3] + hi.w));
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void q1_gemv_kernel(const uint32_t *bits, const uint4 *scales,
+                                                           const uint16_t *a, float *y, int64_t rows, int64_t nb,
+                                                           int64_t nb8) {
     __shared__ float tab[kTableFloats];
     const int64_t c = blockIdx.y;   // activation column
     Q1Args p{bits, scales, a + c * (nb * 4) * 17, y + c * rows};
     q1_gemv_body(p, tab, rows, nb, nb8);
 }
 
-__global__ __launch_bounds__(kRowsPerWG) void q1_gemv_grouped_kernel(const gd_q1_problem *probs,
-                                                                     int64_t rows, int64_t nb,
-                                                                     int64_t nb8) {
+__global__ __launch_bounds__(kThreads) void q1_gemv_grouped_kernel(const gd_q1_problem *probs, int64_t rows,
+                                                                   int64_t nb, int64_t nb8) {
     __shared__ float tab[kTableFloats];
     const gd_q1_problem pr = probs[blockIdx.y];
-    Q1Args p{static_cast<const uint4 *>(pr.bits_plane), static_cast<const uint4 *>(pr.scale_plane),
+    Q1Args p{static_cast<const uint32_t *>(pr.bits_plane), static_cast<const uint4 *>(pr.scale_plane),
              static_cast<const uint16_t *>(pr.a_q8), pr.y};
     q1_gemv_body(p, tab, rows, nb, nb8);
 }
 
 // ------------------------------------------------------------ validation
 int plane_sizes(int64_t rows, int64_t K, int64_t *bits_bytes, int64_t *scale_bytes) {
-    GD_REQUIRE(rows >= 1 && K >= 1, GD_EINVAL, "rows (%lld) and K (%lld) must be >= 1",
-               (long long)rows, (long long)K);
+    GD_REQUIRE(rows >= 1 && K >= 1, GD_EINVAL, "rows (%lld) and K (%lld) must be >= 1", (long long)rows,
+               (long long)K);
     GD_REQUIRE(K % 128 == 0, GD_ESHAPE, "K (%lld) must be a multiple of 128", (long long)K);
     GD_REQUIRE(rows <= INT64_C(2147483584), GD_ERANGE, "rows (%lld) above 2^31 - 64", (long long)rows);
     const int64_t nb = K / 128, nb8 = (nb + 7) / 8 * 8, r64 = (rows + 63) / 64 * 64;
@@ -247,8 +431,8 @@ extern "C" int q1_repack(const void *w_aos, int64_t rows, int64_t K, void *bits_
     return check_launch("q1_repack");
 }
 
-extern "C" int q1_q8_gemv(const void *bits_plane, const void *scale_plane, const void *a_q8, float *y,
-                          int64_t rows, int64_t K, int64_t n_act, void *stream) {
+extern "C" int q1_q8_gemv(const void *bits_plane, const void *scale_plane, const void *a_q8, float *y, int64_t rows,
+                          int64_t K, int64_t n_act, void *stream) {
     GD_REQUIRE(bits_plane && scale_plane && a_q8 && y, GD_EINVAL, "q1_q8_gemv: null pointer");
     int64_t b, s;
     int st = plane_sizes(rows, K, &b, &s);
@@ -262,9 +446,9 @@ extern "C" int q1_q8_gemv(const void *bits_plane, const void *scale_plane, const
     const int64_t nb = K / 128, nb8 = (nb + 7) / 8 * 8;
     const int64_t gx = (rows + kRowsPerWG - 1) / kRowsPerWG;
     hipLaunchKernelGGL(q1_gemv_kernel, dim3(static_cast<uint32_t>(gx), static_cast<uint32_t>(n_act)),
-                       dim3(kRowsPerWG), 0, as_stream(stream), static_cast<const uint4 *>(bits_plane),
-                       static_cast<const uint4 *>(scale_plane), static_cast<const uint16_t *>(a_q8), y, rows,
-                       nb, nb8);
+                       dim3(kThreads), 0, as_stream(stream), static_cast<const uint32_t *>(bits_plane),
+                       static_cast<const uint4 *>(scale_plane), static_cast<const uint16_t *>(a_q8), y, rows, nb,
+                       nb8);
     return check_launch("q1_q8_gemv");
 }
 
@@ -280,6 +464,6 @@ extern "C" int q1_q8_gemv_grouped(const gd_q1_problem *problems, int64_t count, 
     const int64_t nb = K / 128, nb8 = (nb + 7) / 8 * 8;
     const int64_t gx = (rows + kRowsPerWG - 1) / kRowsPerWG;
     hipLaunchKernelGGL(q1_gemv_grouped_kernel, dim3(static_cast<uint32_t>(gx), static_cast<uint32_t>(count)),
-                       dim3(kRowsPerWG), 0, as_stream(stream), problems, rows, nb, nb8);
+                       dim3(kThreads), 0, as_stream(stream), problems, rows, nb, nb8);
     return check_launch("q1_q8_gemv_grouped");
 }

@@ -82,10 +82,12 @@ int gemm_decode_abi_version(void);
  * reason). With R64 = rows rounded up to 64, nb = K/128 and nb8 = nb rounded
  * up to 8:
  *  - bits plane, R64*nb*16 bytes, 16-byte aligned: u32 index
- *    ((r/64)*nb + i)*256 + (r%64)*4 + k holds the sign bits of elements
- *    32k..32k+31 of block i of row r; element 32k + 4l + j (l = 0..7,
- *    j = 0..3) sits at bit (8*(l%4) + 2 + 4*(l/4) + j) mod 32. (Each 4-bit
- *    group, pre-shifted by 2, indexes a 16-entry table of 4-byte products.)
+ *    ((((r/64)*nb + i)*2 + h)*64 + r%64)*2 + m holds, for half h (lanes
+ *    4h..4h+3) and word m (sub-blocks 2m, 2m+1) of block i of row r, the sign
+ *    bits of elements 32k + 4l + j with l = 4h + jj (jj = 0..3),
+ *    k = 2m + kk (kk = 0..1), j = 0..3, at bit (8*jj + 2 + 4*kk + j) mod 32.
+ *    (Each 4-bit group, pre-shifted by 2, indexes a 16-entry table of 4-byte
+ *    products; the two halves are read by two different waves.)
  *  - scale plane, R64*nb8*2 bytes, 16-byte aligned: u16 index
  *    ((r/64)*(nb8/8) + i/8)*512 + (r%64)*8 + i%8 holds the f16 bits of d0
  *    of block i of row r.

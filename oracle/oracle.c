@@ -208,9 +208,10 @@ void gdo_q1_q8_gemv_p1packed(const float *wd, const uint32_t *wb,
  * The library's Q1 plane layout, written from its published definition
  * (include/gemm_decode.h, "Q1 planes"). Integer byte moves only.
  *   R64 = rows rounded up to 64, nb = K/128, nb8 = nb rounded up to 8.
- *   bits  : u32 [R64/64][nb][64][4]; word k of (row r, block i) holds the
- *           sign bits of elements 32k..32k+31, element 32k+4l+j at bit
- *           (8*(l%4) + 2 + 4*(l/4) + j) mod 32.
+ *   bits  : u32 [R64/64][nb][2 halves][64][2]; word m of half h of
+ *           (row r, block i) holds the sign bits of elements 32k + 4l + j
+ *           with l = 4h + jj (jj = 0..3), k = 2m + kk (kk = 0..1), j = 0..3,
+ *           at bit (8*jj + 2 + 4*kk + j) mod 32.
  *   scales: u16 [R64/64][nb8/8][64][8]; entry (r, i) = the f16 bits of d0.
  *   Padding rows and padding blocks are zero.
  * ------------------------------------------------------------------------ */
@@ -228,17 +229,21 @@ void gdo_q1_planes(const uint8_t *w, int64_t rows, int64_t K,
             const uint8_t *o = w + (r * nb + i) * Q1_BYTES;
             scales[((t * (nb8 / 8) + i / 8) * 64 + lane) * 8 + (i % 8)] =
                 (uint16_t)(o[0] | (o[1] << 8));
-            for (int k = 0; k < 4; k++) {
-                uint32_t word = 0;
-                for (int l = 0; l < 8; l++) {
-                    for (int j = 0; j < 4; j++) {
-                        int e = 32 * k + 4 * l + j;          /* element in block */
-                        int bit = (o[2 + e / 8] >> (e % 8)) & 1;
-                        int pos = (8 * (l % 4) + 2 + 4 * (l / 4) + j) % 32;
-                        word |= (uint32_t)bit << pos;
+            for (int h = 0; h < 2; h++) {
+                for (int m = 0; m < 2; m++) {
+                    uint32_t word = 0;
+                    for (int jj = 0; jj < 4; jj++) {
+                        for (int kk = 0; kk < 2; kk++) {
+                            for (int j = 0; j < 4; j++) {
+                                int e = 32 * (2 * m + kk) + 4 * (4 * h + jj) + j;
+                                int bit = (o[2 + e / 8] >> (e % 8)) & 1;
+                                int pos = (8 * jj + 2 + 4 * kk + j) % 32;
+                                word |= (uint32_t)bit << pos;
+                            }
+                        }
                     }
+                    bits[(((t * nb + i) * 2 + h) * 64 + lane) * 2 + m] = word;
                 }
-                bits[((t * nb + i) * 64 + lane) * 4 + k] = word;
             }
         }
     }

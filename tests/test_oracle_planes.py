@@ -13,8 +13,10 @@ import workloads as wl
 
 
 def declared_pos(e):
+    """(u32 index within the block for row 0, bit) of element e of a block."""
     k, l, j = e // 32, (e % 32) // 4, e % 4
-    return k, (8 * (l % 4) + 2 + 4 * (l // 4) + j) % 32
+    h, jj, m, kk = l // 4, l % 4, k // 2, k % 2
+    return h * 128 + m, (8 * jj + 2 + 4 * kk + j) % 32
 
 
 def test_each_element_lands_at_declared_bit(orc):
@@ -24,9 +26,9 @@ def test_each_element_lands_at_declared_bit(orc):
         W[0, 0, 0:2] = [0x00, 0x3C]
         W[0, 0, 2 + e // 8] = 1 << (e % 8)
         bits, scales = orc.q1_planes(W, rows, K)
-        k, pos = declared_pos(e)
+        idx, pos = declared_pos(e)
         want = np.zeros(64 * 4, dtype=np.uint32)
-        want[k] = np.uint32(1) << np.uint32(pos)   # row 0 -> lane 0
+        want[idx] = np.uint32(1) << np.uint32(pos)   # row 0 -> lane 0
         assert np.array_equal(bits, want), e
         assert scales[0] == 0x3C00 and not scales[1:].any()
 
@@ -49,8 +51,9 @@ def _decode_planes(bits, scales, rows, K):
             h = int(scales[((t * (nb8 // 8) + i // 8) * 64 + lane) * 8 + i % 8])
             W[r, i, 0], W[r, i, 1] = h & 0xFF, h >> 8
             for e in range(128):
-                k, pos = declared_pos(e)
-                word = int(bits[((t * nb + i) * 64 + lane) * 4 + k])
+                idx, pos = declared_pos(e)
+                h, m = divmod(idx, 128)
+                word = int(bits[(((t * nb + i) * 2 + h) * 64 + lane) * 2 + m])
                 if (word >> pos) & 1:
                     W[r, i, 2 + e // 8] |= 1 << (e % 8)
     return W
@@ -64,7 +67,7 @@ def test_round_trip_and_zero_padding(orc, rows, K):
     nb = K // 128
     nb8 = (nb + 7) // 8 * 8
     r64 = (rows + 63) // 64 * 64
-    b4 = bits.reshape(r64 // 64, nb, 64, 4)
+    b4 = bits.reshape(r64 // 64, nb, 2, 64, 2).transpose(0, 1, 3, 2, 4).reshape(r64 // 64, nb, 64, 4)
     s8 = scales.reshape(r64 // 64, nb8 // 8, 64, 8)
     pad_rows = [r for r in range(rows, r64)]
     for r in pad_rows:
