@@ -268,6 +268,245 @@ def cpu_baseline_q1(Ws, A, shapes, budget_s: float):
                       f"cycling), {t_used:.2f} s of oracle time, OpenMP over rows, {cpu_model()}"}
 
 
+# ------------------------------------------------- secondary workloads
+
+MFMA_F16_PEAK_TFLOPS = 2500.0    # MI355X dense fp16 matrix peak
+
+
+def _events(torch):
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def _time_launches(torch, launch, n, warmup):
+    """Mean per-launch time (s) from HIP events around each launch, and the
+    total (s) between the first and last event."""
+    for w in range(warmup):
+        launch(w)
+    torch.cuda.synchronize()
+    evs = [_events(torch) for _ in range(n)]
+    t0, t1 = _events(torch)
+    t0.record()
+    for k in range(n):
+        evs[k][0].record()
+        launch(warmup + k)
+        evs[k][1].record()
+    t1.record()
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) / 1e3 for a, b in evs]
+    return float(np.mean(per)), t0.elapsed_time(t1) / 1e3
+
+
+def bench_sign(args, gd, torch):
+    """Sign-bit prefill GEMM y = x @ w^T, M=512 tokens, N=4096, K=4096: MFMA
+    roofline on the useful 2MNK flops."""
+    import oracle
+    c = wl.SIGN_PREFILL
+    M, N, K = c["M"], c["N"], c["K"]
+    x, bits, scales = wl.sign_gemm_inputs(M, N, K, c["seed"])
+    set_bytes = x.nbytes + bits.nbytes + scales.nbytes + M * N * 4
+    ring = max(2, int(np.ceil(0.5 * (1 << 30) / set_bytes)))
+    xs = torch.from_numpy(x).cuda()
+    bs = torch.from_numpy(bits.view(np.int32)).cuda()
+    ss = torch.from_numpy(scales).cuda()
+    sets = [(xs.clone(), bs.clone(), ss.clone(), torch.empty(M * N, device="cuda")) for _ in range(ring)]
+
+    def launch(k):
+        a, b, s_, y = sets[k % ring]
+        gd.q1_sign_gemm(a, b, s_, y, M, N, K)
+    per, _ = _time_launches(torch, launch, args.aux_steps, 3)
+    flops = 2.0 * M * N * K
+    tflops = flops / per / 1e12
+    # parity on a sample of columns
+    y = sets[(3 + args.aux_steps - 1) % ring][3].cpu().numpy().reshape(M, N)
+    cols = np.arange(0, N, 64)
+    want = oracle.sign_gemm_f64(x, bits[cols], scales[cols], nthreads=cpu_cores())
+    rel = float(np.max(np.abs(y[:, cols] - want)) / np.max(np.abs(want)))
+    # oracle on the host: whole rows of y (all N columns) until the budget
+    threads = cpu_cores()
+    t_used, rows_done = 0.0, 0
+    while t_used < args.aux_cpu_seconds and rows_done < M:
+        t = time.perf_counter()
+        oracle.sign_gemm_f64(x[rows_done:rows_done + 4], bits, scales, nthreads=threads)
+        t_used += time.perf_counter() - t
+        rows_done += 4
+    cpu_gflops = 2.0 * rows_done * N * K / t_used / 1e9
+    return {
+        "workload": "sign-bit prefill GEMM y=x@w^T, M=512, N=4096, K=4096, x f32 (fp16 hi+lo on MFMA)",
+        "metric": "useful TFLOP/s (2MNK)", "value": round(tflops, 2), "unit": "TFLOP/s",
+        "us_per_gemm": round(per * 1e6, 2), "prefill_tok_s": round(M / per, 1),
+        "issued_mfma_TFLOPs": round(2 * tflops, 2),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "sign_gemm_kernel", "flops_per_launch": flops},
+        "parity_rel_err_sampled": rel,
+        "cpu_baseline": {"value": round(cpu_gflops / 1e3, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+                         "sample": f"{rows_done} of 512 rows x all 4096 columns (f64 oracle), {t_used:.2f} s"},
+    }
+
+
+def bench_blockq8(args, gd, torch):
+    """Block-Q8 matmul_nt k=960, n=49152 at m=1 and m=16: HBM roofline on the
+    algorithmic bytes (quants + scales once, x once, y once)."""
+    import oracle
+    c = wl.BLOCKQ8_LMHEAD
+    k, n = c["k"], c["n"]
+    out = {}
+    x_all, quants, scales = wl.blockq8_inputs(16, k, n, c["seed"])
+    w_bytes = quants.nbytes + scales.nbytes
+    ring = max(2, int(np.ceil(1.05 * (1 << 30) / w_bytes)))
+    qd = torch.from_numpy(quants.view(np.int32)).cuda()
+    sd = torch.from_numpy(scales).cuda()
+    copies = [(qd.clone(), sd.clone()) for _ in range(ring)]
+    for m in c["ms"]:
+        x = np.ascontiguousarray(x_all[:m])
+        xd = torch.from_numpy(x).cuda()
+        y = torch.empty(m * n, device="cuda")
+
+        def launch(kk):
+            q_, s_ = copies[kk % ring]
+            gd.blockq8_matmul_nt(xd, q_, s_, y, m, k, n)
+        per, _ = _time_launches(torch, launch, args.aux_steps, 3)
+        bytes_ = w_bytes + x.nbytes + m * n * 4
+        gbps = bytes_ / per / 1e9
+        cols = np.arange(0, n, 97)
+        got = y.cpu().numpy().reshape(m, n)[:, cols]
+        want = oracle.blockq8_f32(x, quants[cols], scales[cols], nthreads=cpu_cores())
+        rel = float(np.max(np.abs(got - want)) / np.max(np.abs(want)))
+        threads = cpu_cores()
+        t_used, cols_done, step = 0.0, 0, 4096
+        while t_used < args.aux_cpu_seconds / 2 and cols_done < n:
+            t = time.perf_counter()
+            oracle.blockq8_f32(x, quants[cols_done:cols_done + step], scales[cols_done:cols_done + step],
+                               nthreads=threads)
+            t_used += time.perf_counter() - t
+            cols_done += step
+        cpu_bytes = cols_done * (k + k // 32 * 4) + x.nbytes + m * cols_done * 4
+        out[f"m{m}"] = {
+            "workload": f"block-Q8 matmul_nt k=960 n=49152 m={m}",
+            "metric": "effective HBM GB/s", "value": round(gbps, 1), "unit": "GB/s",
+            "us_per_launch": round(per * 1e6, 2), "pct_of_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+            "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "blockq8_valu_kernel",
+                         "bytes_per_launch": bytes_},
+            "parity_rel_err_sampled": rel,
+            "cpu_baseline": {"value": round(cpu_bytes / t_used / 1e9, 4), "unit": "GB/s", "cores": threads,
+                             "kind": "oracle",
+                             "sample": f"{cols_done} of 49152 output features, m={m}, {t_used:.2f} s"},
+        }
+    return out
+
+
+def bench_ternary(args, gd, torch):
+    """BitNet-2B-like ternary decode step: 210 GEMVs (per layer 4 x 2560x2560,
+    2 x 6912x2560, 1 x 2560x6912), each with its own activation vector (bit
+    planes built on the device inside the step) and its own weight copy."""
+    import oracle
+    shapes = wl.bitnet_step_shapes()
+    groups = {}
+    for j, sh in enumerate(shapes):
+        groups.setdefault(sh, []).append(j)
+    # one weight per shape (copied to every GEMV slot), one activation per GEMV
+    base = {}
+    for sh in groups:
+        P, N, ws, _, _ = wl.ternary_inputs(sh[0], sh[1], wl.TERNARY_SEED_BASE + 1000 + sh[0] + sh[1])
+        base[sh] = (P, N, ws)
+    xq, xsc = {}, {}
+    for j, (rows, K) in enumerate(shapes):
+        rng = np.random.default_rng(wl.TERNARY_SEED_BASE + j)
+        q, s_ = wl.absmax_int8(rng.standard_normal(K))
+        xq[j], xsc[j] = q, s_
+    step_w_bytes = sum(2 * base[sh][0].nbytes * len(idx) for sh, idx in groups.items())
+    n_sets = 2 if step_w_bytes * 2 > (1 << 30) else int(np.ceil((1 << 30) / step_w_bytes)) + 1
+    keep, slots = [], []
+    dev_base = {sh: (torch.from_numpy(base[sh][0].view(np.int32)).cuda(),
+                     torch.from_numpy(base[sh][1].view(np.int32)).cuda()) for sh in groups}
+    x_by_K, planes_by_K, xoff = {}, {}, {}
+    for K in sorted({sh[1] for sh in shapes}):
+        js = [j for j, sh in enumerate(shapes) if sh[1] == K]
+        x_by_K[K] = torch.from_numpy(np.stack([xq[j] for j in js])).cuda()
+        planes_by_K[K] = torch.empty(len(js) * 8 * (K // 32), dtype=torch.int32, device="cuda")
+        for pos, j in enumerate(js):
+            xoff[j] = (K, pos)
+    ys = {j: torch.empty(shapes[j][0], device="cuda") for j in range(len(shapes))}
+    for sset in range(n_sets):
+        per = {}
+        for sh, idx in groups.items():
+            entries = []
+            for j in idx:
+                Pd, Nd = dev_base[sh][0].clone(), dev_base[sh][1].clone()
+                keep.append((Pd, Nd))
+                K, pos = xoff[j]
+                W = K // 32
+                xp = planes_by_K[K][pos * 8 * W:(pos + 1) * 8 * W]
+                entries.append((Pd, Nd, xp, ys[j], None, base[sh][2], xsc[j]))
+            per[sh] = gd.make_ternary_problems(entries)
+        slots.append(per)
+    torch.cuda.synchronize()
+    step_bytes = step_w_bytes + sum(shapes[j][1] + shapes[j][0] * 4 + 8 for j in range(len(shapes)))
+
+    def step(kk, ev=None):
+        sset = slots[kk % n_sets]
+        if ev is not None:
+            ev[0].record()
+        for K, xd in x_by_K.items():
+            gd.ternary_act_bitplanes(xd, xd.shape[0], K, planes_by_K[K])
+        if ev is not None:
+            ev[1].record()
+        for sh, idx in groups.items():
+            gd.ternary_gemv_grouped(sset[sh], len(idx), sh[0], sh[1])
+        if ev is not None:
+            ev[2].record()
+
+    for w in range(3):
+        step(w)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.aux_steps)]
+    t0, t1 = _events(torch)
+    t0.record()
+    for kk in range(args.aux_steps):
+        step(3 + kk, evs[kk])
+    t1.record()
+    torch.cuda.synchronize()
+    total = t0.elapsed_time(t1) / 1e3 / args.aux_steps
+    gemv_s = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) / 1e3
+    gemv_bytes = step_w_bytes + sum(shapes[j][0] * 4 + 8 * (shapes[j][1] // 32) * 4 for j in range(len(shapes)))
+    gbps = step_bytes / total / 1e9
+    # parity: three GEMVs (one per shape), every row, against the oracle
+    mism = 0
+    for sh, idx in groups.items():
+        j = idx[0]
+        yo, _ = oracle.ternary_gemv(base[sh][0], base[sh][1], base[sh][2], xq[j], xsc[j], nthreads=cpu_cores())
+        mism += int((ys[j].cpu().numpy().view(np.uint32) != yo.view(np.uint32)).sum())
+    threads = cpu_cores()
+    t_used, done_bytes, n_g = 0.0, 0, 0
+    while t_used < args.aux_cpu_seconds:
+        j = n_g % len(shapes)
+        sh = shapes[j]
+        rows = min(sh[0], 512)
+        t = time.perf_counter()
+        oracle.ternary_gemv(base[sh][0][:rows], base[sh][1][:rows], base[sh][2], xq[j], xsc[j], nthreads=threads)
+        t_used += time.perf_counter() - t
+        done_bytes += 2 * rows * sh[1] // 8
+        n_g += 1
+    return {
+        "workload": "ternary bitplane decode step: 30 layers x {4x 2560x2560, 2x 6912x2560, 1x 2560x6912} = 210 "
+                    "GEMVs, int8 activations as bit planes, P/N weight planes",
+        "metric": "effective HBM GB/s (step)", "value": round(gbps, 1), "unit": "GB/s",
+        "us_per_step": round(total * 1e6, 2), "equiv_tok_s": round(1.0 / total, 1),
+        "context_tok_s_at_0.69GB": round(gbps / 0.69, 1),
+        "pct_of_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(gemv_bytes / gemv_s / 1e9, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gemv_bytes / gemv_s / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "ternary_gemv_grouped_kernel (3 launches per step)",
+                     "bytes_per_step_gemv": gemv_bytes},
+        "step_bytes": step_bytes, "ring_sets": n_sets,
+        "parity_mismatches_3_gemvs": mism,
+        "cpu_baseline": {"value": round(done_bytes / t_used / 1e9, 4), "unit": "GB/s", "cores": threads,
+                         "kind": "oracle",
+                         "sample": f"{n_g} GEMVs of the step (first 512 rows each), {t_used:.2f} s"},
+    }
+
+
 # --------------------------------------------------------------------- main
 
 def main():
@@ -275,7 +514,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="q1", choices=["q1"])
+    ap.add_argument("--workload", default="all", choices=["all", "q1", "sign", "blockq8", "ternary"],
+                    help="all (default): the Q1 metric line plus the other paths under 'workloads'")
+    ap.add_argument("--aux-steps", type=int, default=20, help="timed launches for the other paths")
+    ap.add_argument("--aux-cpu-seconds", type=float, default=4.0)
     ap.add_argument("--ring-gib", type=float, default=1.25)
     ap.add_argument("--serial-steps", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -300,7 +542,22 @@ def main():
     import gemm_decode_amd as gd
     torch.cuda.set_device(0)
     log(f"[bench] device: {torch.cuda.get_device_name(0)}")
-    out = bench_q1(args, gd, torch)
+    if args.workload in ("all", "q1"):
+        out = bench_q1(args, gd, torch)
+    else:
+        out = {"metric": METRIC, "note": "Q1 workload skipped (--workload)"}
+    if args.workload != "q1":
+        extra = {}
+        if args.workload in ("all", "sign"):
+            log("[bench] sign-bit prefill GEMM")
+            extra["sign_gemm"] = bench_sign(args, gd, torch)
+        if args.workload in ("all", "blockq8"):
+            log("[bench] block-Q8 matmul_nt")
+            extra["blockq8"] = bench_blockq8(args, gd, torch)
+        if args.workload in ("all", "ternary"):
+            log("[bench] ternary decode step")
+            extra["ternary_step"] = bench_ternary(args, gd, torch)
+        out["workloads"] = extra
     print(json.dumps(out), flush=True)
 
 
