@@ -86,6 +86,116 @@ __global__ __launch_bounds__(kThreads) void blockq8_valu_kernel(const float *__r
     }
 }
 
+// ---------------------------------------------------------------- m = 1
+// Decode GEMV (one activation row). Thirty-two lanes share an output
+// feature; lane j owns chunks c = j + 32t (t < kCPL) of 16 quants, the same
+// positions in every row, so its slice of x (up to 32 floats) and each
+// chunk's sum of x stay in registers and no LDS is needed. Quant bytes are
+// read as unsigned u = q + 128 (q xor 0x80, then v_cvt_f32_ubyte) and the
+// bias is removed once per chunk: sum x*q = sum x*u - 128*sum x. A wave
+// covers two rows per step and keeps the loads of the next three steps in
+// flight (four register sets rotated by name).
+constexpr int kLPR = 32;                // lanes per row
+constexpr int kCPL = 2;                 // chunks per lane: k <= 16*kLPR*kCPL = 1024
+constexpr int kGemvThreads = 256;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef const u32x4 __attribute__((address_space(1))) *gq_t;
+typedef const float __attribute__((address_space(1))) *gf_t;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef const f32x4 __attribute__((address_space(1))) *gx_t;
+
+struct RowBuf {
+    u32x4 q[kCPL];
+    float s[kCPL];
+};
+
+__global__ __launch_bounds__(kGemvThreads) void blockq8_gemv_kernel(const float *x_g, const uint32_t *quants_g,
+                                                                     const float *scales_g,
+                                                                     float *__restrict__ y, int64_t k, int64_t n,
+                                                                     int64_t steps_per_wave) {
+    const gq_t quants = (gq_t)quants_g;
+    const gf_t scales = (gf_t)scales_g;
+    const gx_t xq = (gx_t)x_g;                               // x as 16-byte words
+    const int lane = threadIdx.x % kLPR;
+    const int sub = (threadIdx.x % 64) / kLPR;               // row within the wave's pair
+    const int64_t wave = (static_cast<int64_t>(blockIdx.x) * kGemvThreads + threadIdx.x) / 64;
+    const int chunks = static_cast<int>(k / 16);
+    const int64_t bpr = k / 32;
+    const int64_t row0 = wave * 2 * steps_per_wave;          // rows row0 + 2i + sub
+
+    auto load = [&](int64_t i, RowBuf &b) {
+        int64_t r = row0 + 2 * i + sub;
+        r = r < n ? r : n - 1;                                  // clamped: never stored
+#pragma unroll
+        for (int t = 0; t < kCPL; t++) {
+            int c = lane + kLPR * t;
+            c = c < chunks ? c : chunks - 1;                     // masked by x = 0 below
+            b.q[t] = quants[r * chunks + c];
+            b.s[t] = scales[r * bpr + c / 2];
+        }
+    };
+    RowBuf b0, b1, b2, b3;
+    load(0, b0);
+    load(1, b1);
+    load(2, b2);
+
+    float xv[kCPL][16], xs[kCPL];
+#pragma unroll
+    for (int t = 0; t < kCPL; t++) {
+        const int c = lane + kLPR * t;
+        const int cc = c < chunks ? c : chunks - 1;
+        const float keep = c < chunks ? 1.0f : 0.0f;
+        xs[t] = 0.0f;
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+            const f32x4 w = xq[cc * 4 + v];
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                xv[t][4 * v + e] = w[e] * keep;
+                xs[t] += xv[t][4 * v + e];
+            }
+        }
+    }
+    auto row_dot = [&](const RowBuf &b) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int t = 0; t < kCPL; t++) {
+            float s = 0.0f;
+#pragma unroll
+            for (int wq = 0; wq < 4; wq++) {
+                const uint32_t u = b.q[t][wq] ^ 0x80808080u;    // q + 128 per byte
+                s = __builtin_fmaf(xv[t][4 * wq + 0], static_cast<float>(u & 0xffu), s);
+                s = __builtin_fmaf(xv[t][4 * wq + 1], static_cast<float>((u >> 8) & 0xffu), s);
+                s = __builtin_fmaf(xv[t][4 * wq + 2], static_cast<float>((u >> 16) & 0xffu), s);
+                s = __builtin_fmaf(xv[t][4 * wq + 3], static_cast<float>(u >> 24), s);
+            }
+            s = __builtin_fmaf(-128.0f, xs[t], s);
+            acc = __builtin_fmaf(b.s[t], s, acc);
+        }
+        acc += __shfl_xor(acc, 1, kLPR);
+        acc += __shfl_xor(acc, 2, kLPR);
+        acc += __shfl_xor(acc, 4, kLPR);
+        acc += __shfl_xor(acc, 8, kLPR);
+        acc += __shfl_xor(acc, 16, kLPR);
+        return acc;
+    };
+    auto store = [&](int64_t i, float v) {
+        const int64_t r = row0 + 2 * i + sub;
+        if (lane == 0 && i < steps_per_wave && r < n) y[r] = v;
+    };
+    for (int64_t i = 0; i < steps_per_wave; i += 4) {
+        load(i + 3, b3);
+        store(i, row_dot(b0));
+        load(i + 4, b0);
+        store(i + 1, row_dot(b1));
+        load(i + 5, b1);
+        store(i + 2, row_dot(b2));
+        load(i + 6, b2);
+        store(i + 3, row_dot(b3));
+    }
+}
+
 template <int M>
 void launch_valu(const float *x, const uint32_t *q, const float *s, float *y, int m, int64_t k, int64_t n,
                  hipStream_t st) {
@@ -110,11 +220,21 @@ extern "C" int blockq8_matmul_nt(const float *x, const uint32_t *quants, const f
                kMaxXFloats);
     GD_REQUIRE(n <= (INT64_C(1) << 31), GD_ERANGE, "blockq8_matmul_nt: n above 2^31");
     GD_REQUIRE(aligned(quants, 16), GD_EALIGN, "blockq8_matmul_nt: quants must be 16-byte aligned");
-    GD_REQUIRE(aligned(x, 4) && aligned(scales, 4) && aligned(y, 4), GD_EALIGN,
-               "blockq8_matmul_nt: x, scales and y must be 4-byte aligned");
+    GD_REQUIRE(aligned(x, 16), GD_EALIGN, "blockq8_matmul_nt: x must be 16-byte aligned");
+    GD_REQUIRE(aligned(scales, 4) && aligned(y, 4), GD_EALIGN,
+               "blockq8_matmul_nt: scales and y must be 4-byte aligned");
     hipStream_t st = as_stream(stream);
     const int mi = static_cast<int>(m);
-    if (m == 1)
+    if (m == 1 && k <= 16 * kLPR * kCPL) {
+        // steps per wave (a multiple of 4) chosen for ~20 waves per CU on 256 CUs
+        const int64_t pairs = (n + 1) / 2;                        // 2 rows per wave step
+        int64_t spw = (pairs + 5119) / 5120;
+        spw = (spw + 3) / 4 * 4;
+        const int64_t waves = (pairs + spw - 1) / spw;
+        const int64_t blocks = (waves * 64 + kGemvThreads - 1) / kGemvThreads;
+        hipLaunchKernelGGL(blockq8_gemv_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kGemvThreads), 0, st, x,
+                           quants, scales, y, k, n, spw);
+    } else if (m == 1)
         launch_valu<1>(x, quants, scales, y, mi, k, n, st);
     else if (m <= 2)
         launch_valu<2>(x, quants, scales, y, mi, k, n, st);

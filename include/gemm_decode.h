@@ -163,7 +163,7 @@ int q1_sign_gemm(const float *x, const uint32_t *w_bits, const float *w_scales,
  * ACCUMULATION ORDER, quant_at, main)
  * ====================================================================
  *   y[r][c] = sum_b scales[c][b] * sum_{t<32} x[r][32b+t] * q[c][32b+t]
- *   x       device f32 [m][k] row-major, 4-byte aligned.
+ *   x       device f32 [m][k] row-major, 16-byte aligned.
  *   quants  device u32 [n][k/4]: element t of row c in byte t%4 of word
  *           c*k/4 + t/4 (little-endian), two's-complement int8; 16-byte
  *           aligned.

@@ -90,6 +90,7 @@ def test_validation_without_gpu(gd):
     assert L.blockq8_matmul_nt(FAKE, FAKE, FAKE, FAKE, 1, 100, 4, None) == E["shape"]
     assert L.blockq8_matmul_nt(FAKE, FAKE, FAKE, FAKE, 1, 960, 0, None) == E["inval"]
     assert L.blockq8_matmul_nt(FAKE, FAKE + 4, FAKE, FAKE, 1, 960, 4, None) == E["align"]
+    assert L.blockq8_matmul_nt(FAKE + 4, FAKE, FAKE, FAKE, 1, 960, 4, None) == E["align"]
     assert L.blockq8_matmul_nt(FAKE, FAKE, FAKE, FAKE, 65, 960, 4, None) == E["range"]
     # ternary
     assert L.ternary_act_bitplanes(FAKE, 1, 100, FAKE, None) == E["shape"]
