@@ -196,6 +196,171 @@ __global__ __launch_bounds__(kGemvThreads) void blockq8_gemv_kernel(const float 
     }
 }
 
+// ---------------------------------------------------------------- 2 <= m <= 16
+// Small-M GEMM on the matrix cores. One v_mfma_f32_16x16x32_f16 spans
+// exactly one 32-element block (K = 32), so its output is the block's
+// sub-total for a 16 x 16 tile of (activation row, output feature) and the
+// block scale is applied once to it, as in the page's order.
+//   A = x, row i = lane % 16, k slice 8*(lane/16) .. +7 of the block, as an
+//       f16 pair hi + lo (x = hi + lo to 22 bits) after scaling each row by
+//       a power of two 2^e that puts its largest |x| in [2^14, 2^15); the
+//       sub-total is scaled back by 2^-e before the block scale.
+//   B = w, column j = lane % 16 (output feature n0 + j), same k slice: one
+//       8-byte load per lane per block. Bytes become f16 exactly: the byte
+//       of q + 128 under the exponent byte 0x64 is the f16 1024 + q + 128,
+//       and one packed f16 add of -1152 leaves q.
+//   D lane l holds rows 4*(l/16) + r (r < 4) of column l % 16.
+// A wave owns one 16-feature tile and issues the loads of all its blocks
+// (k <= 1024, at most 32) before the activations are staged; a workgroup of
+// twelve waves stages the activations once, in MFMA operand order in LDS.
+constexpr int kMfmaWaves = 12;
+constexpr int kMfmaThreads = 64 * kMfmaWaves;
+constexpr int kMfmaMaxK = 1024;
+constexpr int kScStride = 33;          // padded row of staged block scales
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef const u32x2 __attribute__((address_space(1))) *gq2_t;
+
+// Four f16 values q (two's-complement bytes of w) as two packed f16 pairs.
+__device__ __forceinline__ void q8_to_half4(uint32_t w, uint32_t &lo, uint32_t &hi) {
+    const uint32_t u = w ^ 0x80808080u;                                     // q + 128
+    const uint32_t a = (u & 0xffu) | ((u & 0xff00u) << 8) | 0x64006400u;   // bytes 0, 1
+    const uint32_t b = ((u >> 16) & 0xffu) | ((u >> 8) & 0xff0000u) | 0x64006400u;
+    const half2v bias = {static_cast<_Float16>(-1152.0f), static_cast<_Float16>(-1152.0f)};
+    lo = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, a) + bias);
+    hi = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, b) + bias);
+}
+
+template <int NB>
+__global__ __launch_bounds__(kMfmaThreads) void blockq8_mfma_kernel(const float *x_g, const uint32_t *quants_g,
+                                                                     const float *scales_g, float *__restrict__ y,
+                                                                     int m, int nb, int64_t n) {
+    __shared__ __attribute__((aligned(16))) half8 xop[NB][2][64];   // [block][hi, lo][lane]
+    __shared__ float sc[kMfmaWaves][16][kScStride];                  // [wave][feature][block]
+    __shared__ float wmax[kMfmaWaves][16];
+    __shared__ int rexp[16];
+    constexpr int kSlots = 64 * NB;                                  // (block, k slice, row) triples
+    constexpr int kSlotIters = (kSlots + kMfmaThreads - 1) / kMfmaThreads;
+
+    const gx_t xg = (gx_t)x_g;
+    const gq2_t quants = (gq2_t)quants_g;
+    const gf_t scales = (gf_t)scales_g;
+    const int tid = threadIdx.x;
+    const int l = tid % 64;
+    const int wv = tid / 64;
+    const int j = l % 16;
+    const int g = l / 16;
+    const int64_t k = 32 * static_cast<int64_t>(nb);
+    const int64_t n0 = (static_cast<int64_t>(blockIdx.x) * kMfmaWaves + wv) * 16;
+
+    // 1. activation slots, read first so that waiting for them does not wait
+    //    for the weight loads issued after them (loads complete in order)
+    const int mm = tid % 16;                       // row of every slot of this thread
+    const int mmc = mm < m ? mm : m - 1;
+    const float keep = mm < m ? 1.0f : 0.0f;
+    f32x4 xv[kSlotIters][2];
+#pragma unroll
+    for (int it = 0; it < kSlotIters; it++) {
+        const int s = tid + it * kMfmaThreads;
+        int b = s / 64;
+        b = b < nb ? b : nb - 1;
+        const int64_t off = (mmc * k + 32 * b + 8 * ((s % 64) / 16)) / 4;
+        xv[it][0] = xg[off] * keep;
+        xv[it][1] = xg[off + 1] * keep;
+    }
+    // 2. this wave's block scales: rows n0 .. n0+15, two rows per load
+    float sv[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        int64_t r = n0 + 2 * i + l / 32;
+        r = r < n ? r : n - 1;
+        const int b = (l % 32) < nb ? (l % 32) : nb - 1;
+        sv[i] = scales[r * nb + b];
+    }
+    // 3. every block of this lane's feature: 8 bytes at k slice g
+    const int64_t row = n0 + j < n ? n0 + j : n - 1;
+    u32x2 wq[NB];
+#pragma unroll
+    for (int b = 0; b < NB; b++) {
+        const int bc = b < nb ? b : nb - 1;
+        wq[b] = quants[row * (k / 8) + 4 * bc + g];
+    }
+
+    // 4. per-row power of two: largest |x| of each row over the workgroup
+    float amax = 0.0f;
+#pragma unroll
+    for (int it = 0; it < kSlotIters; it++)
+#pragma unroll
+        for (int h = 0; h < 2; h++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) amax = fmaxf(amax, fabsf(xv[it][h][e]));
+    amax = fmaxf(amax, __shfl_xor(amax, 16));
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    if (l < 16) wmax[wv][l] = amax;
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+        if (l % 32 < nb) sc[wv][2 * i + l / 32][l % 32] = sv[i];
+    __syncthreads();
+    float rm = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kMfmaWaves; w++) rm = fmaxf(rm, wmax[w][mm]);
+    const int ex = rm > 0.0f ? 15 - __builtin_amdgcn_frexp_expf(rm) : 0;
+    if (tid < 16) rexp[tid] = ex;
+#pragma unroll
+    for (int it = 0; it < kSlotIters; it++) {
+        const int s = tid + it * kMfmaThreads;
+        if (s < 64 * nb) {
+            half8 hv, lv;
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                const float v = __builtin_ldexpf(xv[it][e / 4][e % 4], ex);
+                hv[e] = static_cast<_Float16>(v);
+                lv[e] = static_cast<_Float16>(v - static_cast<float>(hv[e]));
+            }
+            xop[s / 64][0][s % 64] = hv;
+            xop[s / 64][1][s % 64] = lv;
+        }
+    }
+    __syncthreads();
+
+    // 5. one block per step: sub-total on the matrix cores, then the scale
+    int nexp[4];
+#pragma unroll
+    for (int r = 0; r < 4; r++) nexp[r] = -rexp[4 * g + r];
+    floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int b = 0; b < NB; b++) {
+        if (b < nb) {
+            union { uint32_t u[4]; half8 h; } bw;
+            q8_to_half4(wq[b][0], bw.u[0], bw.u[1]);
+            q8_to_half4(wq[b][1], bw.u[2], bw.u[3]);
+            floatx4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xop[b][0][l], bw.h, floatx4{0.0f, 0.0f, 0.0f, 0.0f},
+                                                               0, 0, 0);
+            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xop[b][1][l], bw.h, d, 0, 0, 0);
+            const float s = sc[wv][j][b];
+#pragma unroll
+            for (int r = 0; r < 4; r++) acc[r] = __builtin_fmaf(s, __builtin_ldexpf(d[r], nexp[r]), acc[r]);
+        }
+    }
+    if (n0 + j < n) {
+#pragma unroll
+        for (int r = 0; r < 4; r++)
+            if (4 * g + r < m) y[(4 * g + r) * n + n0 + j] = acc[r];
+    }
+}
+
+template <int NB>
+void launch_mfma(const float *x, const uint32_t *q, const float *s, float *y, int m, int64_t k, int64_t n,
+                 hipStream_t st) {
+    const int64_t tiles = (n + 15) / 16;
+    const int64_t gx = (tiles + kMfmaWaves - 1) / kMfmaWaves;
+    hipLaunchKernelGGL(blockq8_mfma_kernel<NB>, dim3(static_cast<uint32_t>(gx)), dim3(kMfmaThreads), 0, st, x, q,
+                       s, y, m, static_cast<int>(k / 32), n);
+}
+
 template <int M>
 void launch_valu(const float *x, const uint32_t *q, const float *s, float *y, int m, int64_t k, int64_t n,
                  hipStream_t st) {
@@ -234,6 +399,13 @@ extern "C" int blockq8_matmul_nt(const float *x, const uint32_t *quants, const f
         const int64_t blocks = (waves * 64 + kGemvThreads - 1) / kGemvThreads;
         hipLaunchKernelGGL(blockq8_gemv_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kGemvThreads), 0, st, x,
                            quants, scales, y, k, n, spw);
+    } else if (m >= 2 && k <= kMfmaMaxK) {
+        if (k <= 256)
+            launch_mfma<8>(x, quants, scales, y, mi, k, n, st);
+        else if (k <= 512)
+            launch_mfma<16>(x, quants, scales, y, mi, k, n, st);
+        else
+            launch_mfma<32>(x, quants, scales, y, mi, k, n, st);
     } else if (m == 1)
         launch_valu<1>(x, quants, scales, y, mi, k, n, st);
     else if (m <= 2)

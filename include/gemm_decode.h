@@ -171,10 +171,14 @@ int q1_sign_gemm(const float *x, const uint32_t *w_bits, const float *w_scales,
  *   y       device f32 [m][n], 4-byte aligned.
  * Requires k % 32 == 0 (an error, where the page's kernel would silently
  * drop a tail) and k % 16 == 0 rows of quants on 16-byte boundaries (implied
- * by k % 32 == 0). Results agree with the page's order within 1e-5 of
- * ||y||_inf. Limits: m <= 16 and m*k <= 16384 (the activation rows are
- * staged whole in LDS). Errors: GD_EINVAL, GD_ESHAPE, GD_EALIGN, GD_ERANGE,
- * GD_EHIP. */
+ * by k % 32 == 0). x must be finite. Results agree with the page's order
+ * within 1e-5 of ||y||_inf. For 2 <= m <= 16 and k <= 1024 the block
+ * sub-totals run on fp16 matrix cores: each activation row is scaled by a
+ * power of two that brings its largest |x| into [2^14, 2^15), split into
+ * high and low fp16 parts, and the sub-total is scaled back exactly, so
+ * rows of any finite magnitude keep ~22 bits. Limits: m <= 16 and
+ * m*k <= 16384 (the activation rows are staged whole in LDS). Errors:
+ * GD_EINVAL, GD_ESHAPE, GD_EALIGN, GD_ERANGE, GD_EHIP. */
 int blockq8_matmul_nt(const float *x, const uint32_t *quants, const float *scales,
                       float *y, int64_t m, int64_t k, int64_t n, void *stream);
 

@@ -84,3 +84,40 @@ def test_sign_extension(gd):
     x = np.ones((1, k), dtype=np.float32)
     y = run(gd, x, quants, np.ones((n, 1), dtype=np.float32))
     assert y.tolist() == [[-1.0, -128.0]]
+
+
+@pytest.mark.parametrize("m", [2, 3, 7, 8, 9, 15, 16])
+@pytest.mark.parametrize("k", [32, 256, 288, 512, 544, 1024])
+def test_small_m_tiles(gd, m, k):
+    """2 <= m <= 16 with k <= 1024 (the matrix-core path): every block-count
+    bucket edge, m across partial row groups, n ragged over 16-feature
+    tiles and twelve-tile workgroups."""
+    n = 16 * 13 + 5
+    x, quants, scales = wl.blockq8_inputs(m, k, n, seed=7 * m + k)
+    y = run(gd, x, quants, scales)
+    assert rel_err(y, oracle.blockq8_f32(x, quants, scales)) <= TOL
+
+
+@pytest.mark.parametrize("m,k", [(1, 2048), (2, 1056), (4, 4096)])
+def test_long_rows(gd, m, k):
+    """k above 1024 (the staged-activation VALU path)."""
+    n = 150
+    x, quants, scales = wl.blockq8_inputs(m, k, n, seed=m + k)
+    y = run(gd, x, quants, scales)
+    assert rel_err(y, oracle.blockq8_f32(x, quants, scales)) <= TOL
+
+
+def test_row_magnitudes(gd):
+    """Activation rows 40 decades apart and an all-zero row: each output row
+    meets the bar against its own largest value, and the zero row is 0."""
+    m, k, n = 7, 512, 200
+    x, quants, scales = wl.blockq8_inputs(m, k, n, seed=5)
+    mags = np.array([1e-20, 1e-4, 1.0, 1e4, 7e4, 1e20, 0.0], dtype=np.float64)
+    x = (x * mags[:, None]).astype(np.float32)
+    y = run(gd, x, quants, scales)
+    want = oracle.blockq8_f32(x, quants, scales)
+    for r in range(m):
+        if mags[r] == 0.0:
+            assert np.all(y[r] == 0.0)
+        else:
+            assert rel_err(y[r:r + 1], want[r:r + 1]) <= TOL, r
