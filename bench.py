@@ -125,13 +125,9 @@ def bench_q1(args, gd, torch):
         slots.append(per_shape)
     torch.cuda.synchronize()
 
-    def step(r, events=None):
+    def step(r):
         for si, s in enumerate(shapes):
-            if events is not None:
-                events[si][0].record()
             gd.q1_q8_gemv_grouped(slots[r][si][0], n_vec, s.rows, s.K)
-            if events is not None:
-                events[si][1].record()
 
     # parity spot check (untimed): every output of the first ring slot
     step(0)
@@ -146,28 +142,67 @@ def bench_q1(args, gd, torch):
             mism += int((got.view(np.uint32) != want.view(np.uint32)).sum())
         log(f"[bench] q1: parity vs oracle: {mism} mismatching outputs")
 
-    for w in range(args.warmup):
-        step(w % ring)
+    # Timed steps: the launches are queued back to back from the host with
+    # no event between them (the GPU runs them without gaps). --graph
+    # replays HIP graphs instead: one graph per full ring cycle (`ring`
+    # steps), one-step graphs per slot for a remainder.
+    cap = torch.cuda.Stream()
+
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            fn()
+        return g
+
+    if args.graph:
+        ring_graph = capture(lambda: [step(r) for r in range(ring)])
+        slot_graphs = [capture(lambda r=r: step(r)) for r in range(ring)]
+        torch.cuda.synchronize()
+
+    def run_steps(n):
+        if not args.graph:
+            for k in range(n):
+                step(k % ring)
+            return
+        for _ in range(n // ring):
+            ring_graph.replay()
+        for r in range(n % ring):
+            slot_graphs[r].replay()
+
+    run_steps(max(args.warmup, ring))
     torch.cuda.synchronize()
 
-    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in shapes] for _ in range(args.steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record()
-    for k in range(args.steps):
-        step((args.warmup + k) % ring, evs[k])
+    run_steps(args.steps)
     t1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_s = t0.elapsed_time(t1) / 1e3
-    per_launch = [[evs[k][si][0].elapsed_time(evs[k][si][1]) / 1e3 for k in range(args.steps)]
-                  for si in range(len(shapes))]
+
+    # Roofline: mean duration of each grouped kernel, from HIP events on the
+    # launch stream around `per_shape` back-to-back launches of that kernel
+    # alone (ring slots in turn), after the same number untimed.
+    per_shape = 8 * ring
     launch_bytes = [n_vec * q1_gemv_bytes(s.rows, s.K) for s in shapes]
-    kern_s = sum(sum(p) for p in per_launch)
-    kern_bytes = sum(launch_bytes[si] * args.steps for si in range(len(shapes)))
-    achieved = kern_bytes / kern_s / 1e9
+    per_launch = []
+    for si, s in enumerate(shapes):
+        def run_shape(si=si, s=s):
+            for j in range(per_shape):
+                gd.q1_q8_gemv_grouped(slots[j % ring][si][0], n_vec, s.rows, s.K)
+        run_shape()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        run_shape()
+        e1.record()
+        torch.cuda.synchronize()
+        per_launch.append(e0.elapsed_time(e1) / 1e3 / per_shape)
+    kern_s = sum(per_launch)
+    achieved = sum(launch_bytes) / kern_s / 1e9
 
     gbps = step_bytes * args.steps / total_s / 1e9
     ms_per_step = total_s / args.steps * 1e3
@@ -223,6 +258,8 @@ def bench_q1(args, gd, torch):
                         "copies (ring > 1 GiB)",
             "rows": [s.rows for s in shapes], "K": K, "activation_vectors": n_vec,
             "step_bytes": step_bytes, "ring_sets": ring,
+            "timed_as": (f"HIP graph replays ({ring} steps per graph)" if args.graph
+                         else "launches queued back to back, events only at the ends"),
         },
         "pct_of_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "equiv_tok_s": round(gbps * 1e9 / MODEL_8B_Q1_BYTES, 1),
@@ -231,8 +268,8 @@ def bench_q1(args, gd, torch):
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
             "kernel": "q1_gemv_grouped_kernel",
-            "per_shape_us": {f"{s.rows}x{s.K}": round(float(np.mean(per_launch[si])) * 1e6, 2)
-                             for si, s in enumerate(shapes)},
+            "per_shape_us": {f"{s.rows}x{s.K}": round(per_launch[si] * 1e6, 2) for si, s in enumerate(shapes)},
+            "timing": f"HIP events around {per_shape} back-to-back launches of one shape",
             "bytes_per_launch": {f"{s.rows}x{s.K}": launch_bytes[si] for si, s in enumerate(shapes)},
         },
         "parity_mismatches": mism,
@@ -523,6 +560,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-ceiling", dest="ceiling", action="store_false")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the Q1 steps as HIP graph replays instead of queued launches")
     ap.add_argument("--ceiling-gib", type=float, default=2.0)
     ap.add_argument("--ceiling-passes", type=int, default=8)
     ap.add_argument("--ceiling-reps", type=int, default=5)

@@ -224,29 +224,6 @@ __device__ __forceinline__ void half_math(const float (&v)[16], float d0, float 
     }
 }
 
-// Eight blocks U0..U0+7 of the chunk: table reads of block u+1 are issued
-// before the arithmetic of block u consumes its own.
-template <int H, int U0>
-__device__ __forceinline__ void group8(const char *tab, const u32x2 (&wb)[8], const u32x4 &s8, float (&acc)[4]) {
-    float va[16], vb[16];
-    half_reads<H, U0 + 0>(tab, wb[0], va);
-    half_reads<H, U0 + 1>(tab, wb[1], vb);
-    half_math(va, d0_half<0>(s8), acc);
-    half_reads<H, U0 + 2>(tab, wb[2], va);
-    half_math(vb, d0_half<1>(s8), acc);
-    half_reads<H, U0 + 3>(tab, wb[3], vb);
-    half_math(va, d0_half<2>(s8), acc);
-    half_reads<H, U0 + 4>(tab, wb[4], va);
-    half_math(vb, d0_half<3>(s8), acc);
-    half_reads<H, U0 + 5>(tab, wb[5], vb);
-    half_math(va, d0_half<4>(s8), acc);
-    half_reads<H, U0 + 6>(tab, wb[6], va);
-    half_math(vb, d0_half<5>(s8), acc);
-    half_reads<H, U0 + 7>(tab, wb[7], vb);
-    half_math(va, d0_half<6>(s8), acc);
-    half_math(vb, d0_half<7>(s8), acc);
-}
-
 struct RowPtrs {
     gptr_u2 bits;          // this wave's half of block 0 of this row; + i*128 per block
     gptr_u4 sc;            // scales of blocks 0..7 of this row; + (i/8)*64
@@ -257,6 +234,46 @@ __device__ __forceinline__ void load_group(const RowPtrs &rp, int64_t g, u32x2 (
     for (int u = 0; u < 8; u++) wb[u] = rp.bits[(8 * g + u) * 128];
     s8 = rp.sc[g * 64];
 }
+
+// Eight blocks U0..U0+7 of the chunk: table reads of block u+1 are issued
+// before the arithmetic of block u consumes its own. With REFILL, block u's
+// register is reloaded with block u of group gn as soon as its table offsets
+// have been extracted, and the scales once the last d0 has been read, so the
+// next loads leave one block at a time instead of after the whole group.
+template <int H, int U0, bool REFILL>
+__device__ __forceinline__ void group8(const char *tab, u32x2 (&wb)[8], u32x4 &s8, float (&acc)[4],
+                                       const RowPtrs &rp, int64_t gn) {
+    float va[16], vb[16];
+    auto refill = [&](int u) {
+        if constexpr (REFILL) wb[u] = rp.bits[(8 * gn + u) * 128];
+    };
+    half_reads<H, U0 + 0>(tab, wb[0], va);
+    refill(0);
+    half_reads<H, U0 + 1>(tab, wb[1], vb);
+    refill(1);
+    half_math(va, d0_half<0>(s8), acc);
+    half_reads<H, U0 + 2>(tab, wb[2], va);
+    refill(2);
+    half_math(vb, d0_half<1>(s8), acc);
+    half_reads<H, U0 + 3>(tab, wb[3], vb);
+    refill(3);
+    half_math(va, d0_half<2>(s8), acc);
+    half_reads<H, U0 + 4>(tab, wb[4], va);
+    refill(4);
+    half_math(vb, d0_half<3>(s8), acc);
+    half_reads<H, U0 + 5>(tab, wb[5], vb);
+    refill(5);
+    half_math(va, d0_half<4>(s8), acc);
+    half_reads<H, U0 + 6>(tab, wb[6], va);
+    refill(6);
+    half_math(vb, d0_half<5>(s8), acc);
+    half_reads<H, U0 + 7>(tab, wb[7], vb);
+    refill(7);
+    half_math(va, d0_half<6>(s8), acc);
+    half_math(vb, d0_half<7>(s8), acc);
+    if constexpr (REFILL) s8 = rp.sc[gn * 64];
+}
+
 
 // One chunk of up to 32 blocks starting at group g0 (n4 full groups), with
 // the chunk's tables built in LDS. Straight-line code: three register
@@ -280,11 +297,10 @@ __device__ __forceinline__ void chunk(float *tab, const Q1Args &p, const RowPtrs
     if (g0 > 0) __syncthreads();
     table_store(tab, raw, cb);
     __syncthreads();
-    group8<H, 0>(tabc, w0, s0, acc);
-    load_group(rp, (g0 + 3 < gl) ? g0 + 3 : gl, w0, s0);
-    if (n4 > 1) group8<H, 8>(tabc, w1, s1, acc);
-    if (n4 > 2) group8<H, 16>(tabc, w2, s2, acc);
-    if (n4 > 3) group8<H, 24>(tabc, w0, s0, acc);
+    group8<H, 0, true>(tabc, w0, s0, acc, rp, (g0 + 3 < gl) ? g0 + 3 : gl);
+    if (n4 > 1) group8<H, 8, false>(tabc, w1, s1, acc, rp, 0);
+    if (n4 > 2) group8<H, 16, false>(tabc, w2, s2, acc, rp, 0);
+    if (n4 > 3) group8<H, 24, false>(tabc, w0, s0, acc, rp, 0);
 }
 
 // One block of half H at a run-time position (tail blocks past the last full

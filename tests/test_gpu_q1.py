@@ -157,6 +157,36 @@ def test_deterministic_repeat(gd):
     assert_bits_equal(outs[2], outs[0], "repeat 2")
 
 
+def test_grouped_graph_replay(gd):
+    """The grouped launch captured in a HIP graph (as the benchmark replays
+    it): four replays, with eager launches and host synchronisation between
+    them, each bit-exact with the oracle."""
+    rows, K, n = 1000, 4096, 6
+    W = wl.q1_weights_aos(rows, K, 21)
+    A = np.concatenate([wl.q8_acts_aos(K, 2100 + c) for c in range(n)])
+    b, s = planes_on_gpu(gd, W, rows, K)
+    a_dev = [dev(A[c]) for c in range(n)]
+    ys = [torch.full((rows,), float("nan"), device="cuda") for _ in range(n)]
+    probs = gd.make_q1_problems([(b, s, a_dev[c], ys[c]) for c in range(n)])
+    want = oracle.q1_q8_gemv_aos(W, A, rows, K, n_act=n, nthreads=oracle.max_threads())
+    gd.q1_q8_gemv_grouped(probs, n, rows, K)      # eager warm-up
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+        gd.q1_q8_gemv_grouped(probs, n, rows, K)
+    other = torch.empty(rows, device="cuda")
+    for rep in range(4):
+        for y in ys:
+            y.fill_(float("nan"))
+        gd.q1_q8_gemv(b, s, a_dev[rep % n], other, rows, K, 1)   # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = np.stack([y.cpu().numpy() for y in ys])
+        assert_bits_equal(got, want, f"replay {rep}")
+        assert_bits_equal(other.cpu().numpy(), want[rep % n], f"eager between replays {rep}")
+
+
 def test_validation_errors_raise(gd):
     b, s = gd.q1_alloc_planes(64, 128)
     y = torch.empty(64, device="cuda")
