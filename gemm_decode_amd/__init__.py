@@ -59,7 +59,8 @@ def _declare():
         "q1_repack": [_P, _I64, _I64, _P, _P, _P],
         "q1_q8_gemv": [_P, _P, _P, _P, _I64, _I64, _I64, _P],
         "q1_q8_gemv_grouped": [_P, _I64, _I64, _I64, _P],
-        "q1_sign_gemm": [_P, _P, _P, _P, _I64, _I64, _I64, _P],
+        "q1_sign_gemm": [_P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_size_t, _P],
+        "q1_sign_gemm_workspace_bytes": [_I64, _I64, _I64, ctypes.POINTER(ctypes.c_size_t)],
         "blockq8_matmul_nt": [_P, _P, _P, _P, _I64, _I64, _I64, _P],
         "ternary_act_bitplanes": [_P, _I64, _I64, _P, _P],
         "ternary_gemv": [_P, _P, _F32, _P, _F32, _P, _P, _I64, _I64, _P],
@@ -161,13 +162,35 @@ def make_q1_problems(entries, device="cuda"):
 
 # --------------------------------------------------------- sign-bit GEMM
 
-def q1_sign_gemm(x, w_bits, w_scales, y, M: int, N: int, K: int):
+def q1_sign_gemm_workspace_bytes(M: int, N: int, K: int) -> int:
+    out = ctypes.c_size_t()
+    _check(_lib.q1_sign_gemm_workspace_bytes(M, N, K, ctypes.byref(out)))
+    return out.value
+
+
+_sign_ws = {}
+
+
+def q1_sign_gemm(x, w_bits, w_scales, y, M: int, N: int, K: int, workspace=None):
+    """y = x @ w^T for sign-bit weights. `workspace` (a uint8 CUDA tensor of
+    at least q1_sign_gemm_workspace_bytes(M, N, K)) defaults to one cached per
+    device, grown as needed and shared by every call on that device that
+    passes none: pass your own to run calls on several streams at once."""
     import torch
     G = K // 32 if K % 32 == 0 else -1
+    if workspace is None:
+        need = q1_sign_gemm_workspace_bytes(M, N, K) if G > 0 else 16
+        dev = x.device
+        ws = _sign_ws.get(dev)
+        if ws is None or ws.numel() < need:
+            ws = torch.empty(need, dtype=torch.uint8, device=dev)
+            _sign_ws[dev] = ws
+        workspace = ws
     _check(_lib.q1_sign_gemm(_dev(x, torch.float32, M * K, "x"),
                              _dev(w_bits, torch.int32, N * G if G > 0 else None, "w_bits"),
                              _dev(w_scales, torch.float32, N * G if G > 0 else None, "w_scales"),
-                             _dev(y, torch.float32, M * N, "y"), M, N, K, _stream()))
+                             _dev(y, torch.float32, M * N, "y"), M, N, K,
+                             _dev(workspace, torch.uint8, None, "workspace"), workspace.numel(), _stream()))
 
 
 # ------------------------------------------------------ block-Q8 matmul_nt

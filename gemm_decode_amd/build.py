@@ -23,6 +23,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",  # MFMA results in VGPRs, not AGPRs read back one by one
     "-fno-fast-math", "-ffp-contract=off",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]

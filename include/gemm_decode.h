@@ -53,7 +53,7 @@ const char *gemm_decode_status_string(int status);
 const char *gemm_decode_last_error(void);
 /* ABI version of this header (incremented on incompatible changes). */
 int gemm_decode_abi_version(void);
-#define GEMM_DECODE_ABI_VERSION 1
+#define GEMM_DECODE_ABI_VERSION 2
 
 /* ====================================================================
  * Q1_0 . q8_0  ("browseml-gpu.js": header comment "The arithmetic, as the
@@ -146,17 +146,32 @@ int q1_q8_gemv_grouped(const gd_q1_problem *problems, int64_t count,
  * bit 0 -> -1.0; prefill is the compute-bound M-token case)
  * ====================================================================
  *   y[m][n] = sum_g scales[n][g] * sum_{j<32} x[m][32g+j] * (bit_j ? +1 : -1)
- *   x       device f32 [M][K] row-major, 16-byte aligned, |x| < 65504
- *           (the product runs on fp16 matrix cores with x split into a
- *           high and a low fp16 part; relative error ~1e-7 of ||y||_inf).
+ *   x       device f32 [M][K] row-major, 16-byte aligned, finite. The
+ *           product runs on fp16 matrix cores: each row is scaled by a
+ *           power of two that brings its largest |x| into [2^14, 2^15) and
+ *           split into a high and a low fp16 part (the scaling is undone
+ *           exactly on y); relative error ~1e-7 of ||y||_inf.
  *   w_bits  device u32 [N][K/32], bit j of word g = weight 32g+j (LSB
- *           first), 16-byte aligned.
- *   w_scales device f32 [N][K/32], 16-byte aligned.
- *   y       device f32 [M][N], 16-byte aligned.
+ *           first), 4-byte aligned.
+ *   w_scales device f32 [N][K/32], 4-byte aligned.
+ *   y       device f32 [M][N], 4-byte aligned.
+ *   workspace  device scratch of at least q1_sign_gemm_workspace_bytes(M,
+ *           N, K) bytes, 16-byte aligned, owned by the caller. A first
+ *           kernel writes the split activations and the weights regrouped
+ *           by pairs of groups into it for the second; calls that share it
+ *           must be ordered on one stream. Its contents on entry do not
+ *           matter and on return are unspecified.
  * Requires K % 32 == 0. Errors: GD_EINVAL, GD_ESHAPE, GD_EALIGN, GD_ERANGE
- * (M, N or K/32 above 2^31 - 1), GD_EHIP. */
+ * (M, N or K above 2^31 - 1, workspace too small), GD_EHIP. */
 int q1_sign_gemm(const float *x, const uint32_t *w_bits, const float *w_scales,
-                 float *y, int64_t M, int64_t N, int64_t K, void *stream);
+                 float *y, int64_t M, int64_t N, int64_t K,
+                 void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes q1_sign_gemm needs: 4*K per token (tokens padded to a
+ * multiple of 16) plus 4 per padded token, plus 16 per output and pair of
+ * 32-weight groups (ceil(K/64) pairs). Host only. Errors: GD_EINVAL,
+ * GD_ESHAPE (K % 32 != 0), GD_ERANGE. */
+int q1_sign_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t *bytes);
 
 /* ====================================================================
  * Block-scaled int8 matmul_nt  ("block_q8_matmul_nt.wgsl": PACKING,

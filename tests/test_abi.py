@@ -26,6 +26,7 @@ def gd():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ["q1_planes_bytes", "q1_repack", "q1_q8_gemv", "q1_q8_gemv_grouped", "q1_sign_gemm",
+              "q1_sign_gemm_workspace_bytes",
               "blockq8_matmul_nt", "ternary_act_bitplanes", "ternary_gemv", "ternary_gemv_grouped",
               "gemm_decode_status_string", "gemm_decode_last_error", "gemm_decode_abi_version",
               "gemm_decode_fill", "gemm_decode_stream_read"]:
@@ -36,7 +37,7 @@ def test_library_exports_every_declared_symbol(gd):
     lib = ctypes.CDLL(gd.LIB_PATH)
     missing = [n for n in declared_functions() if not hasattr(lib, n)]
     assert not missing, missing
-    assert lib.gemm_decode_abi_version() == 1
+    assert lib.gemm_decode_abi_version() == 2
 
 
 def test_status_strings(gd):
@@ -82,10 +83,21 @@ def test_validation_without_gpu(gd):
     assert L.q1_q8_gemv_grouped(FAKE, 65536, 4, 128, None) == E["range"]
     assert L.q1_q8_gemv_grouped(FAKE + 4, 1, 4, 128, None) == E["align"]
     # sign-bit GEMM
-    assert L.q1_sign_gemm(FAKE, FAKE, FAKE, FAKE, 4, 4, 100, None) == E["shape"]
-    assert L.q1_sign_gemm(None, FAKE, FAKE, FAKE, 4, 4, 128, None) == E["inval"]
-    assert L.q1_sign_gemm(FAKE + 4, FAKE, FAKE, FAKE, 4, 4, 128, None) == E["align"]
-    assert L.q1_sign_gemm(FAKE, FAKE, FAKE, FAKE, 0, 4, 128, None) == E["inval"]
+    WS = 1 << 20
+    assert L.q1_sign_gemm(FAKE, FAKE, FAKE, FAKE, 4, 4, 100, FAKE, WS, None) == E["shape"]
+    assert L.q1_sign_gemm(None, FAKE, FAKE, FAKE, 4, 4, 128, FAKE, WS, None) == E["inval"]
+    assert L.q1_sign_gemm(FAKE, FAKE, FAKE, FAKE, 4, 4, 128, None, WS, None) == E["inval"]
+    assert L.q1_sign_gemm(FAKE + 4, FAKE, FAKE, FAKE, 4, 4, 128, FAKE, WS, None) == E["align"]
+    assert L.q1_sign_gemm(FAKE, FAKE, FAKE, FAKE, 4, 4, 128, FAKE + 8, WS, None) == E["align"]
+    assert L.q1_sign_gemm(FAKE, FAKE, FAKE, FAKE, 0, 4, 128, FAKE, WS, None) == E["inval"]
+    # workspace: 4*K bytes per token (padded to 16), 4 per padded token, 16 per output and group pair
+    ws = ctypes.c_size_t()
+    assert L.q1_sign_gemm_workspace_bytes(17, 5, 128, ctypes.byref(ws)) == 0
+    assert ws.value == 32 * 128 * 4 + 32 * 4 + 5 * 2 * 16
+    assert L.q1_sign_gemm_workspace_bytes(17, 5, 96, ctypes.byref(ws)) == 0
+    assert ws.value == 32 * 96 * 4 + 32 * 4 + 5 * 2 * 16
+    assert L.q1_sign_gemm_workspace_bytes(17, 5, 100, ctypes.byref(ws)) == E["shape"]
+    assert L.q1_sign_gemm(FAKE, FAKE, FAKE, FAKE, 17, 5, 128, FAKE, 32 * 128 * 4, None) == E["range"]
     # block-Q8
     assert L.blockq8_matmul_nt(FAKE, FAKE, FAKE, FAKE, 1, 100, 4, None) == E["shape"]
     assert L.blockq8_matmul_nt(FAKE, FAKE, FAKE, FAKE, 1, 960, 0, None) == E["inval"]

@@ -78,3 +78,42 @@ def test_all_ones_row_sums(gd):
     y = run(gd, x, bits, np.ones((N, K // 32), dtype=np.float32))
     want = x.astype(np.float64).sum(axis=1)
     assert np.max(np.abs(y - want[:, None])) <= 1e-5 * np.max(np.abs(want))
+
+
+def test_row_magnitudes(gd):
+    """Token rows 40 decades apart and an all-zero row: each output row meets
+    the bar against its own largest value, and the zero row is 0."""
+    M, N, K = 7, 150, 512
+    x, bits, scales = wl.sign_gemm_inputs(M, N, K, seed=9)
+    mags = np.array([1e-20, 1e-4, 1.0, 1e4, 7e4, 1e20, 0.0])
+    x = (x.astype(np.float64) * mags[:, None]).astype(np.float32)
+    y = run(gd, x, bits, scales)
+    want = oracle.sign_gemm_f64(x, bits, scales)
+    for r in range(M):
+        if mags[r] == 0.0:
+            assert np.all(y[r] == 0.0)
+        else:
+            assert rel_err(y[r:r + 1], want[r:r + 1]) <= TOL, r
+
+
+def test_explicit_workspace_and_reuse(gd):
+    """A caller-owned workspace of exactly the reported size gives the same
+    bits as the cached one, and reusing it for a second, smaller call on the
+    same stream leaves no trace of the first."""
+    M, N, K = 100, 200, 640
+    need = gd.q1_sign_gemm_workspace_bytes(M, N, K)
+    assert need == 112 * K * 4 + 112 * 4 + N * (K // 64) * 16
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    x, bits, scales = wl.sign_gemm_inputs(M, N, K, seed=3)
+    y1 = torch.empty(M * N, device="cuda")
+    gd.q1_sign_gemm(dev(x), dev(bits.view(np.int32)), dev(scales), y1, M, N, K, workspace=ws)
+    y0 = run(gd, x, bits, scales)
+    torch.cuda.synchronize()
+    assert np.array_equal(y1.cpu().numpy().reshape(M, N), y0)
+    x2, bits2, scales2 = wl.sign_gemm_inputs(20, 40, 96, seed=4)
+    y2 = torch.empty(20 * 40, device="cuda")
+    gd.q1_sign_gemm(dev(x2), dev(bits2.view(np.int32)), dev(scales2), y2, 20, 40, 96, workspace=ws)
+    torch.cuda.synchronize()
+    assert rel_err(y2.cpu().numpy().reshape(20, 40), oracle.sign_gemm_f64(x2, bits2, scales2)) <= TOL
+    with pytest.raises(gd.GemmDecodeError):
+        gd.q1_sign_gemm(dev(x), dev(bits.view(np.int32)), dev(scales), y1, M, N, K, workspace=ws[:need - 16])
