@@ -481,32 +481,38 @@ def bench_ternary(args, gd, torch):
     torch.cuda.synchronize()
     step_bytes = step_w_bytes + sum(shapes[j][1] + shapes[j][0] * 4 + 8 for j in range(len(shapes)))
 
-    def step(kk, ev=None):
+    def step(kk):
         sset = slots[kk % n_sets]
-        if ev is not None:
-            ev[0].record()
         for K, xd in x_by_K.items():
             gd.ternary_act_bitplanes(xd, xd.shape[0], K, planes_by_K[K])
-        if ev is not None:
-            ev[1].record()
         for sh, idx in groups.items():
             gd.ternary_gemv_grouped(sset[sh], len(idx), sh[0], sh[1])
-        if ev is not None:
-            ev[2].record()
 
     for w in range(3):
         step(w)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.aux_steps)]
+    # timed steps: launches queued back to back, events only at the ends
     t0, t1 = _events(torch)
     t0.record()
     for kk in range(args.aux_steps):
-        step(3 + kk, evs[kk])
+        step(3 + kk)
     t1.record()
     torch.cuda.synchronize()
     total = t0.elapsed_time(t1) / 1e3 / args.aux_steps
-    gemv_s = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) / 1e3
-    gemv_bytes = step_w_bytes + sum(shapes[j][0] * 4 + 8 * (shapes[j][1] // 32) * 4 for j in range(len(shapes)))
+    # GEMV kernels alone: each shape's grouped launch, reps back to back over
+    # the weight sets, between two events
+    reps = 8
+    gemv_s = 0.0
+    for sh, idx in groups.items():
+        for kk in range(2):
+            gd.ternary_gemv_grouped(slots[kk % n_sets][sh], len(idx), sh[0], sh[1])
+        a0, a1 = _events(torch)
+        a0.record()
+        for kk in range(reps):
+            gd.ternary_gemv_grouped(slots[kk % n_sets][sh], len(idx), sh[0], sh[1])
+        a1.record()
+        torch.cuda.synchronize()
+        gemv_s += a0.elapsed_time(a1) / 1e3 / reps
     gbps = step_bytes / total / 1e9
     # parity: three GEMVs (one per shape), every row, against the oracle
     mism = 0
@@ -534,7 +540,7 @@ def bench_ternary(args, gd, torch):
         "pct_of_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "roofline": {"bound": "hbm", "achieved": round(gemv_bytes / gemv_s / 1e9, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(gemv_bytes / gemv_s / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": "ternary_gemv_grouped_kernel (3 launches per step)",
+                     "kernel": "ternary_held_grouped_kernel (3 launches per step, one per shape)",
                      "bytes_per_step_gemv": gemv_bytes},
         "step_bytes": step_bytes, "ring_sets": n_sets,
         "parity_mismatches_3_gemvs": mism,

@@ -11,7 +11,9 @@
 // i.e. one bit-select and one popcount-accumulate per plane per 32 weights.
 // An element with P and N both set contributes 0 here, as in w = P - N.
 //
-// Mapping. Eight lanes share a row and split its K range in 16-byte pieces
+// Mapping (general kernel; the held-row kernel below covers K % 128 == 0,
+// K <= 8192 with all of a lane's loads issued at once). Eight lanes share a
+// row and split its K range in 16-byte pieces
 // (integer sums are associative, so the split is exact); a wave covers eight
 // rows and reads 128 contiguous bytes of each. The activation planes are
 // copied once per workgroup into LDS, where the eight lanes of a row read
@@ -141,6 +143,113 @@ __global__ __launch_bounds__(kThreads) void ternary_gemv_grouped_kernel(const gd
     ternary_body(a, xl, rows, W);
 }
 
+// ----------------------------------------------------- held-row GEMV
+// For K % 128 == 0 and K <= 8192 (NIT = K/1024 rounded up <= 8 sixteen-byte
+// pieces per lane): a workgroup of kHeldThreads covers kHeldRows rows in one
+// pass, eight lanes per row, and every lane issues the loads of all its
+// pieces of P and N before counting, so a wave keeps 2*NIT 1 KiB loads in
+// flight. Pieces past the row end read a clamped (valid) address and count
+// as zero words.
+constexpr int kHeldThreads = 512;
+constexpr int kHeldRows = kHeldThreads / kLanesPerRow;   // 64
+constexpr int kHeldMaxIt = 8;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef const u32x4 __attribute__((address_space(1))) *g_u4;
+
+template <int NIT>
+__device__ __forceinline__ void ternary_held_body(const TernArgs &a, uint32_t *xl, int64_t rows, int64_t W) {
+    const int lane = threadIdx.x % kLanesPerRow;
+    const int rsub = threadIdx.x / kLanesPerRow;
+    const int64_t r = static_cast<int64_t>(blockIdx.x) * kHeldRows + rsub;
+    const int64_t rc = r < rows ? r : rows - 1;                 // clamped: loads valid, never stored
+    const g_u4 Pr = (g_u4)(a.P + rc * W), Nr = (g_u4)(a.N + rc * W);
+    u32x4 pv[NIT], nv[NIT];
+#pragma unroll
+    for (int it = 0; it < NIT; it++) {                          // all loads first
+        int64_t w4 = lane + kLanesPerRow * it;                  // 16-byte piece index in the row
+        w4 = w4 < W / 4 ? w4 : W / 4 - 1;
+        pv[it] = Pr[w4];
+        nv[it] = Nr[w4];
+    }
+    // stage the planes into LDS while the weight loads are in flight
+    for (int64_t i = threadIdx.x; i < 8 * W; i += kHeldThreads) xl[i] = a.X[i];
+    __syncthreads();
+    uint32_t cnt[8] = {0, 0, 0, 0, 0, 0, 0, 0}, cn = 0;
+#pragma unroll
+    for (int it = 0; it < NIT; it++) {
+        const int64_t w0 = 4 * (lane + kLanesPerRow * it);
+        const bool live = w0 < W;
+        const u32x4 p4 = live ? pv[it] : u32x4{0u, 0u, 0u, 0u};
+        const u32x4 n4 = live ? nv[it] : u32x4{0u, 0u, 0u, 0u};
+        const int64_t wx = live ? w0 : 0;
+#pragma unroll
+        for (int b = 0; b < 8; b++) {
+            const uint4 x4 = *reinterpret_cast<const uint4 *>(xl + b * W + wx);
+            const uint32_t xb[4] = {x4.x, x4.y, x4.z, x4.w};
+#pragma unroll
+            for (int q = 0; q < 4; q++) cnt[b] += __builtin_popcount((p4[q] & xb[q]) | (n4[q] & ~xb[q]));
+        }
+#pragma unroll
+        for (int q = 0; q < 4; q++) cn += __builtin_popcount(n4[q]);
+    }
+    int32_t part = static_cast<int32_t>(cn) - 128 * static_cast<int32_t>(cnt[7]);
+#pragma unroll
+    for (int b = 0; b < 7; b++) part += static_cast<int32_t>(cnt[b]) << b;
+    part += __shfl_xor(part, 1, kLanesPerRow);
+    part += __shfl_xor(part, 2, kLanesPerRow);
+    part += __shfl_xor(part, 4, kLanesPerRow);
+    if (lane == 0 && r < rows) {
+        const float s = a.w_scale * a.x_scale;
+        a.y[r] = static_cast<float>(part) * s;
+        if (a.dot) a.dot[r] = part;
+    }
+}
+
+template <int NIT>
+__global__ __launch_bounds__(kHeldThreads) void ternary_held_kernel(TernArgs a, int64_t rows, int64_t W) {
+    extern __shared__ uint32_t xl[];
+    ternary_held_body<NIT>(a, xl, rows, W);
+}
+
+template <int NIT>
+__global__ __launch_bounds__(kHeldThreads) void ternary_held_grouped_kernel(const gd_ternary_problem *probs,
+                                                                            int64_t rows, int64_t W) {
+    extern __shared__ uint32_t xl[];
+    const gd_ternary_problem pr = probs[blockIdx.y];
+    TernArgs a{pr.w_pos, pr.w_neg, pr.x_planes, pr.y, pr.dot_out, pr.w_scale, pr.x_scale};
+    ternary_held_body<NIT>(a, xl, rows, W);
+}
+
+// Launch the held-row kernel for W = K/32 (W % 4 == 0, W <= 256); false if
+// the shape does not qualify. `grouped` selects the problem-array form.
+template <int NIT>
+void launch_held_n(bool grouped, const TernArgs &a, const gd_ternary_problem *probs, int64_t count, int64_t rows,
+                   int64_t W, hipStream_t st) {
+    const dim3 grid(static_cast<uint32_t>((rows + kHeldRows - 1) / kHeldRows), static_cast<uint32_t>(count));
+    const size_t lds = static_cast<size_t>(8 * W * 4);
+    if (grouped)
+        hipLaunchKernelGGL(ternary_held_grouped_kernel<NIT>, grid, dim3(kHeldThreads), lds, st, probs, rows, W);
+    else
+        hipLaunchKernelGGL(ternary_held_kernel<NIT>, grid, dim3(kHeldThreads), lds, st, a, rows, W);
+}
+
+bool launch_held(bool grouped, const TernArgs &a, const gd_ternary_problem *probs, int64_t count, int64_t rows,
+                 int64_t W, hipStream_t st) {
+    if (W % 4 != 0 || W > 32 * kHeldMaxIt) return false;
+    switch ((W + 31) / 32) {
+        case 1: launch_held_n<1>(grouped, a, probs, count, rows, W, st); return true;
+        case 2: launch_held_n<2>(grouped, a, probs, count, rows, W, st); return true;
+        case 3: launch_held_n<3>(grouped, a, probs, count, rows, W, st); return true;
+        case 4: launch_held_n<4>(grouped, a, probs, count, rows, W, st); return true;
+        case 5: launch_held_n<5>(grouped, a, probs, count, rows, W, st); return true;
+        case 6: launch_held_n<6>(grouped, a, probs, count, rows, W, st); return true;
+        case 7: launch_held_n<7>(grouped, a, probs, count, rows, W, st); return true;
+        case 8: launch_held_n<8>(grouped, a, probs, count, rows, W, st); return true;
+        default: return false;
+    }
+}
+
 int check_shape(int64_t rows, int64_t K) {
     GD_REQUIRE(rows >= 1 && K >= 1, GD_EINVAL, "rows (%lld) and K (%lld) must be >= 1", (long long)rows,
                (long long)K);
@@ -183,6 +292,7 @@ extern "C" int ternary_gemv(const uint32_t *w_pos, const uint32_t *w_neg, float 
     const size_t lds = lds_bytes(K);
     GD_REQUIRE(lds <= 64 * 1024, GD_ERANGE, "ternary_gemv: K too large for the LDS plane stage");
     TernArgs a{w_pos, w_neg, x_planes, y, dot_out, w_scale, x_scale};
+    if (launch_held(false, a, nullptr, 1, rows, W, as_stream(stream))) return check_launch("ternary_gemv");
     const int64_t gx = (rows + kRowsPerWG - 1) / kRowsPerWG;
     hipLaunchKernelGGL(ternary_gemv_kernel, dim3(static_cast<uint32_t>(gx)), dim3(kThreads), lds,
                        as_stream(stream), a, rows, W);
@@ -200,6 +310,8 @@ extern "C" int ternary_gemv_grouped(const gd_ternary_problem *problems, int64_t 
     const int64_t W = K / 32;
     const size_t lds = lds_bytes(K);
     GD_REQUIRE(lds <= 64 * 1024, GD_ERANGE, "ternary_gemv_grouped: K too large for the LDS plane stage");
+    if (launch_held(true, TernArgs{}, problems, count, rows, W, as_stream(stream)))
+        return check_launch("ternary_gemv_grouped");
     const int64_t gx = (rows + kRowsPerWG - 1) / kRowsPerWG;
     hipLaunchKernelGGL(ternary_gemv_grouped_kernel, dim3(static_cast<uint32_t>(gx), static_cast<uint32_t>(count)),
                        dim3(kThreads), lds, as_stream(stream), problems, rows, W);

@@ -63,7 +63,8 @@ def test_bitplanes_match_definition(gd, K):
     assert np.array_equal(xp.cpu().numpy().view(np.uint32).reshape(8, -1), planes_ref(xq))
 
 
-@pytest.mark.parametrize("rows,K", [(2560, 2560), (6912, 2560), (2560, 6912), (1, 32), (37, 96), (200, 4000)])
+@pytest.mark.parametrize("rows,K", [(2560, 2560), (6912, 2560), (2560, 6912), (1, 32), (37, 96), (200, 4000),
+                                    (100, 128), (65, 1152), (64, 8192), (10, 8320)])
 def test_gemv_bit_exact(gd, rows, K):
     P, N, ws, xq, xs = wl.ternary_inputs(rows, K, seed=rows + K)
     _, y, d = run(gd, P, N, ws, xq, xs)
