@@ -114,20 +114,19 @@ def bench_q1(args, gd, torch):
         gd.q1_repack(torch.from_numpy(W.reshape(-1)).cuda(), s.rows, s.K, b, sc)
         base.append((b, sc))
     ys = [[torch.empty(s.rows, dtype=torch.float32, device="cuda") for _ in range(n_vec)] for s in shapes]
-    slots = []     # slots[r][shape] = (problems tensor, keep-alive list)
+    # slots[r]: the step's problems over the r-th set of plane copies, one
+    # grouped launch per weight shape (32 problems each)
+    slots = []
     for r in range(ring):
-        per_shape = []
-        for si, s in enumerate(shapes):
-            copies = [(base[si][0].clone(), base[si][1].clone()) for _ in range(n_vec)]
-            probs = gd.make_q1_problems([(copies[c][0], copies[c][1], a_dev[c], ys[si][c])
-                                         for c in range(n_vec)])
-            per_shape.append((probs, copies))
-        slots.append(per_shape)
+        copies = [[(base[si][0].clone(), base[si][1].clone()) for _ in range(n_vec)] for si in range(len(shapes))]
+        per_shape = [gd.make_q1_problems([(copies[si][c][0], copies[si][c][1], a_dev[c], ys[si][c])
+                                          for c in range(n_vec)]) for si in range(len(shapes))]
+        slots.append({"shape": per_shape, "copies": copies})
     torch.cuda.synchronize()
 
     def step(r):
         for si, s in enumerate(shapes):
-            gd.q1_q8_gemv_grouped(slots[r][si][0], n_vec, s.rows, s.K)
+            gd.q1_q8_gemv_grouped(slots[r]["shape"][si], n_vec, s.rows, s.K)
 
     # parity spot check (untimed): every output of the first ring slot
     step(0)
@@ -183,24 +182,25 @@ def bench_q1(args, gd, torch):
     wall = time.perf_counter() - wall0
     total_s = t0.elapsed_time(t1) / 1e3
 
-    # Roofline: mean duration of each grouped kernel, from HIP events on the
-    # launch stream around `per_shape` back-to-back launches of that kernel
-    # alone (ring slots in turn), after the same number untimed.
-    per_shape = 8 * ring
-    launch_bytes = [n_vec * q1_gemv_bytes(s.rows, s.K) for s in shapes]
-    per_launch = []
-    for si, s in enumerate(shapes):
-        def run_shape(si=si, s=s):
-            for j in range(per_shape):
-                gd.q1_q8_gemv_grouped(slots[j % ring][si][0], n_vec, s.rows, s.K)
-        run_shape()
+    # Roofline: mean duration of each shape's grouped kernel, from HIP events
+    # on the launch stream around `reps` back-to-back launches (ring slots in
+    # turn), after the same number untimed.
+    reps = 8 * ring
+
+    def timed(fn):
+        fn()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
-        run_shape()
+        fn()
         e1.record()
         torch.cuda.synchronize()
-        per_launch.append(e0.elapsed_time(e1) / 1e3 / per_shape)
+        return e0.elapsed_time(e1) / 1e3 / reps
+
+    per_launch = [timed(lambda si=si, s=s: [gd.q1_q8_gemv_grouped(slots[j % ring]["shape"][si], n_vec, s.rows, s.K)
+                                            for j in range(reps)])
+                  for si, s in enumerate(shapes)]
+    launch_bytes = [n_vec * q1_gemv_bytes(s.rows, s.K) for s in shapes]
     kern_s = sum(per_launch)
     achieved = sum(launch_bytes) / kern_s / 1e9
 
@@ -213,7 +213,7 @@ def bench_q1(args, gd, torch):
         for r in range(min(2, ring)):     # warm
             for si, s in enumerate(shapes):
                 for c in range(n_vec):
-                    b, sc = slots[r][si][1][c]
+                    b, sc = slots[r]["copies"][si][c]
                     gd.q1_q8_gemv(b, sc, a_dev[c], ys[si][c], s.rows, s.K, 1)
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
@@ -223,7 +223,7 @@ def bench_q1(args, gd, torch):
             r = k % ring
             for si, s in enumerate(shapes):
                 for c in range(n_vec):
-                    b, sc = slots[r][si][1][c]
+                    b, sc = slots[r]["copies"][si][c]
                     gd.q1_q8_gemv(b, sc, a_dev[c], ys[si][c], s.rows, s.K, 1)
         e1.record()
         torch.cuda.synchronize()
@@ -268,9 +268,9 @@ def bench_q1(args, gd, torch):
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
             "kernel": "q1_gemv_grouped_kernel",
-            "per_shape_us": {f"{s.rows}x{s.K}": round(per_launch[si] * 1e6, 2) for si, s in enumerate(shapes)},
-            "timing": f"HIP events around {per_shape} back-to-back launches of one shape",
+            "us_per_launch": {f"{s.rows}x{s.K}": round(per_launch[si] * 1e6, 2) for si, s in enumerate(shapes)},
             "bytes_per_launch": {f"{s.rows}x{s.K}": launch_bytes[si] for si, s in enumerate(shapes)},
+            "timing": f"HIP events around {reps} back-to-back launches of one shape",
         },
         "parity_mismatches": mism,
         "serial_one_launch_per_gemv": serial,
@@ -315,22 +315,20 @@ def _events(torch):
 
 
 def _time_launches(torch, launch, n, warmup):
-    """Mean per-launch time (s) from HIP events around each launch, and the
-    total (s) between the first and last event."""
+    """Mean time (s) per launch of n launches queued back to back between two
+    HIP events on the launch stream (no event between launches, so the mean
+    is the kernel's own duration plus the hardware's dispatch gap)."""
     for w in range(warmup):
         launch(w)
     torch.cuda.synchronize()
-    evs = [_events(torch) for _ in range(n)]
     t0, t1 = _events(torch)
     t0.record()
     for k in range(n):
-        evs[k][0].record()
         launch(warmup + k)
-        evs[k][1].record()
     t1.record()
     torch.cuda.synchronize()
-    per = [a.elapsed_time(b) / 1e3 for a, b in evs]
-    return float(np.mean(per)), t0.elapsed_time(t1) / 1e3
+    total = t0.elapsed_time(t1) / 1e3
+    return total / n, total
 
 
 def bench_sign(args, gd, torch):

@@ -38,7 +38,7 @@ class GemmDecodeError(RuntimeError):
 
 class Q1Problem(ctypes.Structure):
     """gd_q1_problem: one batch-1 problem of q1_q8_gemv_grouped."""
-    _fields_ = [("bits_plane", _P), ("scale_plane", _P), ("a_q8", _P), ("y", _P)]
+    _fields_ = [("bits_plane", _P), ("scale_plane", _P), ("a_q8", _P), ("y", _P), ("rows", _I64)]
 
 
 class TernaryProblem(ctypes.Structure):
@@ -151,11 +151,13 @@ def q1_q8_gemv_grouped(problems, count: int, rows: int, K: int):
 
 
 def make_q1_problems(entries, device="cuda"):
-    """Device array of gd_q1_problem from [(bits_plane, scale_plane, a_q8, y), ...]."""
+    """Device array of gd_q1_problem from [(bits_plane, scale_plane, a_q8, y[, rows]), ...]
+    (rows 0 or absent: the launch's rows)."""
     import torch
     arr = (Q1Problem * len(entries))()
-    for i, (b, s, a, y) in enumerate(entries):
-        arr[i] = Q1Problem(b.data_ptr(), s.data_ptr(), a.data_ptr(), y.data_ptr())
+    for i, e in enumerate(entries):
+        b, s, a, y = e[:4]
+        arr[i] = Q1Problem(b.data_ptr(), s.data_ptr(), a.data_ptr(), y.data_ptr(), e[4] if len(e) > 4 else 0)
     host = torch.frombuffer(bytearray(bytes(arr)), dtype=torch.uint8)
     return host.to(device)
 

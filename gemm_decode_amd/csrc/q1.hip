@@ -394,9 +394,11 @@ __global__ __launch_bounds__(kThreads) void q1_gemv_grouped_kernel(const gd_q1_p
                                                                    int64_t nb, int64_t nb8) {
     __shared__ float tab[kTableFloats];
     const gd_q1_problem pr = probs[blockIdx.y];
+    const int64_t prow = (pr.rows >= 1 && pr.rows <= rows) ? pr.rows : rows;
+    if (static_cast<int64_t>(blockIdx.x) * kRowsPerWG >= prow) return;   // uniform: before any barrier
     Q1Args p{static_cast<const uint32_t *>(pr.bits_plane), static_cast<const uint4 *>(pr.scale_plane),
              static_cast<const uint16_t *>(pr.a_q8), pr.y};
-    q1_gemv_body(p, tab, rows, nb, nb8);
+    q1_gemv_body(p, tab, prow, nb, nb8);
 }
 
 // ------------------------------------------------------------ validation

@@ -122,18 +122,23 @@ int q1_q8_gemv(const void *bits_plane, const void *scale_plane, const void *a_q8
 
 /* One independent batch-1 problem of a grouped launch. */
 typedef struct gd_q1_problem {
-    const void *bits_plane;   /* device Q1 bits plane, 16-byte aligned   */
-    const void *scale_plane;  /* device Q1 scale plane, 16-byte aligned  */
-    const void *a_q8;         /* device q8_0 activation (one column)     */
-    float *y;                 /* device f32 [rows]                        */
+    const void *bits_plane;   /* device Q1 bits plane, 16-byte aligned     */
+    const void *scale_plane;  /* device Q1 scale plane, 16-byte aligned    */
+    const void *a_q8;         /* device q8_0 activation (one column)       */
+    float *y;                 /* device f32 [its rows]                      */
+    int64_t rows;             /* its rows, 1 .. the launch's rows; 0 (or a
+                                 value outside that range) means the
+                                 launch's rows. Planes are sized for it.   */
 } gd_q1_problem;
 
-/* `count` independent batch-1 Q1_0 . q8_0 GEMVs of one shape (rows x K) in
- * one launch, each with its own weights, activation and output; the same
- * kernel body and the same bits as q1_q8_gemv with n_act = 1.
+/* `count` independent batch-1 Q1_0 . q8_0 GEMVs with a common K in one
+ * launch, each with its own weights, row count, activation and output; the
+ * same kernel body and the same bits as q1_q8_gemv with n_act = 1.
  *   problems  device array of `count` gd_q1_problem, 8-byte aligned. The
- *             pointers inside it are read by the kernel and cannot be
- *             validated by the host: they must satisfy q1_q8_gemv's rules.
+ *             pointers and row counts inside it are read by the kernel and
+ *             cannot be validated by the host: they must satisfy
+ *             q1_q8_gemv's rules for that problem's rows.
+ *   rows      the largest row count of the problems (sets the grid).
  * Limits: 1 <= count <= 65535. Errors: GD_EINVAL, GD_ESHAPE, GD_EALIGN,
  * GD_ERANGE, GD_EHIP. */
 int q1_q8_gemv_grouped(const gd_q1_problem *problems, int64_t count,

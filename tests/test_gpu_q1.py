@@ -157,6 +157,31 @@ def test_deterministic_repeat(gd):
     assert_bits_equal(outs[2], outs[0], "repeat 2")
 
 
+def test_grouped_mixed_rows(gd):
+    """One grouped launch over problems of different row counts (common K):
+    each output bit-exact with the oracle for its own shape, nothing written
+    past a problem's rows, and rows = 0 meaning the launch's rows."""
+    K, rows_max = 1024, 1000
+    shapes = [(1000, 1000), (300, 300), (65, 65), (1000, 0), (1, 1), (257, 257)]   # (rows, field)
+    entries, keep, wants = [], [], []
+    for i, (rows, field) in enumerate(shapes):
+        W = wl.q1_weights_aos(rows, K, 40 + i)
+        A = wl.q8_acts_aos(K, 4000 + i)
+        b, s = planes_on_gpu(gd, W, rows, K)
+        a = dev(A.reshape(-1))
+        y = torch.full((rows + 64,), float("nan"), device="cuda")      # 64 guard elements
+        entries.append((b, s, a, y, field))
+        keep.append((b, s, a, y, rows))
+        wants.append(oracle.q1_q8_gemv_aos(W, A, rows, K, nthreads=oracle.max_threads()))
+    probs = gd.make_q1_problems(entries)
+    gd.q1_q8_gemv_grouped(probs, len(entries), rows_max, K)
+    torch.cuda.synchronize()
+    for (b, s, a, y, rows), want in zip(keep, wants):
+        got = y.cpu().numpy()
+        assert_bits_equal(got[:rows], want.reshape(-1), f"rows {rows}")
+        assert np.all(np.isnan(got[rows:])), f"rows {rows}: wrote past its rows"
+
+
 def test_grouped_graph_replay(gd):
     """The grouped launch captured in a HIP graph (as the benchmark replays
     it): four replays, with eager launches and host synchronisation between
