@@ -38,6 +38,31 @@ MODEL_8B_Q1_BYTES = 8e9 * 18 / 128   # 8B weights at 18 bytes per 128 -> bytes p
 METRIC = "Q1_0·q8_0 GEMV effective HBM GB/s (% of peak) + equiv tok/s, batch 1"
 
 
+# HBM bytes per launch from rocprofv3 counters (2 x FETCH_SIZE + WRITE_SIZE,
+# the factors read off a streaming read and a fill of known size), valid for
+# the kernel source they were measured on: reported only while its hash
+# matches, null after any change to it.
+_TRAFFIC = {
+    "q1": ("q1.hip", "d7e3682a6799afc1",
+           {"4096x4096": (37732.8, 512.0), "14336x4096": (129959.6, 1792.0)}),
+    "ternary": ("ternary.hip", "91879f9a6f9284ff",
+                {"2560x2560": (97281.8, 1200.0), "6912x2560": (130259.4, 1620.0), "2560x6912": (65832.3, 300.0)}),
+    "blockq8": ("blockq8.hip", "f95d58bedf096572", {"m1": (35445.7, 207.1), "m16": (26266.3, 3072.0)}),
+    "sign": ("sign_gemm.hip", "850acc3ab2e1ded4",
+             {"split": (4128.6, 8208.0), "wpack": (2074.0, 4096.0), "gemm": (21355.3, 9728.0)}),
+}
+
+
+def measured_traffic(path: str):
+    """{launch: HBM bytes} for one path, or None if its source has changed."""
+    import hashlib
+    src, sha, launches = _TRAFFIC[path]
+    with open(os.path.join(ROOT, "gemm_decode_amd", "csrc", src), "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest()[:16] != sha:
+            return None
+    return {k: int(round((2.0 * fetch + write) * 1024)) for k, (fetch, write) in launches.items()}
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -201,36 +226,46 @@ def bench_q1(args, gd, torch):
                                             for j in range(reps)])
                   for si, s in enumerate(shapes)]
     launch_bytes = [n_vec * q1_gemv_bytes(s.rows, s.K) for s in shapes]
+    q1_traffic = measured_traffic("q1")
     kern_s = sum(per_launch)
     achieved = sum(launch_bytes) / kern_s / 1e9
 
     gbps = step_bytes * args.steps / total_s / 1e9
     ms_per_step = total_s / args.steps * 1e3
 
-    # serial mode: one launch per GEMV, back to back (decode-schedule figure)
+    # serial mode: one launch per GEMV (the decode schedule), the step's 64
+    # launches captured in a HIP graph per ring slot and replayed back to back
     serial = None
     if args.serial_steps > 0:
-        for r in range(min(2, ring)):     # warm
+        def one_step(r):
             for si, s in enumerate(shapes):
                 for c in range(n_vec):
                     b, sc = slots[r]["copies"][si][c]
                     gd.q1_q8_gemv(b, sc, a_dev[c], ys[si][c], s.rows, s.K, 1)
+        one_step(0)
+        torch.cuda.synchronize()
+        sgraphs = []
+        for r in range(ring):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+                one_step(r)
+            sgraphs.append(g)
+        for g in sgraphs:
+            g.replay()
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
         for k in range(args.serial_steps):
-            r = k % ring
-            for si, s in enumerate(shapes):
-                for c in range(n_vec):
-                    b, sc = slots[r]["copies"][si][c]
-                    gd.q1_q8_gemv(b, sc, a_dev[c], ys[si][c], s.rows, s.K, 1)
+            sgraphs[k % ring].replay()
         e1.record()
         torch.cuda.synchronize()
         ser_s = e0.elapsed_time(e1) / 1e3
         serial = {"GBps": round(step_bytes * args.serial_steps / ser_s / 1e9, 1),
                   "us_per_gemv": round(ser_s / (args.serial_steps * 2 * n_vec) * 1e6, 3),
-                  "launches": args.serial_steps * 2 * n_vec}
+                  "launches": args.serial_steps * 2 * n_vec,
+                  "timing": "one HIP graph of the step's 64 single-GEMV launches per ring slot"}
+        del sgraphs
 
     ceiling = (measured_read_ceiling(gd, torch, gib=args.ceiling_gib, passes=args.ceiling_passes,
                                      reps=args.ceiling_reps) if args.ceiling else None)
@@ -266,7 +301,9 @@ def bench_q1(args, gd, torch):
         "rows_K_per_s": round(sum(n_vec * s.rows * s.K for s in shapes) * args.steps / total_s, 1),
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None if q1_traffic is None else sum(q1_traffic.values()),
+            "traffic_per_launch": q1_traffic,
             "kernel": "q1_gemv_grouped_kernel",
             "us_per_launch": {f"{s.rows}x{s.K}": round(per_launch[si] * 1e6, 2) for si, s in enumerate(shapes)},
             "bytes_per_launch": {f"{s.rows}x{s.K}": launch_bytes[si] for si, s in enumerate(shapes)},
@@ -315,16 +352,22 @@ def _events(torch):
 
 
 def _time_launches(torch, launch, n, warmup):
-    """Mean time (s) per launch of n launches queued back to back between two
-    HIP events on the launch stream (no event between launches, so the mean
-    is the kernel's own duration plus the hardware's dispatch gap)."""
+    """Mean time (s) per launch of n launches captured in one HIP graph and
+    replayed between two HIP events on the launch stream: the launches run
+    back to back whatever the host's launch rate (a kernel shorter than a
+    Python launch would otherwise leave the GPU idle between launches)."""
     for w in range(warmup):
         launch(w)
     torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+        for k in range(n):
+            launch(warmup + k)
+    g.replay()
+    torch.cuda.synchronize()
     t0, t1 = _events(torch)
     t0.record()
-    for k in range(n):
-        launch(warmup + k)
+    g.replay()
     t1.record()
     torch.cuda.synchronize()
     total = t0.elapsed_time(t1) / 1e3
@@ -351,6 +394,7 @@ def bench_sign(args, gd, torch):
     per, _ = _time_launches(torch, launch, args.aux_steps, 3)
     flops = 2.0 * M * N * K
     tflops = flops / per / 1e12
+    sg_traffic = measured_traffic("sign")
     # parity on a sample of columns
     y = sets[(3 + args.aux_steps - 1) % ring][3].cpu().numpy().reshape(M, N)
     cols = np.arange(0, N, 64)
@@ -371,8 +415,11 @@ def bench_sign(args, gd, torch):
         "us_per_gemm": round(per * 1e6, 2), "prefill_tok_s": round(M / per, 1),
         "issued_mfma_TFLOPs": round(2 * tflops, 2),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
-                     "kernel": "sign_gemm_kernel", "flops_per_launch": flops},
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
+                     "traffic": None if sg_traffic is None else sum(sg_traffic.values()),
+                     "traffic_per_kernel": sg_traffic,
+                     "kernel": "q1_sign_gemm call (sign_split, sign_wpack, sign_gemm kernels)",
+                     "flops_per_launch": flops},
         "parity_rel_err_sampled": rel,
         "cpu_baseline": {"value": round(cpu_gflops / 1e3, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
                          "sample": f"{rows_done} of 512 rows x all 4096 columns (f64 oracle), {t_used:.2f} s"},
@@ -392,6 +439,7 @@ def bench_blockq8(args, gd, torch):
     qd = torch.from_numpy(quants.view(np.int32)).cuda()
     sd = torch.from_numpy(scales).cuda()
     copies = [(qd.clone(), sd.clone()) for _ in range(ring)]
+    bq_traffic = measured_traffic("blockq8")
     for m in c["ms"]:
         x = np.ascontiguousarray(x_all[:m])
         xd = torch.from_numpy(x).cuda()
@@ -421,7 +469,9 @@ def bench_blockq8(args, gd, torch):
             "metric": "effective HBM GB/s", "value": round(gbps, 1), "unit": "GB/s",
             "us_per_launch": round(per * 1e6, 2), "pct_of_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
             "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "blockq8_valu_kernel",
+                         "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                         "traffic": None if bq_traffic is None else bq_traffic[f"m{m}"],
+                         "kernel": "blockq8_gemv_kernel" if m == 1 else "blockq8_mfma_kernel<32>",
                          "bytes_per_launch": bytes_},
             "parity_rel_err_sampled": rel,
             "cpu_baseline": {"value": round(cpu_bytes / t_used / 1e9, 4), "unit": "GB/s", "cores": threads,
@@ -511,6 +561,9 @@ def bench_ternary(args, gd, torch):
         a1.record()
         torch.cuda.synchronize()
         gemv_s += a0.elapsed_time(a1) / 1e3 / reps
+    # GEMV bytes of a step: both weight planes, the activation planes, y
+    gemv_bytes = step_w_bytes + sum(shapes[j][0] * 4 + 8 * (shapes[j][1] // 32) * 4 for j in range(len(shapes)))
+    tern_traffic = measured_traffic("ternary")
     gbps = step_bytes / total / 1e9
     # parity: three GEMVs (one per shape), every row, against the oracle
     mism = 0
@@ -537,7 +590,9 @@ def bench_ternary(args, gd, torch):
         "context_tok_s_at_0.69GB": round(gbps / 0.69, 1),
         "pct_of_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "roofline": {"bound": "hbm", "achieved": round(gemv_bytes / gemv_s / 1e9, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(gemv_bytes / gemv_s / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(gemv_bytes / gemv_s / 1e9 / HBM_PEAK_GBPS, 4),
+                     "traffic": None if tern_traffic is None else sum(tern_traffic.values()),
+                     "traffic_per_launch": tern_traffic,
                      "kernel": "ternary_held_grouped_kernel (3 launches per step, one per shape)",
                      "bytes_per_step_gemv": gemv_bytes},
         "step_bytes": step_bytes, "ring_sets": n_sets,
