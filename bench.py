@@ -342,6 +342,61 @@ def cpu_baseline_q1(Ws, A, shapes, budget_s: float):
                       f"cycling), {t_used:.2f} s of oracle time, OpenMP over rows, {cpu_model()}"}
 
 
+# ------------------------------------------- Q1 small-M (several columns)
+
+def bench_q1_mm(args, gd, torch):
+    """Q1_0.q8_0 with several activation columns (P1's multi-column Q1_MM,
+    the prompt side of the same method) on the 14336x4096 decode weight: the
+    columns share one read of the weights and keep the bits of their own
+    batch-1 GEMVs. Weight copies rotate over a ring > 1 GiB."""
+    import oracle
+    cfg = wl.Q1_DECODE[1]
+    rows, K = cfg.rows, cfg.K
+    W = wl.q1_weights_aos(rows, K, cfg.weight_seed)
+    b0, s0 = gd.q1_alloc_planes(rows, K)
+    gd.q1_repack(torch.from_numpy(W.reshape(-1)).cuda(), rows, K, b0, s0)
+    plane = sum(gd.q1_planes_bytes(rows, K))
+    ring = max(2, int(np.ceil(1.05 * (1 << 30) / plane)))
+    copies = [(b0.clone(), s0.clone()) for _ in range(ring)]
+    w_bytes = rows * (K // 128) * 18
+    out = {}
+    for M in (2, 4, 8):
+        A = np.concatenate([wl.q8_acts_aos(K, sd) for sd in cfg.act_seeds[:M]])
+        a = torch.from_numpy(np.ascontiguousarray(A.reshape(-1))).cuda()
+        y = torch.empty(M * rows, device="cuda")
+
+        def launch(k, a=a, y=y, M=M):
+            bb, ss = copies[k % ring]
+            gd.q1_q8_gemv(bb, ss, a, y, rows, K, M)
+        per, _ = _time_launches(torch, launch, args.aux_steps, 3)
+        got = y.cpu().numpy().reshape(M, rows)
+        sample = np.arange(0, rows, 37)
+        want = oracle.q1_q8_gemv_aos(W[sample], A, len(sample), K, n_act=M, nthreads=cpu_cores())
+        mism = int((got[:, sample].view(np.uint32) != want.reshape(M, -1).view(np.uint32)).sum())
+        launch_bytes = w_bytes + M * ((K // 32) * 34 + rows * 4)
+        threads = cpu_cores()
+        t = time.perf_counter()
+        n_cpu = 512
+        oracle.q1_q8_gemv_aos(W[:n_cpu], A, n_cpu, K, n_act=M, nthreads=threads)
+        t_cpu = time.perf_counter() - t
+        out[f"m{M}"] = {
+            "workload": f"Q1_0.q8_0 small-M: {M} activation columns x 14336x4096 weight",
+            "metric": "HBM GB/s (weights read once)", "value": round(launch_bytes / per / 1e9, 1), "unit": "GB/s",
+            "us_per_launch": round(per * 1e6, 2),
+            "gemv_equivalent_GBps": round(M * q1_gemv_bytes(rows, K) / per / 1e9, 1),
+            "token_rows_K_per_s": round(M * rows * K / per, 1),
+            "roofline": {"bound": "hbm", "achieved": round(launch_bytes / per / 1e9, 1), "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": round(launch_bytes / per / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None,
+                         "kernel": f"q1_gemv_mc_kernel<{2 if M <= 2 else 4 if M <= 4 else 8}>",
+                         "bytes_per_launch": launch_bytes},
+            "parity_mismatches_sampled": mism, "parity_sample": f"every 37th row ({len(sample)} rows) x {M} columns",
+            "cpu_baseline": {"value": round(M * n_cpu * (K // 128) * 18 / t_cpu / 1e9, 4), "unit": "GB/s (GEMV-equivalent)",
+                             "cores": threads, "kind": "oracle",
+                             "sample": f"first {n_cpu} rows x {M} columns, {t_cpu:.2f} s"},
+        }
+    return out
+
+
 # ------------------------------------------------- secondary workloads
 
 MFMA_F16_PEAK_TFLOPS = 2500.0    # MI355X dense fp16 matrix peak
@@ -610,7 +665,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="all", choices=["all", "q1", "sign", "blockq8", "ternary"],
+    ap.add_argument("--workload", default="all", choices=["all", "q1", "q1mm", "sign", "blockq8", "ternary"],
                     help="all (default): the Q1 metric line plus the other paths under 'workloads'")
     ap.add_argument("--aux-steps", type=int, default=20, help="timed launches for the other paths")
     ap.add_argument("--aux-cpu-seconds", type=float, default=4.0)
@@ -652,6 +707,9 @@ def main():
         if args.workload in ("all", "blockq8"):
             log("[bench] block-Q8 matmul_nt")
             extra["blockq8"] = bench_blockq8(args, gd, torch)
+        if args.workload in ("all", "q1mm"):
+            log("[bench] Q1 small-M (several columns)")
+            extra["q1_small_m"] = bench_q1_mm(args, gd, torch)
         if args.workload in ("all", "ternary"):
             log("[bench] ternary decode step")
             extra["ternary_step"] = bench_ternary(args, gd, torch)

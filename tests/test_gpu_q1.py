@@ -94,6 +94,36 @@ def test_ragged_and_chunked_shapes(gd, rows, K, seed):
     assert_bits_equal(y, oracle.q1_q8_gemv_aos(W, A, rows, K, nthreads=8), f"rows={rows} K={K}")
 
 
+@pytest.mark.parametrize("n_act", [2, 3, 4, 5, 7, 8, 9, 16])
+@pytest.mark.parametrize("rows,K", [(65, 128), (300, 1152), (257, 4608), (64, 8192)])
+def test_multi_column_bit_exact(gd, n_act, rows, K):
+    """Several activation columns against one weight (the small-M product):
+    columns share one read of the weights in groups of 2, 4 or 8; K covers
+    one block, short last chunks and several chunk pairs; every column must
+    carry the bits of its own batch-1 GEMV."""
+    W = wl.q1_weights_aos(rows, K, rows + K)
+    A = np.concatenate([wl.q8_acts_aos(K, 7000 + 31 * c + K) for c in range(n_act)])
+    got = run_gemv(gd, W, A, rows, K, n_act)
+    want = oracle.q1_q8_gemv_aos(W, A, rows, K, n_act=n_act, nthreads=oracle.max_threads())
+    assert_bits_equal(got.reshape(n_act, rows), want.reshape(n_act, rows), f"n_act={n_act} {rows}x{K}")
+
+
+@pytest.mark.parametrize("rows,K,n_act", [
+    (14329, 4096, 16),   # 56 row blocks: groups of 4 columns
+    (14329, 4096, 29),   # groups of 8, the last one partial (5 columns)
+    (12289, 1152, 16),   # 49 row blocks, 9 blocks per row: groups of 4, short chunks
+    (12289, 1152, 40),   # groups of 8, short chunks
+])
+def test_multi_column_wide_groups(gd, rows, K, n_act):
+    """Shapes whose row count makes the 4- and 8-column kernels the ones
+    chosen; every column bit-exact with its own batch-1 GEMV."""
+    W = wl.q1_weights_aos(rows, K, 11 + n_act)
+    A = np.concatenate([wl.q8_acts_aos(K, 9000 + c) for c in range(n_act)])
+    got = run_gemv(gd, W, A, rows, K, n_act)
+    want = oracle.q1_q8_gemv_aos(W, A, rows, K, n_act=n_act, nthreads=oracle.max_threads())
+    assert_bits_equal(got.reshape(n_act, rows), want.reshape(n_act, rows), f"n_act={n_act} {rows}x{K}")
+
+
 def test_special_scales_and_bits(gd):
     """Subnormal, zero and large d0/d1, all-ones and all-zeros sign bits."""
     rows, K = 128, 1024
