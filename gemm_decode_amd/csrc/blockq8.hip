@@ -90,11 +90,12 @@ __global__ __launch_bounds__(kThreads) void blockq8_valu_kernel(const float *__r
 // Decode GEMV (one activation row). Thirty-two lanes share an output
 // feature; lane j owns chunks c = j + 32t (t < kCPL) of 16 quants, the same
 // positions in every row, so its slice of x (up to 32 floats) and each
-// chunk's sum of x stay in registers and no LDS is needed. Quant bytes are
+// chunk's sum of x stay in registers for all its rows. Quant bytes are
 // read as unsigned u = q + 128 (q xor 0x80, then v_cvt_f32_ubyte) and the
-// bias is removed once per chunk: sum x*q = sum x*u - 128*sum x. A wave
-// covers two rows per step and keeps the loads of the next three steps in
-// flight (four register sets rotated by name).
+// bias is removed once per chunk: sum x*q = sum x*u - 128*sum x. x is read
+// from HBM once per workgroup into LDS. A wave covers two rows per step and
+// keeps the loads of the next three steps in flight (four register sets
+// rotated by name).
 constexpr int kLPR = 32;                // lanes per row
 constexpr int kCPL = 2;                 // chunks per lane: k <= 16*kLPR*kCPL = 1024
 constexpr int kGemvThreads = 256;
@@ -135,10 +136,15 @@ __global__ __launch_bounds__(kGemvThreads) void blockq8_gemv_kernel(const float 
             b.s[t] = scales[r * bpr + c / 2];
         }
     };
+    // x once per workgroup into LDS (read before the quant loads, which the
+    // in-order load counter would otherwise make it wait for)
+    __shared__ f32x4 xl[kLPR * kCPL * 4];                    // k <= 1024 floats
+    for (int i = threadIdx.x; i < chunks * 4; i += kGemvThreads) xl[i] = xq[i];
     RowBuf b0, b1, b2, b3;
     load(0, b0);
     load(1, b1);
     load(2, b2);
+    __syncthreads();
 
     float xv[kCPL][16], xs[kCPL];
 #pragma unroll
@@ -149,7 +155,7 @@ __global__ __launch_bounds__(kGemvThreads) void blockq8_gemv_kernel(const float 
         xs[t] = 0.0f;
 #pragma unroll
         for (int v = 0; v < 4; v++) {
-            const f32x4 w = xq[cc * 4 + v];
+            const f32x4 w = xl[cc * 4 + v];
 #pragma unroll
             for (int e = 0; e < 4; e++) {
                 xv[t][4 * v + e] = w[e] * keep;
