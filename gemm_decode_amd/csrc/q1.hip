@@ -32,6 +32,10 @@ constexpr int kRowsPerWG = 256;
 constexpr int kChunkBlocks = 32;          // blocks whose tables fit in LDS
 constexpr int kTableFloats = kChunkBlocks * 32 * 16;   // 64 KiB
 constexpr int kGroupsPerThread = kChunkBlocks * 32 / kThreads;   // 2
+// A single GEMV of up to this many 256-row blocks takes the one-chain-per-
+// thread kernel (latency); larger ones fill the chip with 256-row blocks.
+constexpr int64_t kLatMaxRowBlocks = 64;
+constexpr int64_t kLatWideRows = 8192;
 
 // Pointers into device global memory (address space 1), so weight loads are
 // global_load (counted by vmcnt only), not flat loads that also hold lgkmcnt.
@@ -94,21 +98,26 @@ __global__ void q1_repack_kernel(const uint16_t *__restrict__ w_aos, uint32_t *_
 }
 
 // ------------------------------------------------------------ tables (a2)
-// Group g = (i_local*4 + k)*8 + l of a chunk holds 16 floats. Each thread
-// owns two groups (g = tid + 512j). The build is split so its activation
+// Group g = (i_local*4 + k)*8 + l of a chunk holds 16 floats. With NT
+// threads, thread tid owns groups g = tid + NT*j. The build is split so its activation
 // loads can be issued ahead of the weight prefetch (the load counter is in
 // order: waiting for loads issued after the prefetch would drain it).
-struct TableRaw {
-    uint32_t d[kGroupsPerThread], q01[kGroupsPerThread], q23[kGroupsPerThread];
+// NT threads build a chunk, 1024 / NT groups each.
+template <int NT>
+struct TableRawN {
+    static constexpr int NG = kChunkBlocks * 32 / NT;
+    uint32_t d[NG], q01[NG], q23[NG];
 };
+typedef TableRawN<kThreads> TableRaw;
 
-__device__ __forceinline__ void table_loads(TableRaw &raw, const uint16_t *a_generic, int64_t c0, int cb) {
+template <int NT = kThreads>
+__device__ __forceinline__ void table_loads(TableRawN<NT> &raw, const uint16_t *a_generic, int64_t c0, int cb) {
     // C-style cast: an address-space cast from the generic pointer
     const auto a = (const uint16_t __attribute__((address_space(1))) *)a_generic;
     const int ng = cb * 32;
 #pragma unroll
-    for (int j = 0; j < kGroupsPerThread; j++) {
-        int g = threadIdx.x + kThreads * j;
+    for (int j = 0; j < TableRawN<NT>::NG; j++) {
+        int g = threadIdx.x + NT * j;
         g = g < ng ? g : ng - 1;                  // clamped: computed, never stored
         const int il = g >> 5, k = (g >> 3) & 3, l = g & 7;
         const auto blk = a + ((c0 + il) * 4 + k) * 17;   // 34 bytes = 17 halves
@@ -121,11 +130,12 @@ __device__ __forceinline__ void table_loads(TableRaw &raw, const uint16_t *a_gen
 // Entries: T[0] = d1*s(0) and T[n] = T[n without its lowest set bit] +
 // d1*delta(lowest bit). Every partial value is d1 times an integer of
 // magnitude <= 512, so each add is exact and T[n] = d1*s(n) bit for bit.
-__device__ __forceinline__ void table_store(float *tab, const TableRaw &raw, int cb) {
+template <int NT = kThreads>
+__device__ __forceinline__ void table_store(float *tab, const TableRawN<NT> &raw, int cb) {
     const int ng = cb * 32;
 #pragma unroll
-    for (int j = 0; j < kGroupsPerThread; j++) {
-        const int g = threadIdx.x + kThreads * j;
+    for (int j = 0; j < TableRawN<NT>::NG; j++) {
+        const int g = threadIdx.x + NT * j;
         const float d1 = f16_to_f32(static_cast<uint16_t>(raw.d[j]));
         const int32_t q[4] = {static_cast<int8_t>(raw.q01[j] & 0xff), static_cast<int8_t>(raw.q01[j] >> 8),
                               static_cast<int8_t>(raw.q23[j] & 0xff), static_cast<int8_t>(raw.q23[j] >> 8)};
@@ -588,6 +598,179 @@ __global__ __launch_bounds__(kThreads) void q1_gemv_mc_kernel(const uint32_t *bi
     }
 }
 
+// -------------------------------------------------- one GEMV, few rows
+// A lone GEMV with few row tiles (a decode step's projection) leaves most
+// CUs idle under the 256-row mapping, and each of its threads walks four
+// chains through every block. Here a thread runs ONE chain l of one row: a
+// wave covers 16 rows and the four chains of half H (lanes 16j..16j+15 run
+// chain 4H + j), and a workgroup of WAVES waves covers 8*WAVES rows, so the
+// same GEMV occupies 4-16 times more waves with a quarter of the arithmetic
+// each. The chain order, and so every bit, is that of the kernels above.
+// A chain's byte of each weight word is lane-dependent, so its offsets come
+// from a rotate by a per-lane amount and one and-or that also adds the
+// chain's table base; the block and sub-block parts stay immediate offsets.
+// Every load of a 32-block chunk is issued at once: weights, their scales
+// and the next chunk's activations, the weights of the next chunk refilled
+// into each block's registers as soon as that block's offsets are taken.
+struct LatLane {
+    uint32_t sh0, sh1;   // rotate amounts: sub-blocks 2m and 2m+1 of word m
+    uint32_t lbase;      // byte offset of this chain's tables within a sub-block
+};
+
+// (w rotated right by sh) & 0x3c, or-ed with the table base: the nibble's
+// byte offset, pre-shifted by 2. One v_and_or_b32 (the compiler would turn
+// the or into an add and split it in two).
+__device__ __forceinline__ uint32_t lat_off(uint32_t w, uint32_t sh, uint32_t lbase) {
+    const uint32_t rot = __builtin_amdgcn_alignbit(w, w, sh);
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, 60, %2" : "=v"(r) : "v"(rot), "v"(lbase));
+    return r;
+}
+
+// The four table reads of chunk block u for this lane's chain (u is a
+// constant in every unrolled use, so its part of the offset is immediate).
+__device__ __forceinline__ void lat_reads(const char *tab, int u, const u32x2 &wb, const LatLane &ln,
+                                          float (&v)[4]) {
+    const char *t = tab + u * 2048;
+    v[0] = *reinterpret_cast<const float *>(t + 0 * 512 + lat_off(wb.x, ln.sh0, ln.lbase));
+    v[1] = *reinterpret_cast<const float *>(t + 1 * 512 + lat_off(wb.x, ln.sh1, ln.lbase));
+    v[2] = *reinterpret_cast<const float *>(t + 2 * 512 + lat_off(wb.y, ln.sh0, ln.lbase));
+    v[3] = *reinterpret_cast<const float *>(t + 3 * 512 + lat_off(wb.y, ln.sh1, ln.lbase));
+}
+
+__device__ __forceinline__ void lat_math(const float (&v)[4], float d0, float &acc) {
+    float ab = v[0];
+    ab = ab + v[1];
+    ab = ab + v[2];
+    ab = ab + v[3];
+    acc = __builtin_fmaf(d0, ab, acc);
+}
+
+struct LatBuf {
+    u32x2 w[kChunkBlocks];
+    u32x4 s[kChunkBlocks / 8];
+};
+
+// Block i of chunk c (clamped to the last block; scale groups to the last
+// padded group) into the register of slot u.
+__device__ __forceinline__ u32x2 lat_wload(const RowPtrs &rp, int64_t c, int u, int64_t nb) {
+    int64_t i = c * kChunkBlocks + u;
+    i = i < nb ? i : nb - 1;
+    return rp.bits[i * 128];
+}
+
+__device__ __forceinline__ u32x4 lat_sload(const RowPtrs &rp, int64_t c, int g, int64_t ng8) {
+    int64_t gi = c * (kChunkBlocks / 8) + g;
+    gi = gi < ng8 ? gi : ng8 - 1;
+    return rp.sc[gi * 64];
+}
+
+__device__ __forceinline__ void lat_load(const RowPtrs &rp, int64_t c, int64_t nb, int64_t ng8, LatBuf &b) {
+#pragma unroll
+    for (int u = 0; u < kChunkBlocks; u++) b.w[u] = lat_wload(rp, c, u, nb);
+#pragma unroll
+    for (int g = 0; g < kChunkBlocks / 8; g++) b.s[g] = lat_sload(rp, c, g, ng8);
+}
+
+// A full chunk in straight-line code: the reads of block u+2 are issued
+// before block u's arithmetic (the scheduler would otherwise batch each
+// block's reads with its own arithmetic and wait for them); with REFILL,
+// block u's register then takes block u of chunk cn, and a scale group's
+// register its successor once its last d0 has been read.
+template <bool REFILL>
+__device__ __forceinline__ void lat_chunk(const char *tab, LatBuf &b, const LatLane &ln, float &acc,
+                                          const RowPtrs &rp, int64_t cn, int64_t nb, int64_t ng8) {
+    constexpr int D = 2;   // blocks of read lookahead
+    float v[D + 1][4];
+#pragma unroll
+    for (int u = 0; u < D; u++) lat_reads(tab, u, b.w[u], ln, v[u]);
+#pragma unroll
+    for (int u = 0; u < kChunkBlocks; u++) {
+        if (u + D < kChunkBlocks) lat_reads(tab, u + D, b.w[u + D], ln, v[(u + D) % (D + 1)]);
+        if constexpr (REFILL) b.w[u] = lat_wload(rp, cn, u, nb);
+        __builtin_amdgcn_sched_barrier(0);
+        lat_math(v[u % (D + 1)], d0_of(b.s[u / 8], u % 8), acc);
+        if constexpr (REFILL) {
+            if (u % 8 == 7) b.s[u / 8] = lat_sload(rp, cn, u / 8, ng8);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// The last chunk when it holds fewer than 32 blocks: the same steps, block
+// by block, guarded by the (uniform) block count.
+__device__ __forceinline__ void lat_chunk_short(const char *tab, const LatBuf &b, const LatLane &ln, float &acc,
+                                                int cb) {
+#pragma unroll
+    for (int u = 0; u < kChunkBlocks; u++) {
+        if (u < cb) {
+            float v[4];
+            lat_reads(tab, u, b.w[u], ln, v);
+            lat_math(v, d0_of(b.s[u / 8], u % 8), acc);
+        }
+    }
+}
+
+template <int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void q1_gemv_lat_kernel(const uint32_t *bits, const uint4 *scales,
+                                                                 const uint16_t *a, float *y, int64_t rows,
+                                                                 int64_t nb, int64_t nb8) {
+    constexpr int NT = WAVES * 64;
+    constexpr int R = 8 * WAVES;   // rows per workgroup
+    __shared__ float tab[kTableFloats];
+    __shared__ float xch[R * 8];
+    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+    const int h = wave & 1, j = lane >> 4;
+    const int rloc = (wave >> 1) * 16 + (lane & 15);
+    const int64_t r = static_cast<int64_t>(blockIdx.x) * R + rloc;
+    const int64_t r64 = (rows + 63) / 64 * 64;
+    const int64_t rl = r < r64 ? r : r64 - 1;   // padded rows: same work, never stored
+    const int64_t t = rl / 64, lnr = rl % 64;
+    const RowPtrs rp{(gptr_u2)bits + ((t * nb) * 2 + h) * 64 + lnr, (gptr_u4)scales + t * (nb8 / 8) * 64 + lnr};
+    const LatLane ln{static_cast<uint32_t>(8 * j), static_cast<uint32_t>(8 * j + 4),
+                     static_cast<uint32_t>((4 * h + j) * 64)};
+    const char *tabc = reinterpret_cast<const char *>(tab);
+    const int64_t nch = (nb + kChunkBlocks - 1) / kChunkBlocks, ng8 = nb8 / 8;
+    auto blocks_in = [&](int64_t c) {
+        const int64_t left = nb - c * kChunkBlocks;
+        return static_cast<int>(left < kChunkBlocks ? left : kChunkBlocks);
+    };
+
+    TableRawN<NT> raw;
+    table_loads<NT>(raw, a, 0, blocks_in(0));
+    asm volatile("" ::: "memory");   // activations first: the table build waits for them only
+    LatBuf b;
+    lat_load(rp, 0, nb, ng8, b);
+    table_store<NT>(tab, raw, blocks_in(0));
+    __syncthreads();
+    float acc = 0.0f;
+    for (int64_t c = 0; c < nch; c++) {
+        const int64_t cn = (c + 1 < nch) ? c + 1 : c;   // the next chunk, clamped
+        table_loads<NT>(raw, a, cn * kChunkBlocks, blocks_in(cn));
+        asm volatile("" ::: "memory");
+        const int cb = blocks_in(c);
+        if (cb < kChunkBlocks)
+            lat_chunk_short(tabc, b, ln, acc, cb);   // only ever the last chunk
+        else if (c + 1 < nch)
+            lat_chunk<true>(tabc, b, ln, acc, rp, cn, nb, ng8);
+        else
+            lat_chunk<false>(tabc, b, ln, acc, rp, cn, nb, ng8);
+        if (c + 1 < nch) {
+            __syncthreads();
+            table_store<NT>(tab, raw, blocks_in(cn));
+            __syncthreads();
+        }
+    }
+    // The eight chains of a row meet in LDS for the fixed final tree.
+    xch[rloc * 8 + 4 * h + j] = acc;
+    __syncthreads();
+    if (threadIdx.x < R) {
+        const int64_t ro = static_cast<int64_t>(blockIdx.x) * R + threadIdx.x;
+        const float *x = xch + threadIdx.x * 8;
+        if (ro < rows) y[ro] = ((x[0] + x[4]) + (x[2] + x[6])) + ((x[1] + x[5]) + (x[3] + x[7]));
+    }
+}
+
 // ------------------------------------------------------------ validation
 int plane_sizes(int64_t rows, int64_t K, int64_t *bits_bytes, int64_t *scale_bytes) {
     GD_REQUIRE(rows >= 1 && K >= 1, GD_EINVAL, "rows (%lld) and K (%lld) must be >= 1", (long long)rows,
@@ -672,6 +855,19 @@ extern "C" int q1_q8_gemv(const void *bits_plane, const void *scale_plane, const
             hipLaunchKernelGGL(q1_gemv_mc_kernel<4>, grid, dim3(kThreads), 0, hs, bp, sp, ap, y, rows, nb, nb8, n_act);
         else
             hipLaunchKernelGGL(q1_gemv_mc_kernel<8>, grid, dim3(kThreads), 0, hs, bp, sp, ap, y, rows, nb, nb8, n_act);
+        return check_launch("q1_q8_gemv");
+    }
+    if (gx <= kLatMaxRowBlocks) {
+        // One chain per thread. A wave is 16 rows whatever the workgroup, so
+        // 32-row workgroups (one wave per SIMD) until they would stack on the
+        // CUs, then 64-row ones, which build half as many tables.
+        if (rows >= kLatWideRows) {
+            hipLaunchKernelGGL(q1_gemv_lat_kernel<8>, dim3(static_cast<uint32_t>((rows + 63) / 64)), dim3(512), 0, hs,
+                               bp, sp, ap, y, rows, nb, nb8);
+        } else {
+            hipLaunchKernelGGL(q1_gemv_lat_kernel<4>, dim3(static_cast<uint32_t>((rows + 31) / 32)), dim3(256), 0, hs,
+                               bp, sp, ap, y, rows, nb, nb8);
+        }
         return check_launch("q1_q8_gemv");
     }
     hipLaunchKernelGGL(q1_gemv_kernel, dim3(static_cast<uint32_t>(gx), static_cast<uint32_t>(n_act)),

@@ -124,6 +124,31 @@ def test_multi_column_wide_groups(gd, rows, K, n_act):
     assert_bits_equal(got.reshape(n_act, rows), want.reshape(n_act, rows), f"n_act={n_act} {rows}x{K}")
 
 
+@pytest.mark.parametrize("rows,K", [
+    (4096, 4096),     # one chunk of 32 blocks, 32-row workgroups
+    (8191, 4224),     # a full chunk whose next chunk is one block long
+    (8192, 8192),     # 64-row workgroups, two full chunks
+    (14336, 4096),    # 64-row workgroups
+    (16384, 1152),    # the largest row count on the one-chain-per-thread kernel
+    (16385, 256),     # the first on the 256-row kernel
+    (20000, 4224),
+])
+def test_single_gemv_paths(gd, rows, K):
+    """Batch-1 GEMVs across both single-GEMV mappings (one chain per thread
+    for up to 64 row blocks of 256, four per thread above), bit-exact, and
+    nothing written past the last row."""
+    W = wl.q1_weights_aos(rows, K, rows % 97 + K)
+    A = wl.q8_acts_aos(K, 31 * rows + K)
+    b, s = planes_on_gpu(gd, W, rows, K)
+    y = torch.full((rows + 64,), float("nan"), dtype=torch.float32, device="cuda")
+    gd.q1_q8_gemv(b, s, dev(A.reshape(-1)), y[:rows], rows, K, 1)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy()
+    want = oracle.q1_q8_gemv_aos(W, A, rows, K, nthreads=oracle.max_threads())
+    assert_bits_equal(got[:rows], want.reshape(-1), f"{rows}x{K}")
+    assert np.all(np.isnan(got[rows:])), "wrote past the last row"
+
+
 def test_special_scales_and_bits(gd):
     """Subnormal, zero and large d0/d1, all-ones and all-zeros sign bits."""
     rows, K = 128, 1024
