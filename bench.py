@@ -536,6 +536,84 @@ def bench_blockq8(args, gd, torch):
     return out
 
 
+def bench_quant(args, gd, torch):
+    """On-device activation quantization (the step before each GEMV): q8_0
+    blocks for the Q1 path and per-token int8 bit planes for the ternary
+    path, at decode sizes (launch latency) and at a 256 MiB batch (HBM
+    roofline on 4 B read per element plus what is written)."""
+    import oracle
+    out = {}
+    threads = cpu_cores()
+
+    def measure(name, kind, shapes, copies_n):
+        """shapes: list of (count, K) launched back to back as one step."""
+        sets = []
+        for ci in range(copies_n):
+            entry = []
+            for si, (cnt, K) in enumerate(shapes):
+                rng = np.random.default_rng(1000 * ci + si)
+                x = torch.from_numpy(rng.standard_normal(size=(cnt, K), dtype=np.float32)).cuda()
+                if kind == "q8":
+                    o = (torch.empty(cnt * (K // 32) * 34, dtype=torch.uint8, device="cuda"),)
+                else:
+                    o = (torch.empty(cnt * 8 * (K // 32), dtype=torch.int32, device="cuda"),
+                         torch.empty(cnt, device="cuda"))
+                entry.append((x, o))
+            sets.append(entry)
+
+        def launch(kk):
+            for (cnt, K), (x, o) in zip(shapes, sets[kk % copies_n]):
+                if kind == "q8":
+                    gd.q8_0_quantize(x, o[0], cnt, K)
+                else:
+                    gd.ternary_quantize_act(x, cnt, K, o[0], o[1])
+        per, _ = _time_launches(torch, launch, args.aux_steps, 2)
+        bytes_ = sum(cnt * K * 4 + (cnt * (K // 32) * 34 if kind == "q8" else cnt * (K + 4)) for cnt, K in shapes)
+        gbps = bytes_ / per / 1e9
+        # parity on the first rows of the first set, and an oracle sample for the CPU baseline
+        mism = 0
+        t_used, done_bytes = 0.0, 0
+        for (cnt, K), (x, o) in zip(shapes, sets[0]):
+            r = min(cnt, 64)
+            xs = x[:r].cpu().numpy()
+            t = time.perf_counter()
+            if kind == "q8":
+                want = oracle.quantize_q8_0(xs)
+                t_used += time.perf_counter() - t
+                mism += int(np.count_nonzero(o[0][:r * (K // 32) * 34].cpu().numpy() != want))
+                done_bytes += r * K * 4 + r * (K // 32) * 34
+            else:
+                q, sc = oracle.quantize_absmax_int8(xs)
+                t_used += time.perf_counter() - t
+                got_s = o[1][:r].cpu().numpy()
+                u = q.view(np.uint8).astype(np.uint32).reshape(r, K // 32, 32)
+                planes = np.stack([(((u >> b) & 1) << np.arange(32, dtype=np.uint32)).sum(axis=2)
+                                   for b in range(8)], axis=1).astype(np.uint32)
+                got_p = o[0][:r * 8 * (K // 32)].cpu().numpy().view(np.uint32).reshape(r, 8, K // 32)
+                mism += int(np.count_nonzero(got_p != planes)) + int(np.count_nonzero(got_s != sc))
+                done_bytes += r * K * 4 + r * (K + 4)
+        out[name] = {
+            "workload": " + ".join(f"{cnt}x{K}" for cnt, K in shapes) + (" f32 -> q8_0" if kind == "q8"
+                                                                           else " f32 -> int8 planes"),
+            "metric": "effective HBM GB/s", "value": round(gbps, 1), "unit": "GB/s",
+            "us_per_step": round(per * 1e6, 2), "launches_per_step": len(shapes),
+            "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                         "kernel": "q8_0_quantize_kernel" if kind == "q8" else "act_quant_kernel",
+                         "bytes_per_step": bytes_},
+            "parity_mismatches_sampled": mism,
+            "cpu_baseline": {"value": round(done_bytes / max(t_used, 1e-9) / 1e9, 4), "unit": "GB/s",
+                             "cores": 1, "kind": "oracle",
+                             "sample": "first <= 64 rows of each shape, single-threaded oracle"},
+        }
+
+    measure("q8_0_decode", "q8", [(32, 4096)], 8)
+    measure("q8_0_batch_256MiB", "q8", [(16384, 4096)], 2)
+    measure("int8_planes_decode_step", "act", [(90, 2560), (30, 6912)], 8)
+    measure("int8_planes_batch_256MiB", "act", [(16384, 4096)], 2)
+    return out
+
+
 def bench_ternary(args, gd, torch):
     """BitNet-2B-like ternary decode step: 210 GEMVs (per layer 4 x 2560x2560,
     2 x 6912x2560, 1 x 2560x6912), each with its own activation vector (bit
@@ -665,7 +743,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="all", choices=["all", "q1", "q1mm", "sign", "blockq8", "ternary"],
+    ap.add_argument("--workload", default="all",
+                    choices=["all", "q1", "q1mm", "sign", "blockq8", "ternary", "quant"],
                     help="all (default): the Q1 metric line plus the other paths under 'workloads'")
     ap.add_argument("--aux-steps", type=int, default=20, help="timed launches for the other paths")
     ap.add_argument("--aux-cpu-seconds", type=float, default=4.0)
@@ -713,6 +792,9 @@ def main():
         if args.workload in ("all", "ternary"):
             log("[bench] ternary decode step")
             extra["ternary_step"] = bench_ternary(args, gd, torch)
+        if args.workload in ("all", "quant"):
+            log("[bench] activation quantization")
+            extra["act_quant"] = bench_quant(args, gd, torch)
         out["workloads"] = extra
     print(json.dumps(out), flush=True)
 

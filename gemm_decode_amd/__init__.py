@@ -44,7 +44,7 @@ class Q1Problem(ctypes.Structure):
 class TernaryProblem(ctypes.Structure):
     """gd_ternary_problem: one problem of ternary_gemv_grouped."""
     _fields_ = [("w_pos", _P), ("w_neg", _P), ("x_planes", _P), ("y", _P),
-                ("dot_out", _P), ("w_scale", _F32), ("x_scale", _F32)]
+                ("dot_out", _P), ("w_scale", _F32), ("x_scale", _F32), ("x_scale_dev", _P)]
 
 
 def _declare():
@@ -65,6 +65,8 @@ def _declare():
         "ternary_act_bitplanes": [_P, _I64, _I64, _P, _P],
         "ternary_gemv": [_P, _P, _F32, _P, _F32, _P, _P, _I64, _I64, _P],
         "ternary_gemv_grouped": [_P, _I64, _I64, _I64, _P],
+        "q8_0_quantize": [_P, _P, _I64, _I64, _P],
+        "ternary_quantize_act": [_P, _I64, _I64, _P, _P, _P],
         "gemm_decode_fill": [_P, ctypes.c_size_t, ctypes.c_uint32, _P],
         "gemm_decode_stream_read": [_P, ctypes.c_size_t, ctypes.c_int32, _P, _I64, _P],
     }
@@ -226,12 +228,17 @@ def ternary_gemv(w_pos, w_neg, w_scale: float, x_planes, x_scale: float, y, dot_
 
 def make_ternary_problems(entries, device="cuda"):
     """Device array of gd_ternary_problem from
-    [(w_pos, w_neg, x_planes, y, dot_out_or_None, w_scale, x_scale), ...]."""
+    [(w_pos, w_neg, x_planes, y, dot_out_or_None, w_scale, x_scale), ...];
+    x_scale is a float, or a one-element device f32 tensor (x_scale_dev)."""
     import torch
     arr = (TernaryProblem * len(entries))()
     for i, (p, n, xp, y, d, ws, xs) in enumerate(entries):
+        if isinstance(xs, torch.Tensor):
+            xs_val, xs_dev = 0.0, _dev(xs, torch.float32, None, "x_scale")
+        else:
+            xs_val, xs_dev = float(xs), None
         arr[i] = TernaryProblem(p.data_ptr(), n.data_ptr(), xp.data_ptr(), y.data_ptr(),
-                                None if d is None else d.data_ptr(), float(ws), float(xs))
+                                None if d is None else d.data_ptr(), float(ws), xs_val, xs_dev)
     host = torch.frombuffer(bytearray(bytes(arr)), dtype=torch.uint8)
     return host.to(device)
 
@@ -240,6 +247,26 @@ def ternary_gemv_grouped(problems, count: int, rows: int, K: int):
     import torch
     _check(_lib.ternary_gemv_grouped(
         _dev(problems, torch.uint8, count * ctypes.sizeof(TernaryProblem), "problems"), count, rows, K, _stream()))
+
+
+# ------------------------------------------------- activation quantization
+
+def q8_0_quantize(x, a_q8, n: int, K: int):
+    """f32 x [n, K] -> q8_0 blocks (uint8 [n * K/32 * 34]), on the device."""
+    import torch
+    _check(_lib.q8_0_quantize(_dev(x, torch.float32, n * K, "x"),
+                              _dev(a_q8, torch.uint8, n * (K // 32) * 34 if K % 32 == 0 else None, "a_q8"),
+                              n, K, _stream()))
+
+
+def ternary_quantize_act(x, count: int, K: int, planes, x_scale):
+    """f32 x [count, K] -> int8 bit planes (int32 [count * 8 * K/32]) and
+    scales (f32 [count]), on the device."""
+    import torch
+    _check(_lib.ternary_quantize_act(_dev(x, torch.float32, count * K, "x"), count, K,
+                                     _dev(planes, torch.int32, count * 8 * (K // 32) if K % 32 == 0 else None,
+                                          "planes"),
+                                     _dev(x_scale, torch.float32, count, "x_scale"), _stream()))
 
 
 # ------------------------------------------------------------ measurement

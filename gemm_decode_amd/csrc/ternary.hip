@@ -139,7 +139,8 @@ __global__ __launch_bounds__(kThreads) void ternary_gemv_grouped_kernel(const gd
                                                                         int64_t rows, int64_t W) {
     extern __shared__ uint32_t xl[];
     const gd_ternary_problem pr = probs[blockIdx.y];
-    TernArgs a{pr.w_pos, pr.w_neg, pr.x_planes, pr.y, pr.dot_out, pr.w_scale, pr.x_scale};
+    TernArgs a{pr.w_pos, pr.w_neg, pr.x_planes, pr.y, pr.dot_out, pr.w_scale,
+               pr.x_scale_dev ? *pr.x_scale_dev : pr.x_scale};
     ternary_body(a, xl, rows, W);
 }
 
@@ -217,7 +218,8 @@ __global__ __launch_bounds__(kHeldThreads) void ternary_held_grouped_kernel(cons
                                                                             int64_t rows, int64_t W) {
     extern __shared__ uint32_t xl[];
     const gd_ternary_problem pr = probs[blockIdx.y];
-    TernArgs a{pr.w_pos, pr.w_neg, pr.x_planes, pr.y, pr.dot_out, pr.w_scale, pr.x_scale};
+    TernArgs a{pr.w_pos, pr.w_neg, pr.x_planes, pr.y, pr.dot_out, pr.w_scale,
+               pr.x_scale_dev ? *pr.x_scale_dev : pr.x_scale};
     ternary_held_body<NIT>(a, xl, rows, W);
 }
 

@@ -53,7 +53,7 @@ const char *gemm_decode_status_string(int status);
 const char *gemm_decode_last_error(void);
 /* ABI version of this header (incremented on incompatible changes). */
 int gemm_decode_abi_version(void);
-#define GEMM_DECODE_ABI_VERSION 2
+#define GEMM_DECODE_ABI_VERSION 3
 
 /* ====================================================================
  * Q1_0 . q8_0  ("browseml-gpu.js": header comment "The arithmetic, as the
@@ -245,16 +245,56 @@ typedef struct gd_ternary_problem {
     float *y;                  /* device f32 [rows]        */
     int32_t *dot_out;          /* device int32 [rows] or NULL */
     float w_scale;
-    float x_scale;
+    float x_scale;             /* used when x_scale_dev is NULL */
+    const float *x_scale_dev;  /* device f32 (e.g. from ternary_quantize_act) or NULL;
+                                  when set, the activation scale is read from it */
 } gd_ternary_problem;
 
 /* `count` independent ternary GEMVs of one shape in one launch (one decode
  * step's projections of a given shape); same kernel body and bits as
- * ternary_gemv. `problems` is a device array (8-byte aligned) whose inner
+ * ternary_gemv, the scale product w_scale * x_scale taken with the scale
+ * read from x_scale_dev where that is set. `problems` is a device array (8-byte aligned) whose inner
  * pointers must satisfy ternary_gemv's rules. Limits: 1 <= count <= 65535.
  * Errors: GD_EINVAL, GD_ESHAPE, GD_EALIGN, GD_ERANGE, GD_EHIP. */
 int ternary_gemv_grouped(const gd_ternary_problem *problems, int64_t count,
                          int64_t rows, int64_t K, void *stream);
+
+/* ====================================================================
+ * Activation quantization  ("web-xpu-ops", operator table: quantize, and
+ * the reciprocal and rounding rows of its q4 format table, which state the
+ * same convention)
+ * ====================================================================
+ * The step before each GEMV. Per group (a token for the ternary path, a
+ * 32-element block for q8_0): absmax = max |x|; codes are Math.round of
+ * x * (127/absmax), the reciprocal formed in f64, ties toward +infinity
+ * (floor(v) + (v - floor(v) >= 0.5) in f64), clamped to [-127, 127]; the
+ * scale is the f64 quotient absmax/127 rounded to f32. A group whose absmax
+ * is 0 gets scale 0 and zero codes. Inputs must be finite (NaN or infinity
+ * give unspecified codes). Codes and scales are bit-exact with this rule.
+ * ==================================================================== */
+
+/* f32 activations -> q8_0 blocks in the layout q1_q8_gemv reads
+ * ("browseml-gpu.js", packQ8: 34 bytes, f16 d then 32 int8 codes). The
+ * pages fix the block, not its quantizer: the rule above is applied to each
+ * block of 32, and d is the f32 scale rounded to f16 (nearest even).
+ *   x     device f32 [n][K], 16-byte aligned.
+ *   a_q8  device, n * (K/32) * 34 bytes (column c at byte c * (K/32) * 34),
+ *         2-byte aligned; written whole.
+ * Requires K % 32 == 0, n >= 1, n * K/32 <= 2^34. Errors: GD_EINVAL,
+ * GD_ESHAPE, GD_EALIGN, GD_ERANGE, GD_EHIP. */
+int q8_0_quantize(const float *x, void *a_q8, int64_t n, int64_t K, void *stream);
+
+/* f32 activations -> per-token int8 codes (the rule above over each token's
+ * K values), written as the bit planes ternary_gemv reads, and the scales.
+ *   x        device f32 [count][K], 16-byte aligned.
+ *   planes   device u32 [count][8][K/32], the layout of
+ *            ternary_act_bitplanes; 4-byte aligned (ternary_gemv itself
+ *            needs 16).
+ *   x_scale  device f32 [count] (for gd_ternary_problem.x_scale_dev).
+ * Requires K % 32 == 0, 1 <= count <= 2^31 - 1, K <= 2^30. Errors:
+ * GD_EINVAL, GD_ESHAPE, GD_EALIGN, GD_ERANGE, GD_EHIP. */
+int ternary_quantize_act(const float *x, int64_t count, int64_t K, uint32_t *planes,
+                         float *x_scale, void *stream);
 
 /* ====================================================================
  * Measurement kernels  ("roofline.html": the FILL kernel writes a non-zero,

@@ -71,10 +71,14 @@ def _declare(L):
     L.gdo_blockq8_f32.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _INT]
     L.gdo_ternary_dot_direct.argtypes = [_P, _P, _P, _P, _I64, _I64]
     L.gdo_ternary_gemv.argtypes = [_P, _P, _F32, _P, _F32, _P, _P, _I64, _I64, _INT]
+    L.gdo_quantize_absmax_int8.argtypes = [_P, _I64, _I64, _P, _P]
+    L.gdo_f32_to_f16.argtypes = [_F32]
+    L.gdo_f32_to_f16.restype = ctypes.c_uint16
+    L.gdo_quantize_q8_0.argtypes = [_P, _I64, _I64, _P]
     for name in ("gdo_q1_q8_gemv_aos", "gdo_pack_q1_p1", "gdo_pack_q8_p1",
                  "gdo_q1_q8_gemv_p1packed", "gdo_q1_planes", "gdo_sign_gemm_f64",
                  "gdo_sign_gemm_f32", "gdo_blockq8_f32", "gdo_ternary_dot_direct",
-                 "gdo_ternary_gemv"):
+                 "gdo_ternary_gemv", "gdo_quantize_absmax_int8", "gdo_quantize_q8_0"):
         getattr(L, name).restype = None
 
 
@@ -225,3 +229,37 @@ def ternary_gemv(P, N, w_scale, x_q, x_scale, nthreads: int = 1):
     lib().gdo_ternary_gemv(pp, np_, float(w_scale), xp, float(x_scale), y.ctypes.data,
                            dot.ctypes.data, rows, K, nthreads)
     return y, dot
+
+
+# -------------------------------------------------------- activation quantization
+
+def quantize_absmax_int8(x):
+    """Per-row absmax int8 codes (Math.round of x * 127/absmax in f64, ties
+    toward +inf, clamped to [-127, 127]) and f32 scales absmax/127.
+    x f32 [M, K] (or [K]); returns (codes int8 same shape, scales f32 [M])."""
+    x = np.asarray(x, dtype=np.float32)
+    shape = x.shape
+    x2, xp = _c(x.reshape(-1, shape[-1]) if x.ndim else x.reshape(1, 1), np.float32)
+    M, K = x2.shape
+    q = np.empty((M, K), dtype=np.int8)
+    s = np.empty(M, dtype=np.float32)
+    lib().gdo_quantize_absmax_int8(xp, M, K, q.ctypes.data, s.ctypes.data)
+    return q.reshape(shape), s
+
+
+def f32_to_f16_bits(v) -> int:
+    """IEEE binary16 bits of f32 v, rounded to nearest even."""
+    return int(lib().gdo_f32_to_f16(float(np.float32(v))))
+
+
+def quantize_q8_0(x):
+    """q8_0 AoS bytes [n * K/32 * 34] from f32 x [n, K] (or [K]): per block of
+    32, codes as quantize_absmax_int8 does per row, d = f16(f32(absmax/127))."""
+    x = np.asarray(x, dtype=np.float32)
+    x2, xp = _c(x.reshape(-1, x.shape[-1]), np.float32)
+    n, K = x2.shape
+    if K % 32:
+        raise ValueError("K must be a multiple of 32")
+    out = np.empty(n * (K // 32) * 34, dtype=np.uint8)
+    lib().gdo_quantize_q8_0(xp, n, K, out.ctypes.data)
+    return out

@@ -407,3 +407,104 @@ void gdo_ternary_gemv(const uint32_t *P, const uint32_t *N, float w_scale,
         y[r] = (float)dot * s;
     }
 }
+
+/* ------------------------------------------------------------------------
+ * Activation quantization.
+ *
+ * [P4] "web-xpu-ops", operator table entry "quantize" and the q4 format
+ * table (its reciprocal and rounding rows, which name quantize's own
+ * convention): per row, absmax to int8 symmetric in [-127, 127]; the
+ * reciprocal 127/absmax is formed in f64; each code is Math.round of
+ * x * (127/absmax), i.e. floor(v) + (v - floor(v) >= 0.5), ties toward
+ * +infinity, clamped to [-127, 127]; the scale is absmax/127. A row whose
+ * absmax is 0 gets scale 0 and all-zero codes. Inputs must be finite.
+ * ------------------------------------------------------------------------ */
+static int32_t math_round_code(double v)
+{
+    double f = floor(v);
+    double q = f + ((v - f) >= 0.5 ? 1.0 : 0.0);
+    if (q > 127.0) q = 127.0;
+    if (q < -127.0) q = -127.0;
+    return (int32_t)q;
+}
+
+void gdo_quantize_absmax_int8(const float *x, int64_t M, int64_t K, int8_t *q, float *scale)
+{
+    for (int64_t r = 0; r < M; r++) {
+        const float *xr = x + r * K;
+        double amax = 0.0;
+        for (int64_t j = 0; j < K; j++) {
+            double a = fabs((double)xr[j]);
+            if (a > amax) amax = a;
+        }
+        if (amax == 0.0) {
+            for (int64_t j = 0; j < K; j++) q[r * K + j] = 0;
+            scale[r] = 0.0f;
+            continue;
+        }
+        double inv = 127.0 / amax;
+        for (int64_t j = 0; j < K; j++) q[r * K + j] = (int8_t)math_round_code((double)xr[j] * inv);
+        scale[r] = (float)(amax / 127.0);
+    }
+}
+
+/* f32 -> IEEE binary16, round to nearest even: the value is written as an
+ * integer significand in units of the target spacing 2^(E-10) (E the binade,
+ * at least -14, where the spacing of the subnormals is reached), rounded by
+ * rint() under the default nearest-even mode; a carry into 2048 moves one
+ * binade up, and E > 15 is infinity. NaN becomes a quiet NaN. */
+uint16_t gdo_f32_to_f16(float f)
+{
+    uint16_t s = signbit(f) ? 0x8000u : 0u;
+    if (isnan(f)) return (uint16_t)(s | 0x7e00u);
+    if (isinf(f)) return (uint16_t)(s | 0x7c00u);
+    double a = fabs((double)f);
+    if (a == 0.0) return s;
+    int E;
+    frexp(a, &E);
+    E -= 1;                                  /* a in [2^E, 2^(E+1)) */
+    if (E < -14) E = -14;
+    double m = rint(ldexp(a, 10 - E));       /* exact scaling, then one rounding */
+    if (m >= 2048.0) {
+        m = 1024.0;
+        E += 1;
+    }
+    if (E > 15) return (uint16_t)(s | 0x7c00u);
+    if (m < 1024.0) return (uint16_t)(s | (uint16_t)m);   /* subnormal */
+    return (uint16_t)(s | (uint16_t)(((uint32_t)(E + 15) << 10) | ((uint32_t)m - 1024u)));
+}
+
+/* q8_0 activation blocks in [P1]'s 34-byte format (f16 d, then 32 int8
+ * codes; packQ8 reads d from the first two bytes, little-endian). The pages
+ * fix the block but not how it is quantized; reading: the [P4] per-row rule
+ * above applied to each block of 32 elements (codes from 127/absmax in f64
+ * and Math.round), with d = f16_RNE(f32(absmax / 127)). A block whose
+ * absmax is 0 is all zero. x is [n][K] f32, K a multiple of 32; out is
+ * n * (K/32) blocks. */
+void gdo_quantize_q8_0(const float *x, int64_t n, int64_t K, uint8_t *out)
+{
+    const int64_t nb = K / QK8;
+    for (int64_t c = 0; c < n; c++) {
+        for (int64_t i = 0; i < nb; i++) {
+            const float *xb = x + c * K + i * QK8;
+            uint8_t *o = out + (c * nb + i) * Q8_BYTES;
+            double amax = 0.0;
+            for (int j = 0; j < QK8; j++) {
+                double a = fabs((double)xb[j]);
+                if (a > amax) amax = a;
+            }
+            uint16_t d = 0;
+            int8_t codes[QK8];
+            if (amax == 0.0) {
+                memset(codes, 0, sizeof codes);
+            } else {
+                double inv = 127.0 / amax;
+                for (int j = 0; j < QK8; j++) codes[j] = (int8_t)math_round_code((double)xb[j] * inv);
+                d = gdo_f32_to_f16((float)(amax / 127.0));
+            }
+            o[0] = (uint8_t)(d & 0xffu);
+            o[1] = (uint8_t)(d >> 8);
+            memcpy(o + 2, codes, QK8);
+        }
+    }
+}

@@ -28,6 +28,7 @@ def test_header_declares_the_entry_points():
     for n in ["q1_planes_bytes", "q1_repack", "q1_q8_gemv", "q1_q8_gemv_grouped", "q1_sign_gemm",
               "q1_sign_gemm_workspace_bytes",
               "blockq8_matmul_nt", "ternary_act_bitplanes", "ternary_gemv", "ternary_gemv_grouped",
+              "q8_0_quantize", "ternary_quantize_act",
               "gemm_decode_status_string", "gemm_decode_last_error", "gemm_decode_abi_version",
               "gemm_decode_fill", "gemm_decode_stream_read"]:
         assert n in names, n
@@ -37,7 +38,7 @@ def test_library_exports_every_declared_symbol(gd):
     lib = ctypes.CDLL(gd.LIB_PATH)
     missing = [n for n in declared_functions() if not hasattr(lib, n)]
     assert not missing, missing
-    assert lib.gemm_decode_abi_version() == 2
+    assert lib.gemm_decode_abi_version() == 3
 
 
 def test_status_strings(gd):
@@ -111,6 +112,18 @@ def test_validation_without_gpu(gd):
     assert L.ternary_gemv(FAKE, None, 1.0, FAKE, 1.0, FAKE, None, 4, 128, None) == E["inval"]
     assert L.ternary_gemv(FAKE, FAKE, 1.0, FAKE, 1.0, FAKE, None, 4, 1 << 20, None) == E["range"]
     assert L.ternary_gemv_grouped(FAKE, 0, 4, 128, None) == E["inval"]
+    # activation quantization
+    assert L.q8_0_quantize(None, FAKE, 1, 128, None) == E["inval"]
+    assert L.q8_0_quantize(FAKE, FAKE, 0, 128, None) == E["inval"]
+    assert L.q8_0_quantize(FAKE, FAKE, 1, 100, None) == E["shape"]
+    assert L.q8_0_quantize(FAKE + 4, FAKE, 1, 128, None) == E["align"]
+    assert L.q8_0_quantize(FAKE, FAKE + 1, 1, 128, None) == E["align"]
+    assert L.q8_0_quantize(FAKE, FAKE, 1 << 40, 1 << 20, None) == E["range"]
+    assert L.ternary_quantize_act(FAKE, 1, 128, None, FAKE, None) == E["inval"]
+    assert L.ternary_quantize_act(FAKE, 1, 96 + 4, FAKE, FAKE, None) == E["shape"]
+    assert L.ternary_quantize_act(FAKE + 8, 1, 128, FAKE, FAKE, None) == E["align"]
+    assert L.ternary_quantize_act(FAKE, 1, 128, FAKE + 2, FAKE, None) == E["align"]
+    assert L.ternary_quantize_act(FAKE, 1 << 31, 128, FAKE, FAKE, None) == E["range"]
     # measurement
     assert L.gemm_decode_fill(FAKE, 100, 1, None) == E["shape"]
     assert L.gemm_decode_stream_read(FAKE, 160, 0, FAKE, 1, None) == E["inval"]
