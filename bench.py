@@ -43,13 +43,17 @@ METRIC = "Q1_0·q8_0 GEMV effective HBM GB/s (% of peak) + equiv tok/s, batch 1"
 # the kernel source they were measured on: reported only while its hash
 # matches, null after any change to it.
 _TRAFFIC = {
-    "q1": ("q1.hip", "d7e3682a6799afc1",
-           {"4096x4096": (37732.8, 512.0), "14336x4096": (129959.6, 1792.0)}),
-    "ternary": ("ternary.hip", "91879f9a6f9284ff",
-                {"2560x2560": (97281.8, 1200.0), "6912x2560": (130259.4, 1620.0), "2560x6912": (65832.3, 300.0)}),
-    "blockq8": ("blockq8.hip", "f95d58bedf096572", {"m1": (35445.7, 207.1), "m16": (26266.3, 3072.0)}),
+    "q1": ("q1.hip", "96265188f0492ae9",
+           {"4096x4096": (37698.5, 512.0), "14336x4096": (129875.5, 1792.0)}),
+    "ternary": ("ternary.hip", "16436179a92f165c",
+                {"2560x2560": (97291.4, 1200.0), "6912x2560": (130263.3, 1620.0), "2560x6912": (65789.8, 300.0)}),
+    "blockq8": ("blockq8.hip", "a0d67a1723d13bce", {"m1": (25974.9, 202.4), "m16": (26263.1, 3072.0)}),
     "sign": ("sign_gemm.hip", "850acc3ab2e1ded4",
              {"split": (4128.6, 8208.0), "wpack": (2074.0, 4096.0), "gemm": (21355.3, 9728.0)}),
+    "quant": ("quantize.hip", "a7b47e9235f09149",
+              {"q8_0_decode": (266.9, 136.0), "q8_0_batch_256MiB": (131085.5, 69632.0),
+               "int8_planes_decode_step": (538.5 + 559.5, 227.8 + 203.4),
+               "int8_planes_batch_256MiB": (131167.4, 66048.0)}),
 }
 
 
@@ -598,7 +602,8 @@ def bench_quant(args, gd, torch):
             "metric": "effective HBM GB/s", "value": round(gbps, 1), "unit": "GB/s",
             "us_per_step": round(per * 1e6, 2), "launches_per_step": len(shapes),
             "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                         "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                         "traffic": None if qt is None else qt[name],
                          "kernel": "q8_0_quantize_kernel" if kind == "q8" else "act_quant_kernel",
                          "bytes_per_step": bytes_},
             "parity_mismatches_sampled": mism,
@@ -607,6 +612,7 @@ def bench_quant(args, gd, torch):
                              "sample": "first <= 64 rows of each shape, single-threaded oracle"},
         }
 
+    qt = measured_traffic("quant")
     measure("q8_0_decode", "q8", [(32, 4096)], 8)
     measure("q8_0_batch_256MiB", "q8", [(16384, 4096)], 2)
     measure("int8_planes_decode_step", "act", [(90, 2560), (30, 6912)], 8)

@@ -126,8 +126,12 @@ __global__ __launch_bounds__(kGemvThreads) void blockq8_gemv_kernel(const float 
     const int64_t row0 = wave * 2 * steps_per_wave;          // rows row0 + 2i + sub
 
     auto load = [&](int64_t i, RowBuf &b) {
-        int64_t r = row0 + 2 * i + sub;
-        r = r < n ? r : n - 1;                                  // clamped: never stored
+        // Steps past this wave's last are clamped to that step (a cache
+        // hit; never stored), not run into the next wave's rows, which
+        // would be fetched a second time.
+        const int64_t ic = i < steps_per_wave ? i : steps_per_wave - 1;
+        int64_t r = row0 + 2 * ic + sub;
+        r = r < n ? r : n - 1;
 #pragma unroll
         for (int t = 0; t < kCPL; t++) {
             int c = lane + kLPR * t;
