@@ -468,6 +468,27 @@ def bench_sign(args, gd, torch):
         t_used += time.perf_counter() - t
         rows_done += 4
     cpu_gflops = 2.0 * rows_done * N * K / t_used / 1e9
+
+    # the same GEMM on weights packed once (q1_sign_pack), and the LUT4
+    # comparator on those packed weights
+    packed = []
+    for a, b, s_, y in sets:
+        wp = torch.empty(gd.q1_sign_packed_bytes(N, K), dtype=torch.uint8, device="cuda")
+        gd.q1_sign_pack(b, s_, N, K, wp)
+        packed.append((a, wp, y))
+
+    def launch_packed(k):
+        a, wp, y = packed[k % ring]
+        gd.q1_sign_gemm_packed(a, wp, y, M, N, K)
+    per_p, _ = _time_launches(torch, launch_packed, args.aux_steps, 3)
+
+    def launch_lut(k):
+        a, wp, y = packed[k % ring]
+        gd.q1_sign_gemm_lut4(a, wp, y, M, N, K)
+    per_l, _ = _time_launches(torch, launch_lut, max(4, args.aux_steps // 4), 1)
+    y_l = packed[(1 + max(4, args.aux_steps // 4) - 1) % ring][2].cpu().numpy().reshape(M, N)
+    rel_l = float(np.max(np.abs(y_l[:, cols] - want)) / np.max(np.abs(want)))
+    decode = bench_sign_gemv(args, gd, torch)
     return {
         "workload": "sign-bit prefill GEMM y=x@w^T, M=512, N=4096, K=4096, x f32 (fp16 hi+lo on MFMA)",
         "metric": "useful TFLOP/s (2MNK)", "value": round(tflops, 2), "unit": "TFLOP/s",
@@ -482,7 +503,51 @@ def bench_sign(args, gd, torch):
         "parity_rel_err_sampled": rel,
         "cpu_baseline": {"value": round(cpu_gflops / 1e3, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
                          "sample": f"{rows_done} of 512 rows x all 4096 columns (f64 oracle), {t_used:.2f} s"},
+        "packed_weights": {"note": "weights packed once by q1_sign_pack; per call: split + GEMM kernels",
+                           "us_per_gemm": round(per_p * 1e6, 2), "value": round(flops / per_p / 1e12, 2),
+                           "unit": "TFLOP/s", "frac": round(flops / per_p / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)},
+        "lut4_comparator": {"note": "the page's LUT4 prefill (table lookup, VALU + LDS), packed weights",
+                            "us_per_gemm": round(per_l * 1e6, 2), "value": round(flops / per_l / 1e12, 2),
+                            "unit": "TFLOP/s", "vs_mfma_packed": round(per_l / per_p, 2),
+                            "parity_rel_err_sampled": rel_l},
+        "decode_gemv": decode,
     }
+
+
+def bench_sign_gemv(args, gd, torch):
+    """Sign-bit decode GEMV (M=1) on packed weights at the 8B-class decode
+    shapes, one launch per GEMV over a ring of weight copies > 1 GiB; HBM
+    roofline on the packed weight bytes + x + y."""
+    import oracle
+    out = {}
+    for N, K in ((4096, 4096), (14336, 4096)):
+        x, bits, scales = wl.sign_gemm_inputs(1, N, K, seed=N + K)
+        wbytes = N * K // 4        # 1 bit + 1/32 of an f32 per weight
+        ring = max(2, int(np.ceil(1.05 * (1 << 30) / wbytes)))
+        bd = torch.from_numpy(bits.view(np.int32)).cuda()
+        sd = torch.from_numpy(scales).cuda()
+        wp0 = torch.empty(gd.q1_sign_packed_bytes(N, K), dtype=torch.uint8, device="cuda")
+        gd.q1_sign_pack(bd, sd, N, K, wp0)
+        copies = [wp0] + [wp0.clone() for _ in range(ring - 1)]
+        xd = torch.from_numpy(x).cuda()
+        y = torch.empty(N, device="cuda")
+
+        def launch(k):
+            gd.q1_sign_gemv(xd, copies[k % ring], y, 1, N, K)
+        per, _ = _time_launches(torch, launch, 64, 4)
+        bytes_ = wbytes + K * 4 + N * 4
+        got = y.cpu().numpy()
+        want = oracle.sign_gemm_f64(x, bits, scales, nthreads=cpu_cores())[0]
+        out[f"{N}x{K}"] = {
+            "us_per_gemv": round(per * 1e6, 2), "value": round(bytes_ / per / 1e9, 1), "unit": "GB/s",
+            "roofline": {"bound": "hbm", "achieved": round(bytes_ / per / 1e9, 1), "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": round(bytes_ / per / 1e9 / HBM_PEAK_GBPS, 4),
+                         "kernel": "sign_gemv_kernel", "bytes_per_launch": bytes_,
+                         "timing": "one HIP graph of 64 launches over distinct weight copies"},
+            "parity_rel_err": float(np.max(np.abs(got - want)) / np.max(np.abs(want))),
+        }
+        del copies
+    return out
 
 
 def bench_blockq8(args, gd, torch):

@@ -61,6 +61,11 @@ def _declare():
         "q1_q8_gemv_grouped": [_P, _I64, _I64, _I64, _P],
         "q1_sign_gemm": [_P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_size_t, _P],
         "q1_sign_gemm_workspace_bytes": [_I64, _I64, _I64, ctypes.POINTER(ctypes.c_size_t)],
+        "q1_sign_packed_bytes": [_I64, _I64, ctypes.POINTER(ctypes.c_size_t)],
+        "q1_sign_pack": [_P, _P, _I64, _I64, _P, _P],
+        "q1_sign_gemm_packed": [_P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_size_t, _P],
+        "q1_sign_gemv": [_P, _P, _P, _I64, _I64, _I64, _P],
+        "q1_sign_gemm_lut4": [_P, _P, _P, _I64, _I64, _I64, _P],
         "blockq8_matmul_nt": [_P, _P, _P, _P, _I64, _I64, _I64, _P],
         "ternary_act_bitplanes": [_P, _I64, _I64, _P, _P],
         "ternary_gemv": [_P, _P, _F32, _P, _F32, _P, _P, _I64, _I64, _P],
@@ -175,6 +180,18 @@ def q1_sign_gemm_workspace_bytes(M: int, N: int, K: int) -> int:
 _sign_ws = {}
 
 
+def _sign_workspace(M: int, N: int, K: int, device=None):
+    """The per-device cached sign-GEMM workspace, grown to the call's need."""
+    import torch
+    need = q1_sign_gemm_workspace_bytes(M, N, K) if K >= 32 and K % 32 == 0 else 16
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+    ws = _sign_ws.get(dev)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        _sign_ws[dev] = ws
+    return ws
+
+
 def q1_sign_gemm(x, w_bits, w_scales, y, M: int, N: int, K: int, workspace=None):
     """y = x @ w^T for sign-bit weights. `workspace` (a uint8 CUDA tensor of
     at least q1_sign_gemm_workspace_bytes(M, N, K)) defaults to one cached per
@@ -183,18 +200,50 @@ def q1_sign_gemm(x, w_bits, w_scales, y, M: int, N: int, K: int, workspace=None)
     import torch
     G = K // 32 if K % 32 == 0 else -1
     if workspace is None:
-        need = q1_sign_gemm_workspace_bytes(M, N, K) if G > 0 else 16
-        dev = x.device
-        ws = _sign_ws.get(dev)
-        if ws is None or ws.numel() < need:
-            ws = torch.empty(need, dtype=torch.uint8, device=dev)
-            _sign_ws[dev] = ws
-        workspace = ws
+        workspace = _sign_workspace(M, N, K, x.device)
     _check(_lib.q1_sign_gemm(_dev(x, torch.float32, M * K, "x"),
                              _dev(w_bits, torch.int32, N * G if G > 0 else None, "w_bits"),
                              _dev(w_scales, torch.float32, N * G if G > 0 else None, "w_scales"),
                              _dev(y, torch.float32, M * N, "y"), M, N, K,
                              _dev(workspace, torch.uint8, None, "workspace"), workspace.numel(), _stream()))
+
+
+def q1_sign_packed_bytes(N: int, K: int) -> int:
+    b = ctypes.c_size_t()
+    _check(_lib.q1_sign_packed_bytes(N, K, ctypes.byref(b)))
+    return b.value
+
+
+def q1_sign_pack(w_bits, w_scales, N: int, K: int, w_packed):
+    """One-time repack of sign words + scales (uint8 [q1_sign_packed_bytes])."""
+    import torch
+    G = K // 32 if K % 32 == 0 else None
+    _check(_lib.q1_sign_pack(_dev(w_bits, torch.int32, N * G if G else None, "w_bits"),
+                             _dev(w_scales, torch.float32, N * G if G else None, "w_scales"), N, K,
+                             _dev(w_packed, torch.uint8, q1_sign_packed_bytes(N, K) if G else None, "w_packed"),
+                             _stream()))
+
+
+def q1_sign_gemm_packed(x, w_packed, y, M: int, N: int, K: int, workspace=None):
+    import torch
+    if workspace is None:
+        workspace = _sign_workspace(M, N, K, x.device)
+    _check(_lib.q1_sign_gemm_packed(_dev(x, torch.float32, M * K, "x"),
+                                    _dev(w_packed, torch.uint8, None, "w_packed"),
+                                    _dev(y, torch.float32, M * N, "y"), M, N, K,
+                                    _dev(workspace, torch.uint8, None, "workspace"), workspace.numel(), _stream()))
+
+
+def q1_sign_gemv(x, w_packed, y, M: int, N: int, K: int):
+    import torch
+    _check(_lib.q1_sign_gemv(_dev(x, torch.float32, M * K, "x"), _dev(w_packed, torch.uint8, None, "w_packed"),
+                             _dev(y, torch.float32, M * N, "y"), M, N, K, _stream()))
+
+
+def q1_sign_gemm_lut4(x, w_packed, y, M: int, N: int, K: int):
+    import torch
+    _check(_lib.q1_sign_gemm_lut4(_dev(x, torch.float32, M * K, "x"), _dev(w_packed, torch.uint8, None, "w_packed"),
+                                  _dev(y, torch.float32, M * N, "y"), M, N, K, _stream()))
 
 
 # ------------------------------------------------------ block-Q8 matmul_nt

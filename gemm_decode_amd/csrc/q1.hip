@@ -23,6 +23,7 @@
 // immediate LDS offsets. All 64 lanes of a wave read the same 16-entry table
 // per instruction: at most 16 distinct dwords in 16 distinct banks. The two
 // halves meet once per row, through LDS, for the final tree.
+#include "gd_device.h"
 #include "gd_internal.h"
 
 namespace {
@@ -170,27 +171,9 @@ struct Q1Args {
     float *y;                 // output column
 };
 
-// Table offset of the 4-bit group held in byte B of w, pre-shifted by 2:
-// (byte B of w) & 0x3c as one v_and_b32 with an SDWA byte select.
-template <int B>
-__device__ __forceinline__ uint32_t grp(uint32_t w) {
-    static_assert(B >= 0 && B < 4, "byte select");
-    uint32_t r;
-    const uint32_t mask = 0x3cu;
-    if constexpr (B == 0)
-        asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0 src1_sel:DWORD"
-            : "=v"(r) : "v"(w), "v"(mask));
-    else if constexpr (B == 1)
-        asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1 src1_sel:DWORD"
-            : "=v"(r) : "v"(w), "v"(mask));
-    else if constexpr (B == 2)
-        asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2 src1_sel:DWORD"
-            : "=v"(r) : "v"(w), "v"(mask));
-    else
-        asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3 src1_sel:DWORD"
-            : "=v"(r) : "v"(w), "v"(mask));
-    return r;
-}
+// Table offsets: gd::grp<B>(w) is the 4-bit group held in byte B of w,
+// pre-shifted by 2 (one SDWA v_and_b32).
+using gd::grp;
 
 template <int U>
 __device__ __forceinline__ float d0_half(const u32x4 &s8) {

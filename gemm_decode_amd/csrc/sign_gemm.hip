@@ -393,6 +393,89 @@ extern "C" int q1_sign_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, siz
     return GD_OK;
 }
 
+namespace {
+
+int check_mnk(const char *who, int64_t M, int64_t N, int64_t K) {
+    GD_REQUIRE(M >= 1 && N >= 1 && K >= 1, GD_EINVAL, "%s: M (%lld), N (%lld), K (%lld) must be >= 1", who,
+               (long long)M, (long long)N, (long long)K);
+    GD_REQUIRE(K % 32 == 0, GD_ESHAPE, "%s: K (%lld) must be a multiple of 32", who, (long long)K);
+    GD_REQUIRE(M <= INT64_C(2147483647) && N <= INT64_C(2147483647) && K <= INT64_C(2147483647), GD_ERANGE,
+               "%s: M, N or K above 2^31-1", who);
+    return GD_OK;
+}
+
+int packed_size(int64_t N, int64_t K, int64_t *bytes) {
+    int64_t c;
+    GD_REQUIRE(gd::mul_ok((K / 32 + 1) / 2, N, &c) && gd::mul_ok(c, 16, bytes), GD_ERANGE,
+               "packed weight size overflows");
+    return GD_OK;
+}
+
+// Launches split + GEMM against weights already in the packed layout.
+int split_and_gemm(const float *x, const u32x4 *wv, float *y, int64_t M, int64_t N, int64_t K, void *workspace,
+                   hipStream_t s, const char *who) {
+    const int64_t G = K / 32;
+    const int64_t m16 = (M + 15) / 16;
+    uint32_t *xs = static_cast<uint32_t *>(workspace);
+    int32_t *rexp = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + m16 * 16 * K * 4);
+    const int64_t tiles_m = (M + kTM - 1) / kTM, tiles_n = (N + kTN - 1) / kTN;
+    const int64_t tiles = tiles_m * tiles_n;
+    const int64_t per_xcd = (tiles + 7) / 8;
+    GD_REQUIRE(per_xcd * 8 <= INT64_C(0xffffffff), GD_ERANGE, "%s: grid too large", who);
+    hipLaunchKernelGGL(sign_split_kernel, dim3(static_cast<uint32_t>(m16 * 16)), dim3(kPrepThreads), 0, s, x, M, K,
+                       xs, rexp);
+    hipLaunchKernelGGL(sign_gemm_kernel, dim3(static_cast<uint32_t>(per_xcd * 8)), dim3(kThreads), 0, s, xs, rexp,
+                       wv, y, M, N, G, tiles_n, tiles, per_xcd);
+    return check_launch(who);
+}
+
+}  // namespace
+
+extern "C" int q1_sign_packed_bytes(int64_t N, int64_t K, size_t *bytes) {
+    GD_REQUIRE(bytes, GD_EINVAL, "q1_sign_packed_bytes: null output pointer");
+    int st = check_mnk("q1_sign_packed_bytes", 1, N, K);
+    if (st) return st;
+    int64_t b;
+    st = packed_size(N, K, &b);
+    if (st) return st;
+    *bytes = static_cast<size_t>(b);
+    clear_error();
+    return GD_OK;
+}
+
+extern "C" int q1_sign_pack(const uint32_t *w_bits, const float *w_scales, int64_t N, int64_t K, void *w_packed,
+                            void *stream) {
+    GD_REQUIRE(w_bits && w_scales && w_packed, GD_EINVAL, "q1_sign_pack: null pointer");
+    int st = check_mnk("q1_sign_pack", 1, N, K);
+    if (st) return st;
+    GD_REQUIRE(aligned(w_bits, 4) && aligned(w_scales, 4) && aligned(w_packed, 16), GD_EALIGN,
+               "q1_sign_pack: w_bits and w_scales must be 4-byte aligned, w_packed 16-byte");
+    const int64_t G = K / 32;
+    const int64_t wpack_x = (N + kPackRows - 1) / kPackRows, wpack_y = (G + kPackGroups - 1) / kPackGroups;
+    GD_REQUIRE(wpack_x <= INT64_C(0xffffffff) && wpack_y <= 65535, GD_ERANGE, "q1_sign_pack: grid too large");
+    hipLaunchKernelGGL(sign_wpack_kernel, dim3(static_cast<uint32_t>(wpack_x), static_cast<uint32_t>(wpack_y)),
+                       dim3(kPrepThreads), 0, as_stream(stream), w_bits, w_scales, N, G,
+                       static_cast<u32x4 *>(w_packed));
+    return check_launch("q1_sign_pack");
+}
+
+extern "C" int q1_sign_gemm_packed(const float *x, const void *w_packed, float *y, int64_t M, int64_t N, int64_t K,
+                                   void *workspace, size_t workspace_bytes, void *stream) {
+    GD_REQUIRE(x && w_packed && y && workspace, GD_EINVAL, "q1_sign_gemm_packed: null pointer");
+    int st = check_mnk("q1_sign_gemm_packed", M, N, K);
+    if (st) return st;
+    GD_REQUIRE(aligned(x, 16) && aligned(w_packed, 16) && aligned(y, 4) && aligned(workspace, 16), GD_EALIGN,
+               "q1_sign_gemm_packed: x, w_packed and workspace must be 16-byte aligned, y 4-byte");
+    const int64_t m16 = (M + 15) / 16;
+    int64_t a, need;
+    GD_REQUIRE(mul_ok(m16 * 16, K, &a) && mul_ok(a, 4, &need), GD_ERANGE, "q1_sign_gemm_packed: size overflows");
+    need += m16 * 16 * 4;   // split activations and row exponents; no weight part
+    GD_REQUIRE(workspace_bytes >= static_cast<size_t>(need), GD_ERANGE,
+               "q1_sign_gemm_packed: workspace of %zu bytes, %lld needed", workspace_bytes, (long long)need);
+    return split_and_gemm(x, static_cast<const u32x4 *>(w_packed), y, M, N, K, workspace, as_stream(stream),
+                          "q1_sign_gemm_packed");
+}
+
 extern "C" int q1_sign_gemm(const float *x, const uint32_t *w_bits, const float *w_scales, float *y, int64_t M,
                             int64_t N, int64_t K, void *workspace, size_t workspace_bytes, void *stream) {
     GD_REQUIRE(x && w_bits && w_scales && y && workspace, GD_EINVAL, "q1_sign_gemm: null pointer");
@@ -411,21 +494,11 @@ extern "C" int q1_sign_gemm(const float *x, const uint32_t *w_bits, const float 
                "q1_sign_gemm: workspace of %zu bytes, %lld needed", workspace_bytes, (long long)need);
     const int64_t G = K / 32;
     const int64_t m16 = (M + 15) / 16;
-    uint32_t *xs = static_cast<uint32_t *>(workspace);
-    int32_t *rexp = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + m16 * 16 * K * 4);
-    u32x4 *wv = reinterpret_cast<u32x4 *>(rexp + m16 * 16);
+    u32x4 *wv = reinterpret_cast<u32x4 *>(static_cast<char *>(workspace) + m16 * 16 * K * 4 + m16 * 16 * 4);
     const int64_t wpack_x = (N + kPackRows - 1) / kPackRows, wpack_y = (G + kPackGroups - 1) / kPackGroups;
-    const int64_t tiles_m = (M + kTM - 1) / kTM, tiles_n = (N + kTN - 1) / kTN;
-    const int64_t tiles = tiles_m * tiles_n;
-    const int64_t per_xcd = (tiles + 7) / 8;
-    GD_REQUIRE(wpack_x <= INT64_C(0xffffffff) && wpack_y <= 65535 && per_xcd * 8 <= INT64_C(0xffffffff), GD_ERANGE,
-               "q1_sign_gemm: grid too large");
+    GD_REQUIRE(wpack_x <= INT64_C(0xffffffff) && wpack_y <= 65535, GD_ERANGE, "q1_sign_gemm: grid too large");
     hipStream_t s = as_stream(stream);
-    hipLaunchKernelGGL(sign_split_kernel, dim3(static_cast<uint32_t>(m16 * 16)), dim3(kPrepThreads), 0, s, x, M, K,
-                       xs, rexp);
     hipLaunchKernelGGL(sign_wpack_kernel, dim3(static_cast<uint32_t>(wpack_x), static_cast<uint32_t>(wpack_y)),
                        dim3(kPrepThreads), 0, s, w_bits, w_scales, N, G, wv);
-    hipLaunchKernelGGL(sign_gemm_kernel, dim3(static_cast<uint32_t>(per_xcd * 8)), dim3(kThreads), 0, s, xs, rexp,
-                       wv, y, M, N, G, tiles_n, tiles, per_xcd);
-    return check_launch("q1_sign_gemm");
+    return split_and_gemm(x, wv, y, M, N, K, workspace, s, "q1_sign_gemm");
 }

@@ -180,6 +180,54 @@ int q1_sign_gemm(const float *x, const uint32_t *w_bits, const float *w_scales,
  * GD_ESHAPE (K % 32 != 0), GD_ERANGE. */
 int q1_sign_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t *bytes);
 
+/* Bytes of the packed sign-bit weights written by q1_sign_pack:
+ * 16 * N * ceil(K/64). Host only. Errors: GD_EINVAL, GD_ESHAPE, GD_ERANGE. */
+int q1_sign_packed_bytes(int64_t N, int64_t K, size_t *bytes);
+
+/* One-time repack of the page's sign words and scales (the layouts
+ * q1_sign_gemm takes) for the calls below: for each output n and pair of
+ * 32-weight groups (g, g+1), g even, the u32x4 {bits[n][g], bits[n][g+1],
+ * scale[n][g], scale[n][g+1]} (scales as f32 bit patterns) at index
+ * (g/2)*N + n, a missing group g+1 = K/32 having bits 0 and scale 0, so the
+ * words of one group pair for consecutive outputs are contiguous.
+ *   w_bits, w_scales  as for q1_sign_gemm, 4-byte aligned.
+ *   w_packed          device, q1_sign_packed_bytes(N, K) bytes, 16-byte
+ *                     aligned; written whole.
+ * Errors: GD_EINVAL, GD_ESHAPE, GD_EALIGN, GD_ERANGE, GD_EHIP. */
+int q1_sign_pack(const uint32_t *w_bits, const float *w_scales, int64_t N, int64_t K,
+                 void *w_packed, void *stream);
+
+/* q1_sign_gemm on weights packed once by q1_sign_pack (no per-call
+ * regrouping launch); same numerics and bits as q1_sign_gemm. The workspace
+ * holds only the split activations and row exponents: at least
+ * 4*K*M16 + 4*M16 bytes (M16 = M rounded up to 16), so any size
+ * q1_sign_gemm_workspace_bytes(M, N, K) returns is enough. x, w_packed and
+ * workspace 16-byte aligned, y 4-byte. Errors: GD_EINVAL, GD_ESHAPE,
+ * GD_EALIGN, GD_ERANGE, GD_EHIP. */
+int q1_sign_gemm_packed(const float *x, const void *w_packed, float *y,
+                        int64_t M, int64_t N, int64_t K,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* Sign-bit decode GEMV (the page's decode kernel, one token at a time):
+ * y[m][n] = sum_g scale[n][g] * sum_{j<32} s(n, 32g+j) x[m][32g+j] for each
+ * of M activation rows, from packed weights. Each workgroup turns the row
+ * into LDS tables of the signed sums of every 4 consecutive elements (16
+ * per 4), so a nibble of signs costs one table read and one add; partial
+ * sums round in f32 (within 1e-5 of ||y||_inf of the exact sum).
+ *   x  device f32 [M][K], 16-byte aligned; y device f32 [M][N], 4-byte.
+ * Requires K % 32 == 0, 1 <= M <= 65535. Every row reads the weights once
+ * more: meant for a few tokens (use q1_sign_gemm(_packed) for prefill).
+ * Errors: GD_EINVAL, GD_ESHAPE, GD_EALIGN, GD_ERANGE, GD_EHIP. */
+int q1_sign_gemv(const float *x, const void *w_packed, float *y,
+                 int64_t M, int64_t N, int64_t K, void *stream);
+
+/* The page's LUT4 prefill GEMM (binary-lut4-matmul: 16 partial sums of
+ * every 4 activations in workgroup memory, one read per nibble, reused over
+ * a 16-token x 512-output tile), kept as the comparator of the matrix-core
+ * GEMM: same y and contract as q1_sign_gemv, for any M. */
+int q1_sign_gemm_lut4(const float *x, const void *w_packed, float *y,
+                      int64_t M, int64_t N, int64_t K, void *stream);
+
 /* ====================================================================
  * Block-scaled int8 matmul_nt  ("block_q8_matmul_nt.wgsl": PACKING,
  * ACCUMULATION ORDER, quant_at, main)

@@ -28,7 +28,8 @@ def test_header_declares_the_entry_points():
     for n in ["q1_planes_bytes", "q1_repack", "q1_q8_gemv", "q1_q8_gemv_grouped", "q1_sign_gemm",
               "q1_sign_gemm_workspace_bytes",
               "blockq8_matmul_nt", "ternary_act_bitplanes", "ternary_gemv", "ternary_gemv_grouped",
-              "q8_0_quantize", "ternary_quantize_act",
+              "q8_0_quantize", "ternary_quantize_act", "q1_sign_packed_bytes", "q1_sign_pack",
+              "q1_sign_gemm_packed", "q1_sign_gemv", "q1_sign_gemm_lut4",
               "gemm_decode_status_string", "gemm_decode_last_error", "gemm_decode_abi_version",
               "gemm_decode_fill", "gemm_decode_stream_read"]:
         assert n in names, n
@@ -99,6 +100,20 @@ def test_validation_without_gpu(gd):
     assert ws.value == 32 * 96 * 4 + 32 * 4 + 5 * 2 * 16
     assert L.q1_sign_gemm_workspace_bytes(17, 5, 100, ctypes.byref(ws)) == E["shape"]
     assert L.q1_sign_gemm(FAKE, FAKE, FAKE, FAKE, 17, 5, 128, FAKE, 32 * 128 * 4, None) == E["range"]
+    # packed sign-bit weights: 16 bytes per output and group pair
+    assert L.q1_sign_packed_bytes(5, 128, ctypes.byref(ws)) == 0 and ws.value == 5 * 2 * 16
+    assert L.q1_sign_packed_bytes(5, 96, ctypes.byref(ws)) == 0 and ws.value == 5 * 2 * 16
+    assert L.q1_sign_packed_bytes(5, 100, ctypes.byref(ws)) == E["shape"]
+    assert L.q1_sign_pack(FAKE, FAKE, 4, 128, FAKE + 4, None) == E["align"]
+    assert L.q1_sign_pack(FAKE, None, 4, 128, FAKE, None) == E["inval"]
+    assert L.q1_sign_gemm_packed(FAKE, FAKE, FAKE, 17, 5, 128, FAKE, 32 * 128 * 4, None) == E["range"]
+    assert L.q1_sign_gemm_packed(FAKE, FAKE + 8, FAKE, 17, 5, 128, FAKE, 1 << 20, None) == E["align"]
+    for fn in (L.q1_sign_gemv, L.q1_sign_gemm_lut4):
+        assert fn(FAKE, FAKE, FAKE, 1, 4, 100, None) == E["shape"]
+        assert fn(FAKE, FAKE, FAKE, 0, 4, 128, None) == E["inval"]
+        assert fn(FAKE + 4, FAKE, FAKE, 1, 4, 128, None) == E["align"]
+        assert fn(FAKE, FAKE + 8, FAKE, 1, 4, 128, None) == E["align"]
+    assert L.q1_sign_gemv(FAKE, FAKE, FAKE, 70000, 4, 128, None) == E["range"]
     # block-Q8
     assert L.blockq8_matmul_nt(FAKE, FAKE, FAKE, FAKE, 1, 100, 4, None) == E["shape"]
     assert L.blockq8_matmul_nt(FAKE, FAKE, FAKE, FAKE, 1, 960, 0, None) == E["inval"]
