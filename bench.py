@@ -685,6 +685,52 @@ def bench_quant(args, gd, torch):
     return out
 
 
+def bench_attention(args, gd, torch):
+    """Split-K decode attention for one token at the 8B-class shape (32 query
+    heads, 8 KV heads, head dim 128, f32 caches) at kv_len 4096 and 32768:
+    HBM roofline on the K and V rows read once + q + out, over a ring of
+    cache copies > 1 GiB."""
+    import oracle
+    Hq, Hkv, D = 32, 8, 128
+    out = {}
+    for L in (4096, 32768):
+        rng = np.random.default_rng(L)
+        q = rng.standard_normal((Hq, D), dtype=np.float32)
+        k = rng.standard_normal((Hkv, L, D), dtype=np.float32)
+        v = rng.standard_normal((Hkv, L, D), dtype=np.float32)
+        set_bytes = 2 * k.nbytes
+        ring = max(2, int(np.ceil(1.05 * (1 << 30) / set_bytes)))
+        kd, vd = torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda()
+        caches = [(kd, vd)] + [(kd.clone(), vd.clone()) for _ in range(ring - 1)]
+        qd = torch.from_numpy(q).cuda()
+        o = torch.empty(Hq * D, device="cuda")
+        scale = 1.0 / np.sqrt(D)
+        ws = torch.empty(gd.attn_decode_workspace_bytes(Hq, Hkv, D, L), dtype=torch.uint8, device="cuda")
+
+        def launch(kk):
+            kc, vc = caches[kk % ring]
+            gd.attn_decode_splitk(qd, kc, vc, o, Hq, Hkv, D, L, L, scale, 0, ws)
+        per, _ = _time_launches(torch, launch, args.aux_steps, 2)
+        bytes_ = set_bytes + 2 * Hq * D * 4
+        got = o.cpu().numpy().reshape(Hq, D)
+        t = time.perf_counter()
+        want = oracle.attention_decode(q, k, v, scale)
+        t_cpu = time.perf_counter() - t
+        out[f"kv{L}"] = {
+            "workload": f"decode attention, 1 token, {Hq} query / {Hkv} KV heads, d={D}, kv_len={L}, f32 KV",
+            "metric": "effective HBM GB/s", "value": round(bytes_ / per / 1e9, 1), "unit": "GB/s",
+            "us_per_call": round(per * 1e6, 2),
+            "roofline": {"bound": "hbm", "achieved": round(bytes_ / per / 1e9, 1), "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": round(bytes_ / per / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None,
+                         "kernel": "attn_split_kernel<4> + attn_merge_kernel", "bytes_per_call": bytes_},
+            "parity_rel_err": float(np.max(np.abs(got - want)) / np.max(np.abs(want))),
+            "cpu_baseline": {"value": round(bytes_ / t_cpu / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                             "sample": "one whole call (f64 numpy, per head)"},
+        }
+        del caches
+    return out
+
+
 def bench_ternary(args, gd, torch):
     """BitNet-2B-like ternary decode step: 210 GEMVs (per layer 4 x 2560x2560,
     2 x 6912x2560, 1 x 2560x6912), each with its own activation vector (bit
@@ -815,7 +861,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="all",
-                    choices=["all", "q1", "q1mm", "sign", "blockq8", "ternary", "quant"],
+                    choices=["all", "q1", "q1mm", "sign", "blockq8", "ternary", "quant", "attention"],
                     help="all (default): the Q1 metric line plus the other paths under 'workloads'")
     ap.add_argument("--aux-steps", type=int, default=20, help="timed launches for the other paths")
     ap.add_argument("--aux-cpu-seconds", type=float, default=4.0)
@@ -866,6 +912,9 @@ def main():
         if args.workload in ("all", "quant"):
             log("[bench] activation quantization")
             extra["act_quant"] = bench_quant(args, gd, torch)
+        if args.workload in ("all", "attention"):
+            log("[bench] split-K decode attention")
+            extra["decode_attention"] = bench_attention(args, gd, torch)
         out["workloads"] = extra
     print(json.dumps(out), flush=True)
 

@@ -71,6 +71,8 @@ def _declare():
         "ternary_gemv": [_P, _P, _F32, _P, _F32, _P, _P, _I64, _I64, _P],
         "ternary_gemv_grouped": [_P, _I64, _I64, _I64, _P],
         "q8_0_quantize": [_P, _P, _I64, _I64, _P],
+        "attn_decode_workspace_bytes": [_I64, _I64, _I64, _I64, _I64, ctypes.POINTER(ctypes.c_size_t)],
+        "attn_decode_splitk": [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F32, _I64, _P, ctypes.c_size_t, _P],
         "ternary_quantize_act": [_P, _I64, _I64, _P, _P, _P],
         "gemm_decode_fill": [_P, ctypes.c_size_t, ctypes.c_uint32, _P],
         "gemm_decode_stream_read": [_P, ctypes.c_size_t, ctypes.c_int32, _P, _I64, _P],
@@ -316,6 +318,32 @@ def ternary_quantize_act(x, count: int, K: int, planes, x_scale):
                                      _dev(planes, torch.int32, count * 8 * (K // 32) if K % 32 == 0 else None,
                                           "planes"),
                                      _dev(x_scale, torch.float32, count, "x_scale"), _stream()))
+
+
+# ------------------------------------------------------ decode attention
+
+def attn_decode_workspace_bytes(n_heads: int, n_kv_heads: int, head_dim: int, kv_len: int,
+                                num_splits: int = 0) -> int:
+    b = ctypes.c_size_t()
+    _check(_lib.attn_decode_workspace_bytes(n_heads, n_kv_heads, head_dim, kv_len, num_splits, ctypes.byref(b)))
+    return b.value
+
+
+def attn_decode_splitk(q, k_cache, v_cache, out, n_heads: int, n_kv_heads: int, head_dim: int, kv_len: int,
+                       kv_stride: int, scale: float, num_splits: int = 0, workspace=None):
+    """Split-K decode attention for one token; the workspace (uint8) is
+    allocated here when not given."""
+    import torch
+    need = attn_decode_workspace_bytes(n_heads, n_kv_heads, head_dim, kv_len, num_splits)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    cache_n = n_kv_heads * kv_stride * head_dim
+    _check(_lib.attn_decode_splitk(_dev(q, torch.float32, n_heads * head_dim, "q"),
+                                   _dev(k_cache, torch.float32, cache_n, "k_cache"),
+                                   _dev(v_cache, torch.float32, cache_n, "v_cache"),
+                                   _dev(out, torch.float32, n_heads * head_dim, "out"),
+                                   n_heads, n_kv_heads, head_dim, kv_len, kv_stride, float(scale), num_splits,
+                                   _dev(workspace, torch.uint8, None, "workspace"), workspace.numel(), _stream()))
 
 
 # ------------------------------------------------------------ measurement

@@ -345,6 +345,45 @@ int ternary_quantize_act(const float *x, int64_t count, int64_t K, uint32_t *pla
                          float *x_scale, void *stream);
 
 /* ====================================================================
+ * Split-K decode attention  ("BonsaiのWebGPUカーネルを読み解く", section on
+ * split-K flash decode attention: per split a running maximum, denominator
+ * and rescaled output; a merge that rescales every split to the global
+ * maximum)
+ * ====================================================================
+ * One decode token: for query head h and its KV head kv = h / (n_heads /
+ * n_kv_heads), s_j = scale * q[h] . k[kv][j] over positions j < kv_len, and
+ * out[h] = sum_j exp(s_j - max s) v[kv][j] / sum_j exp(s_j - max s). The
+ * pages leave the score scale to the caller (1/sqrt(head_dim) is usual).
+ * f32 throughout; within 1e-5 of ||out||_inf of the f64 definition.
+ * ==================================================================== */
+
+/* Workspace bytes attn_decode_splitk needs: num_splits * n_heads *
+ * (head_dim + 2) * 4, num_splits = 0 meaning the split count the call picks
+ * for that shape. Host only. Errors as attn_decode_splitk's validation. */
+int attn_decode_workspace_bytes(int64_t n_heads, int64_t n_kv_heads, int64_t head_dim,
+                                int64_t kv_len, int64_t num_splits, size_t *bytes);
+
+/*   q         device f32 [n_heads][head_dim], 16-byte aligned.
+ *   k_cache,  device f32 [n_kv_heads][kv_stride][head_dim]: position j of KV
+ *   v_cache   head kv at row kv * kv_stride + j; rows j < kv_len are read.
+ *             16-byte aligned.
+ *   out       device f32 [n_heads][head_dim], 4-byte aligned.
+ *   num_splits  number of key ranges run in parallel (each ceil(kv_len /
+ *             num_splits) keys, trailing splits may be empty); 0 picks about
+ *             512 workgroups in all, at least 64 keys each.
+ *   workspace device, attn_decode_workspace_bytes(...) bytes, 16-byte
+ *             aligned: per split and head the running output, maximum and
+ *             denominator, read by the merge launch of the same call.
+ * Requires head_dim == 128, n_heads % n_kv_heads == 0 with n_heads /
+ * n_kv_heads in {1, 2, 4, 8}, kv_len >= 1, kv_stride >= kv_len,
+ * num_splits <= 65535. Errors: GD_EINVAL, GD_ESHAPE, GD_EALIGN, GD_ERANGE,
+ * GD_EHIP. */
+int attn_decode_splitk(const float *q, const float *k_cache, const float *v_cache, float *out,
+                       int64_t n_heads, int64_t n_kv_heads, int64_t head_dim, int64_t kv_len,
+                       int64_t kv_stride, float scale, int64_t num_splits,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/* ====================================================================
  * Measurement kernels  ("roofline.html": the FILL kernel writes a non-zero,
  * incompressible pattern so reads reach real DRAM; the read kernel streams
  * 16-byte words through an XOR into a sink)

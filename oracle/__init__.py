@@ -263,3 +263,29 @@ def quantize_q8_0(x):
     out = np.empty(n * (K // 32) * 34, dtype=np.uint8)
     lib().gdo_quantize_q8_0(xp, n, K, out.ctypes.data)
     return out
+
+
+# ------------------------------------------------------------ decode attention
+
+def attention_decode(q, k, v, scale: float):
+    """One decode token's attention, the plain f64 definition the split-K
+    kernels reach up to rounding ("BonsaiのWebGPUカーネルを読み解く", section on
+    split-K flash decode attention): for query head h, with KV head
+    kv = h // (Hq / Hkv), s_j = scale * q[h] . k[kv, j], and
+    out[h] = sum_j exp(s_j - max s) v[kv, j] / sum_j exp(s_j - max s).
+    q [Hq, D]; k, v [Hkv, L, D] (f32 or f64); returns f64 [Hq, D]."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    Hq, D = q.shape
+    Hkv, L, Dk = k.shape
+    if Dk != D or v.shape != k.shape or Hq % Hkv or L < 1:
+        raise ValueError("bad attention shapes")
+    G = Hq // Hkv
+    out = np.empty((Hq, D), dtype=np.float64)
+    for h in range(Hq):
+        kv = h // G
+        s = float(scale) * (k[kv] @ q[h])
+        p = np.exp(s - np.max(s))
+        out[h] = (p @ v[kv]) / np.sum(p)
+    return out

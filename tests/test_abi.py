@@ -30,6 +30,7 @@ def test_header_declares_the_entry_points():
               "blockq8_matmul_nt", "ternary_act_bitplanes", "ternary_gemv", "ternary_gemv_grouped",
               "q8_0_quantize", "ternary_quantize_act", "q1_sign_packed_bytes", "q1_sign_pack",
               "q1_sign_gemm_packed", "q1_sign_gemv", "q1_sign_gemm_lut4",
+              "attn_decode_workspace_bytes", "attn_decode_splitk",
               "gemm_decode_status_string", "gemm_decode_last_error", "gemm_decode_abi_version",
               "gemm_decode_fill", "gemm_decode_stream_read"]:
         assert n in names, n
@@ -139,6 +140,23 @@ def test_validation_without_gpu(gd):
     assert L.ternary_quantize_act(FAKE + 8, 1, 128, FAKE, FAKE, None) == E["align"]
     assert L.ternary_quantize_act(FAKE, 1, 128, FAKE + 2, FAKE, None) == E["align"]
     assert L.ternary_quantize_act(FAKE, 1 << 31, 128, FAKE, FAKE, None) == E["range"]
+    # decode attention: workspace = splits * heads * (head_dim + 2) floats
+    assert L.attn_decode_workspace_bytes(32, 8, 128, 4096, 0, ctypes.byref(ws)) == 0
+    assert ws.value == 64 * 32 * 130 * 4                  # 512 workgroups over 8 KV heads
+    assert L.attn_decode_workspace_bytes(32, 8, 128, 100, 0, ctypes.byref(ws)) == 0
+    assert ws.value == 2 * 32 * 130 * 4                   # no more splits than 64-key tiles
+    assert L.attn_decode_workspace_bytes(32, 8, 128, 4096, 3, ctypes.byref(ws)) == 0 and ws.value == 3 * 32 * 130 * 4
+    assert L.attn_decode_workspace_bytes(32, 8, 64, 4096, 0, ctypes.byref(ws)) == E["shape"]
+    assert L.attn_decode_workspace_bytes(24, 8, 128, 4096, 0, ctypes.byref(ws)) == E["shape"]
+    assert L.attn_decode_workspace_bytes(48, 3, 128, 4096, 0, ctypes.byref(ws)) == E["shape"]   # 16 per KV head
+    assert L.attn_decode_workspace_bytes(32, 8, 128, 0, 0, ctypes.byref(ws)) == E["inval"]
+    att = (32, 8, 128, 4096, 4096, 0.1, 0)
+    assert L.attn_decode_splitk(FAKE, FAKE, FAKE, FAKE, 32, 8, 128, 4096, 4000, 0.1, 0, FAKE, 1 << 30, None) == \
+        E["inval"]
+    assert L.attn_decode_splitk(FAKE + 4, FAKE, FAKE, FAKE, *att, FAKE, 1 << 30, None) == E["align"]
+    assert L.attn_decode_splitk(FAKE, FAKE, FAKE, FAKE, *att, FAKE, 1024, None) == E["range"]
+    assert L.attn_decode_splitk(FAKE, FAKE, FAKE, FAKE, 32, 8, 128, 4096, 4096, 0.1, 70000, FAKE, 1 << 30, None) == \
+        E["range"]
     # measurement
     assert L.gemm_decode_fill(FAKE, 100, 1, None) == E["shape"]
     assert L.gemm_decode_stream_read(FAKE, 160, 0, FAKE, 1, None) == E["inval"]
