@@ -43,17 +43,22 @@ METRIC = "Q1_0·q8_0 GEMV effective HBM GB/s (% of peak) + equiv tok/s, batch 1"
 # the kernel source they were measured on: reported only while its hash
 # matches, null after any change to it.
 _TRAFFIC = {
-    "q1": ("q1.hip", "96265188f0492ae9",
-           {"4096x4096": (37698.5, 512.0), "14336x4096": (129875.5, 1792.0)}),
+    "q1": ("q1.hip", "e5f0ac1bd2ae5af4",
+           {"4096x4096": (37685.7, 512.0), "14336x4096": (129892.4, 1792.0)}),
     "ternary": ("ternary.hip", "16436179a92f165c",
-                {"2560x2560": (97291.4, 1200.0), "6912x2560": (130263.3, 1620.0), "2560x6912": (65789.8, 300.0)}),
-    "blockq8": ("blockq8.hip", "a0d67a1723d13bce", {"m1": (25974.9, 202.4), "m16": (26263.1, 3072.0)}),
-    "sign": ("sign_gemm.hip", "850acc3ab2e1ded4",
-             {"split": (4128.6, 8208.0), "wpack": (2074.0, 4096.0), "gemm": (21355.3, 9728.0)}),
+                {"2560x2560": (97292.6, 1200.0), "6912x2560": (130263.3, 1620.0), "2560x6912": (65775.7, 300.0)}),
+    "blockq8": ("blockq8.hip", "a0d67a1723d13bce", {"m1": (25974.9, 196.4), "m16": (26263.4, 3072.0)}),
+    "sign": ("sign_gemm.hip", "1122664298d09035",
+             {"split": (4128.8, 8208.0), "wpack": (2074.7, 4096.0), "gemm": (21355.4, 9728.0)}),
+    "sign_lut": ("sign_lut.hip", "65e2776a84a05262",
+                 {"4096x4096": (2170.1, 16.0), "14336x4096": (7290.0, 56.0), "lut4": (35128.6, 8192.0)}),
     "quant": ("quantize.hip", "a7b47e9235f09149",
-              {"q8_0_decode": (266.9, 136.0), "q8_0_batch_256MiB": (131085.5, 69632.0),
-               "int8_planes_decode_step": (538.5 + 559.5, 227.8 + 203.4),
-               "int8_planes_batch_256MiB": (131167.4, 66048.0)}),
+              {"q8_0_decode": (266.9, 136.0), "q8_0_batch_256MiB": (131083.7, 69633.8),
+               "int8_planes_decode_step": (538.4 + 559.6, 227.8 + 203.4),
+               "int8_planes_batch_256MiB": (131167.0, 66048.0)}),
+    # per call: split kernel + merge kernel
+    "attention": ("attention.hip", "fb26b5a8fcf1f977",
+                  {"kv4096": (16464.3 + 597.0, 1040.0 + 16.0), "kv32768": (131153.7 + 597.0, 1040.0 + 16.0)}),
 }
 
 
@@ -509,6 +514,8 @@ def bench_sign(args, gd, torch):
         "lut4_comparator": {"note": "the page's LUT4 prefill (table lookup, VALU + LDS), packed weights",
                             "us_per_gemm": round(per_l * 1e6, 2), "value": round(flops / per_l / 1e12, 2),
                             "unit": "TFLOP/s", "vs_mfma_packed": round(per_l / per_p, 2),
+                            "traffic": (None if measured_traffic("sign_lut") is None
+                                        else measured_traffic("sign_lut")["lut4"]),
                             "parity_rel_err_sampled": rel_l},
         "decode_gemv": decode,
     }
@@ -520,6 +527,7 @@ def bench_sign_gemv(args, gd, torch):
     roofline on the packed weight bytes + x + y."""
     import oracle
     out = {}
+    lt = measured_traffic("sign_lut")
     for N, K in ((4096, 4096), (14336, 4096)):
         x, bits, scales = wl.sign_gemm_inputs(1, N, K, seed=N + K)
         wbytes = N * K // 4        # 1 bit + 1/32 of an f32 per weight
@@ -542,6 +550,7 @@ def bench_sign_gemv(args, gd, torch):
             "us_per_gemv": round(per * 1e6, 2), "value": round(bytes_ / per / 1e9, 1), "unit": "GB/s",
             "roofline": {"bound": "hbm", "achieved": round(bytes_ / per / 1e9, 1), "peak": HBM_PEAK_GBPS,
                          "unit": "GB/s", "frac": round(bytes_ / per / 1e9 / HBM_PEAK_GBPS, 4),
+                         "traffic": None if lt is None else lt[f"{N}x{K}"],
                          "kernel": "sign_gemv_kernel", "bytes_per_launch": bytes_,
                          "timing": "one HIP graph of 64 launches over distinct weight copies"},
             "parity_rel_err": float(np.max(np.abs(got - want)) / np.max(np.abs(want))),
@@ -693,6 +702,7 @@ def bench_attention(args, gd, torch):
     import oracle
     Hq, Hkv, D = 32, 8, 128
     out = {}
+    at = measured_traffic("attention")
     for L in (4096, 32768):
         rng = np.random.default_rng(L)
         q = rng.standard_normal((Hq, D), dtype=np.float32)
@@ -721,7 +731,8 @@ def bench_attention(args, gd, torch):
             "metric": "effective HBM GB/s", "value": round(bytes_ / per / 1e9, 1), "unit": "GB/s",
             "us_per_call": round(per * 1e6, 2),
             "roofline": {"bound": "hbm", "achieved": round(bytes_ / per / 1e9, 1), "peak": HBM_PEAK_GBPS,
-                         "unit": "GB/s", "frac": round(bytes_ / per / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None,
+                         "unit": "GB/s", "frac": round(bytes_ / per / 1e9 / HBM_PEAK_GBPS, 4),
+                         "traffic": None if at is None else at[f"kv{L}"],
                          "kernel": "attn_split_kernel<4> + attn_merge_kernel", "bytes_per_call": bytes_},
             "parity_rel_err": float(np.max(np.abs(got - want)) / np.max(np.abs(want))),
             "cpu_baseline": {"value": round(bytes_ / t_cpu / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
