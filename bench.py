@@ -202,8 +202,10 @@ def bench_q1(args, gd, torch):
         for r in range(n % ring):
             slot_graphs[r].replay()
 
-    run_steps(max(args.warmup, ring))
-    torch.cuda.synchronize()
+    # Untimed warmup: at least W steps, and at least --min-warmup-s of
+    # sustained load (the clocks take tens of milliseconds to ramp from idle;
+    # a warmup of a few steps would time that ramp).
+    warm_steps = spin_up(torch, run_steps, max(args.warmup, ring), args.min_warmup_s)
 
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
@@ -259,9 +261,7 @@ def bench_q1(args, gd, torch):
             with torch.cuda.graph(g, stream=torch.cuda.Stream()):
                 one_step(r)
             sgraphs.append(g)
-        for g in sgraphs:
-            g.replay()
-        torch.cuda.synchronize()
+        spin_up(torch, lambda n: [sgraphs[k % ring].replay() for k in range(n)], ring, MIN_SPIN_S)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -290,6 +290,8 @@ def bench_q1(args, gd, torch):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_note": f"{warm_steps} untimed steps ran (at least --warmup, and at least "
+                       f"{args.min_warmup_s} s of sustained load) before the {args.steps} timed ones",
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -415,11 +417,29 @@ def _events(torch):
     return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
 
+MIN_SPIN_S = 0.1   # sustained load before each short-kernel timing
+
+
+def spin_up(torch, run, n_min, min_s):
+    """Runs run(n_min), then run(n_min) again until at least min_s seconds of
+    GPU work have passed; returns the number of run() units done (untimed)."""
+    done = 0
+    t = time.perf_counter()
+    while True:
+        run(n_min)
+        torch.cuda.synchronize()
+        done += n_min
+        if time.perf_counter() - t >= min_s:
+            return done
+
+
 def _time_launches(torch, launch, n, warmup):
     """Mean time (s) per launch of n launches captured in one HIP graph and
     replayed between two HIP events on the launch stream: the launches run
     back to back whatever the host's launch rate (a kernel shorter than a
-    Python launch would otherwise leave the GPU idle between launches)."""
+    Python launch would otherwise leave the GPU idle between launches).
+    The graph is replayed untimed for MIN_SPIN_S first, so the clocks have
+    left idle."""
     for w in range(warmup):
         launch(w)
     torch.cuda.synchronize()
@@ -427,8 +447,7 @@ def _time_launches(torch, launch, n, warmup):
     with torch.cuda.graph(g, stream=torch.cuda.Stream()):
         for k in range(n):
             launch(warmup + k)
-    g.replay()
-    torch.cuda.synchronize()
+    spin_up(torch, lambda _n: g.replay(), 1, MIN_SPIN_S)
     t0, t1 = _events(torch)
     t0.record()
     g.replay()
@@ -797,9 +816,7 @@ def bench_ternary(args, gd, torch):
         for sh, idx in groups.items():
             gd.ternary_gemv_grouped(sset[sh], len(idx), sh[0], sh[1])
 
-    for w in range(3):
-        step(w)
-    torch.cuda.synchronize()
+    spin_up(torch, lambda n: [step(w) for w in range(n)], 3, args.min_warmup_s)
     # timed steps: launches queued back to back, events only at the ends
     t0, t1 = _events(torch)
     t0.record()
@@ -871,6 +888,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--min-warmup-s", type=float, default=0.2,
+                    help="untimed warmup continues until this much sustained load has run")
     ap.add_argument("--workload", default="all",
                     choices=["all", "q1", "q1mm", "sign", "blockq8", "ternary", "quant", "attention"],
                     help="all (default): the Q1 metric line plus the other paths under 'workloads'")

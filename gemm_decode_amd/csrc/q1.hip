@@ -37,6 +37,8 @@ constexpr int kGroupsPerThread = kChunkBlocks * 32 / kThreads;   // 2
 // thread kernel (latency); larger ones fill the chip with 256-row blocks.
 constexpr int64_t kLatMaxRowBlocks = 64;
 constexpr int64_t kLatWideRows = 8192;
+// Threads per workgroup of the grouped launch (two per row of a 64-row tile).
+constexpr int kGroupedThreads = 512;
 
 // Pointers into device global memory (address space 1), so weight loads are
 // global_load (counted by vmcnt only), not flat loads that also hold lgkmcnt.
@@ -272,15 +274,15 @@ __device__ __forceinline__ void group8(const char *tab, u32x2 (&wb)[8], u32x4 &s
 // the chunk's tables built in LDS. Straight-line code: three register
 // buffers, each group's loads issued two groups before it is consumed
 // (group indices clamped to the last full group, so every load is issued).
-template <int H>
+template <int H, int NT>
 __device__ __forceinline__ void chunk(float *tab, const Q1Args &p, const RowPtrs &rp, int64_t g0, int64_t n4,
                                       int64_t ng, int64_t nb, float (&acc)[4]) {
     const char *tabc = reinterpret_cast<const char *>(tab);
     const int64_t gl = ng - 1;
     const int64_t i0 = 8 * g0;
     const int cb = static_cast<int>((nb - i0) < kChunkBlocks ? (nb - i0) : kChunkBlocks);
-    TableRaw raw;
-    table_loads(raw, p.a, i0, cb);
+    TableRawN<NT> raw;
+    table_loads<NT>(raw, p.a, i0, cb);
     asm volatile("" ::: "memory");   // keep the table loads ahead of the prefetch
     u32x2 w0[8], w1[8], w2[8];
     u32x4 s0, s1, s2;
@@ -288,7 +290,7 @@ __device__ __forceinline__ void chunk(float *tab, const Q1Args &p, const RowPtrs
     load_group(rp, (g0 + 1 < gl) ? g0 + 1 : gl, w1, s1);
     load_group(rp, (g0 + 2 < gl) ? g0 + 2 : gl, w2, s2);
     if (g0 > 0) __syncthreads();
-    table_store(tab, raw, cb);
+    table_store<NT>(tab, raw, cb);
     __syncthreads();
     group8<H, 0, true>(tabc, w0, s0, acc, rp, (g0 + 3 < gl) ? g0 + 3 : gl);
     if (n4 > 1) group8<H, 8, false>(tabc, w1, s1, acc, rp, 0);
@@ -321,22 +323,22 @@ __device__ __forceinline__ float d0_of(const u32x4 &s8, int idx) {
     return f16_to_f32(static_cast<uint16_t>((idx & 1) ? (word >> 16) : (word & 0xffffu)));
 }
 
-template <int H>
+template <int H, int NT>
 __device__ __forceinline__ void half_row(float *tab, const Q1Args &p, const RowPtrs &rp, int64_t nb, float (&acc)[4]) {
     const int64_t ng = nb / 8;
     constexpr int kGroupsPerChunk = kChunkBlocks / 8;
     for (int64_t g0 = 0; g0 < ng; g0 += kGroupsPerChunk) {
         const int64_t n4 = (ng - g0) < kGroupsPerChunk ? (ng - g0) : kGroupsPerChunk;
-        chunk<H>(tab, p, rp, g0, n4, ng, nb, acc);
+        chunk<H, NT>(tab, p, rp, g0, n4, ng, nb, acc);
     }
     const int64_t it0 = ng * 8;
     if (it0 < nb) {   // tail: the last nb % 8 blocks
         const int64_t c0 = it0 / kChunkBlocks * kChunkBlocks;
         if (it0 % kChunkBlocks == 0) {
             if (ng > 0) __syncthreads();
-            TableRaw raw;
-            table_loads(raw, p.a, it0, static_cast<int>(nb - it0));
-            table_store(tab, raw, static_cast<int>(nb - it0));
+            TableRawN<NT> raw;
+            table_loads<NT>(raw, p.a, it0, static_cast<int>(nb - it0));
+            table_store<NT>(tab, raw, static_cast<int>(nb - it0));
             __syncthreads();
         }
         const u32x4 s8 = rp.sc[(it0 >> 3) * 64];
@@ -348,10 +350,12 @@ __device__ __forceinline__ void half_row(float *tab, const Q1Args &p, const RowP
     }
 }
 
+// NT threads: NT/128 tiles of 64 rows, two waves (halves) each.
+template <int NT>
 __device__ __forceinline__ void q1_gemv_body(const Q1Args &p, float *tab, int64_t rows, int64_t nb, int64_t nb8) {
     const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
     const int tl = wave >> 1, h = wave & 1;
-    const int64_t r = static_cast<int64_t>(blockIdx.x) * kRowsPerWG + tl * 64 + lane;
+    const int64_t r = static_cast<int64_t>(blockIdx.x) * (NT / 2) + tl * 64 + lane;
     const int64_t r64 = (rows + 63) / 64 * 64;
     // Rows past the padded rows read the last padded row (never stored), so
     // every thread runs the same loads and barriers.
@@ -360,9 +364,9 @@ __device__ __forceinline__ void q1_gemv_body(const Q1Args &p, float *tab, int64_
     RowPtrs rp{(gptr_u2)p.bits + ((t * nb) * 2 + h) * 64 + ln, (gptr_u4)p.scales + t * (nb8 / 8) * 64 + ln};
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     if (h == 0)
-        half_row<0>(tab, p, rp, nb, acc);
+        half_row<0, NT>(tab, p, rp, nb, acc);
     else
-        half_row<1>(tab, p, rp, nb, acc);
+        half_row<1, NT>(tab, p, rp, nb, acc);
     // The high half hands lanes 4..7 to the low half through LDS.
     __syncthreads();
     float4 *xch = reinterpret_cast<float4 *>(tab) + tl * 64 + lane;
@@ -380,18 +384,19 @@ __global__ __launch_bounds__(kThreads) void q1_gemv_kernel(const uint32_t *bits,
     __shared__ float tab[kTableFloats];
     const int64_t c = blockIdx.y;   // activation column
     Q1Args p{bits, scales, a + c * (nb * 4) * 17, y + c * rows};
-    q1_gemv_body(p, tab, rows, nb, nb8);
+    q1_gemv_body<kThreads>(p, tab, rows, nb, nb8);
 }
 
-__global__ __launch_bounds__(kThreads) void q1_gemv_grouped_kernel(const gd_q1_problem *probs, int64_t rows,
-                                                                   int64_t nb, int64_t nb8) {
+template <int NT>
+__global__ __launch_bounds__(NT) void q1_gemv_grouped_kernel(const gd_q1_problem *probs, int64_t rows, int64_t nb,
+                                                             int64_t nb8) {
     __shared__ float tab[kTableFloats];
     const gd_q1_problem pr = probs[blockIdx.y];
     const int64_t prow = (pr.rows >= 1 && pr.rows <= rows) ? pr.rows : rows;
-    if (static_cast<int64_t>(blockIdx.x) * kRowsPerWG >= prow) return;   // uniform: before any barrier
+    if (static_cast<int64_t>(blockIdx.x) * (NT / 2) >= prow) return;   // uniform: before any barrier
     Q1Args p{static_cast<const uint32_t *>(pr.bits_plane), static_cast<const uint4 *>(pr.scale_plane),
              static_cast<const uint16_t *>(pr.a_q8), pr.y};
-    q1_gemv_body(p, tab, prow, nb, nb8);
+    q1_gemv_body<NT>(p, tab, prow, nb, nb8);
 }
 
 // ------------------------------------------------------- several columns
@@ -870,8 +875,9 @@ extern "C" int q1_q8_gemv_grouped(const gd_q1_problem *problems, int64_t count, 
     GD_REQUIRE(count <= 65535, GD_ERANGE, "q1_q8_gemv_grouped: count (%lld) above 65535", (long long)count);
     GD_REQUIRE(aligned(problems, 8), GD_EALIGN, "q1_q8_gemv_grouped: problems must be 8-byte aligned");
     const int64_t nb = K / 128, nb8 = (nb + 7) / 8 * 8;
-    const int64_t gx = (rows + kRowsPerWG - 1) / kRowsPerWG;
-    hipLaunchKernelGGL(q1_gemv_grouped_kernel, dim3(static_cast<uint32_t>(gx), static_cast<uint32_t>(count)),
-                       dim3(kThreads), 0, as_stream(stream), problems, rows, nb, nb8);
+    constexpr int NT = kGroupedThreads;
+    const int64_t gx = (rows + NT / 2 - 1) / (NT / 2);
+    hipLaunchKernelGGL(q1_gemv_grouped_kernel<NT>, dim3(static_cast<uint32_t>(gx), static_cast<uint32_t>(count)),
+                       dim3(NT), 0, as_stream(stream), problems, rows, nb, nb8);
     return check_launch("q1_q8_gemv_grouped");
 }
