@@ -227,6 +227,7 @@ constexpr int kMfmaWaves = 12;
 constexpr int kMfmaThreads = 64 * kMfmaWaves;
 constexpr int kMfmaMaxK = 1024;
 constexpr int kScStride = 33;          // padded row of staged block scales
+constexpr int kAhead = 12;             // weight blocks in flight per lane
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
@@ -290,14 +291,19 @@ __global__ __launch_bounds__(kMfmaThreads) void blockq8_mfma_kernel(const float 
         const int b = (l % 32) < nb ? (l % 32) : nb - 1;
         sv[i] = scales[r * nb + b];
     }
-    // 3. every block of this lane's feature: 8 bytes at k slice g
+    // 3. this lane's feature, 8 bytes at k slice g per block: the first
+    //    kAhead blocks now, each later one when the block kAhead before it is
+    //    consumed. A window keeps the data arriving in the order it is used;
+    //    issuing every block at once (all waves on the chip do) lets the
+    //    first ones arrive anywhere in the whole stream.
     const int64_t row = n0 + j < n ? n0 + j : n - 1;
+    auto wload = [&](int b) {
+        const int bc = b < nb ? b : nb - 1;
+        return quants[row * (k / 8) + 4 * bc + g];
+    };
     u32x2 wq[NB];
 #pragma unroll
-    for (int b = 0; b < NB; b++) {
-        const int bc = b < nb ? b : nb - 1;
-        wq[b] = quants[row * (k / 8) + 4 * bc + g];
-    }
+    for (int b = 0; b < (kAhead < NB ? kAhead : NB); b++) wq[b] = wload(b);
 
     // 4. per-row power of two: largest |x| of each row over the workgroup
     float amax = 0.0f;
@@ -311,8 +317,8 @@ __global__ __launch_bounds__(kMfmaThreads) void blockq8_mfma_kernel(const float 
     amax = fmaxf(amax, __shfl_xor(amax, 32));
     if (l < 16) wmax[wv][l] = amax;
 #pragma unroll
-    for (int i = 0; i < 8; i++)
-        if (l % 32 < nb) sc[wv][2 * i + l / 32][l % 32] = sv[i];
+    for (int i = 0; i < 8; i++)   // blocks past nb get scale 0 (computed, contribute 0)
+        if (l % 32 < NB) sc[wv][2 * i + l / 32][l % 32] = (l % 32) < nb ? sv[i] : 0.0f;
     __syncthreads();
     float rm = 0.0f;
 #pragma unroll
@@ -322,11 +328,11 @@ __global__ __launch_bounds__(kMfmaThreads) void blockq8_mfma_kernel(const float 
 #pragma unroll
     for (int it = 0; it < kSlotIters; it++) {
         const int s = tid + it * kMfmaThreads;
-        if (s < 64 * nb) {
+        if (s < kSlots) {   // blocks past nb are staged as zero
             half8 hv, lv;
 #pragma unroll
             for (int e = 0; e < 8; e++) {
-                const float v = __builtin_ldexpf(xv[it][e / 4][e % 4], ex);
+                const float v = s < 64 * nb ? __builtin_ldexpf(xv[it][e / 4][e % 4], ex) : 0.0f;
                 hv[e] = static_cast<_Float16>(v);
                 lv[e] = static_cast<_Float16>(v - static_cast<float>(hv[e]));
             }
@@ -336,29 +342,30 @@ __global__ __launch_bounds__(kMfmaThreads) void blockq8_mfma_kernel(const float 
     }
     __syncthreads();
 
-    // 5. one block per step: sub-total on the matrix cores, then the scale
-    int nexp[4];
-#pragma unroll
-    for (int r = 0; r < 4; r++) nexp[r] = -rexp[4 * g + r];
+    // 5. one block per step: sub-total on the matrix cores, then the scale.
+    //    Every one of the NB blocks is computed (the ones past nb have zero
+    //    activations and scale), so the steps carry no branches and the
+    //    compiler overlaps consecutive blocks. The row's 2^-e is applied once
+    //    at the end: in the normal range scaling by a power of two commutes
+    //    with rounding, so this equals unscaling each sub-total first.
     floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int b = 0; b < NB; b++) {
-        if (b < nb) {
-            union { uint32_t u[4]; half8 h; } bw;
-            q8_to_half4(wq[b][0], bw.u[0], bw.u[1]);
-            q8_to_half4(wq[b][1], bw.u[2], bw.u[3]);
-            floatx4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xop[b][0][l], bw.h, floatx4{0.0f, 0.0f, 0.0f, 0.0f},
-                                                               0, 0, 0);
-            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xop[b][1][l], bw.h, d, 0, 0, 0);
-            const float s = sc[wv][j][b];
+        if (b + kAhead < NB) wq[b + kAhead] = wload(b + kAhead);
+        union { uint32_t u[4]; half8 h; } bw;
+        q8_to_half4(wq[b][0], bw.u[0], bw.u[1]);
+        q8_to_half4(wq[b][1], bw.u[2], bw.u[3]);
+        floatx4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xop[b][0][l], bw.h, floatx4{0.0f, 0.0f, 0.0f, 0.0f},
+                                                           0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xop[b][1][l], bw.h, d, 0, 0, 0);
+        const float s = sc[wv][j][b];
 #pragma unroll
-            for (int r = 0; r < 4; r++) acc[r] = __builtin_fmaf(s, __builtin_ldexpf(d[r], nexp[r]), acc[r]);
-        }
+        for (int r = 0; r < 4; r++) acc[r] = __builtin_fmaf(s, d[r], acc[r]);
     }
     if (n0 + j < n) {
 #pragma unroll
         for (int r = 0; r < 4; r++)
-            if (4 * g + r < m) y[(4 * g + r) * n + n0 + j] = acc[r];
+            if (4 * g + r < m) y[(4 * g + r) * n + n0 + j] = __builtin_ldexpf(acc[r], -rexp[4 * g + r]);
     }
 }
 
