@@ -37,6 +37,11 @@ constexpr int kGroupsPerThread = kChunkBlocks * 32 / kThreads;   // 2
 // thread kernel (latency); larger ones fill the chip with 256-row blocks.
 constexpr int64_t kLatMaxRowBlocks = 64;
 constexpr int64_t kLatWideRows = 8192;
+// While n_act * rows stays within this (about four waves per SIMD in all), a
+// few-row product runs as independent one-chain-per-thread GEMVs, one per
+// column (each re-reads the weights, mostly from cache), rather than the
+// kernel that shares one read of them across columns.
+constexpr int64_t kLatMaxColumnRows = 32768;
 // Threads per workgroup of the grouped launch (two per row of a 64-row tile).
 constexpr int kGroupedThreads = 512;
 
@@ -699,14 +704,17 @@ __device__ __forceinline__ void lat_chunk_short(const char *tab, const LatBuf &b
     }
 }
 
+// blockIdx.y is the activation column: each column is its own batch-1 GEMV.
 template <int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void q1_gemv_lat_kernel(const uint32_t *bits, const uint4 *scales,
-                                                                 const uint16_t *a, float *y, int64_t rows,
+                                                                 const uint16_t *a_all, float *y_all, int64_t rows,
                                                                  int64_t nb, int64_t nb8) {
     constexpr int NT = WAVES * 64;
     constexpr int R = 8 * WAVES;   // rows per workgroup
     __shared__ float tab[kTableFloats];
     __shared__ float xch[R * 8];
+    const uint16_t *a = a_all + static_cast<int64_t>(blockIdx.y) * (nb * 4) * 17;
+    float *y = y_all + static_cast<int64_t>(blockIdx.y) * rows;
     const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
     const int h = wave & 1, j = lane >> 4;
     const int rloc = (wave >> 1) * 16 + (lane & 15);
@@ -825,6 +833,21 @@ extern "C" int q1_q8_gemv(const void *bits_plane, const void *scale_plane, const
     const uint32_t *bp = static_cast<const uint32_t *>(bits_plane);
     const uint4 *sp = static_cast<const uint4 *>(scale_plane);
     const uint16_t *ap = static_cast<const uint16_t *>(a_q8);
+    if (gx <= kLatMaxRowBlocks && (n_act == 1 || n_act * rows <= kLatMaxColumnRows)) {
+        // One chain per thread, each column its own GEMV (blockIdx.y). A
+        // wave is 16 rows whatever the workgroup, so 32-row workgroups (one
+        // wave per SIMD) until they would stack on the CUs, then 64-row ones,
+        // which build half as many tables.
+        const uint32_t cols = static_cast<uint32_t>(n_act);
+        if (rows >= kLatWideRows) {
+            hipLaunchKernelGGL(q1_gemv_lat_kernel<8>, dim3(static_cast<uint32_t>((rows + 63) / 64), cols), dim3(512),
+                               0, hs, bp, sp, ap, y, rows, nb, nb8);
+        } else {
+            hipLaunchKernelGGL(q1_gemv_lat_kernel<4>, dim3(static_cast<uint32_t>((rows + 31) / 32), cols), dim3(256),
+                               0, hs, bp, sp, ap, y, rows, nb, nb8);
+        }
+        return check_launch("q1_q8_gemv");
+    }
     if (n_act >= 2) {   // columns in groups that share one read of the weights
         // The largest group (8, 4, 2 columns) that still gives about three
         // quarters of the 256 CUs a workgroup; fewer workgroups leave CUs
@@ -845,19 +868,7 @@ extern "C" int q1_q8_gemv(const void *bits_plane, const void *scale_plane, const
             hipLaunchKernelGGL(q1_gemv_mc_kernel<8>, grid, dim3(kThreads), 0, hs, bp, sp, ap, y, rows, nb, nb8, n_act);
         return check_launch("q1_q8_gemv");
     }
-    if (gx <= kLatMaxRowBlocks) {
-        // One chain per thread. A wave is 16 rows whatever the workgroup, so
-        // 32-row workgroups (one wave per SIMD) until they would stack on the
-        // CUs, then 64-row ones, which build half as many tables.
-        if (rows >= kLatWideRows) {
-            hipLaunchKernelGGL(q1_gemv_lat_kernel<8>, dim3(static_cast<uint32_t>((rows + 63) / 64)), dim3(512), 0, hs,
-                               bp, sp, ap, y, rows, nb, nb8);
-        } else {
-            hipLaunchKernelGGL(q1_gemv_lat_kernel<4>, dim3(static_cast<uint32_t>((rows + 31) / 32)), dim3(256), 0, hs,
-                               bp, sp, ap, y, rows, nb, nb8);
-        }
-        return check_launch("q1_q8_gemv");
-    }
+
     hipLaunchKernelGGL(q1_gemv_kernel, dim3(static_cast<uint32_t>(gx), static_cast<uint32_t>(n_act)),
                        dim3(kThreads), 0, as_stream(stream), static_cast<const uint32_t *>(bits_plane),
                        static_cast<const uint4 *>(scale_plane), static_cast<const uint16_t *>(a_q8), y, rows, nb,

@@ -149,6 +149,29 @@ def test_single_gemv_paths(gd, rows, K):
     assert np.all(np.isnan(got[rows:])), "wrote past the last row"
 
 
+@pytest.mark.parametrize("rows,K,n_act", [
+    (4096, 4096, 8),     # n_act * rows = 32768: one one-chain-per-thread GEMV per column
+    (4096, 4096, 9),     # just past it: the shared-weight kernel
+    (2049, 1152, 16),    # past it, short chunks
+    (14336, 4096, 2),    # 64-row workgroups, two columns
+    (300, 4224, 3),      # a column chunk of one block
+])
+def test_columns_across_the_dispatch_boundary(gd, rows, K, n_act):
+    """Several columns on either side of the switch between per-column
+    GEMVs and the shared-weight kernel: every column bit-exact with its own
+    batch-1 GEMV, nothing written past the last column."""
+    W = wl.q1_weights_aos(rows, K, rows + 3 * n_act)
+    A = np.concatenate([wl.q8_acts_aos(K, 500 + 17 * c + rows) for c in range(n_act)])
+    b, s = planes_on_gpu(gd, W, rows, K)
+    y = torch.full((n_act * rows + 64,), float("nan"), dtype=torch.float32, device="cuda")
+    gd.q1_q8_gemv(b, s, dev(A.reshape(-1)), y[:n_act * rows], rows, K, n_act)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy()
+    want = oracle.q1_q8_gemv_aos(W, A, rows, K, n_act=n_act, nthreads=oracle.max_threads())
+    assert_bits_equal(got[:n_act * rows].reshape(n_act, rows), want.reshape(n_act, rows), f"{rows}x{K} n={n_act}")
+    assert np.all(np.isnan(got[n_act * rows:])), "wrote past the last column"
+
+
 def test_special_scales_and_bits(gd):
     """Subnormal, zero and large d0/d1, all-ones and all-zeros sign bits."""
     rows, K = 128, 1024
