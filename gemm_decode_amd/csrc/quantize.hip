@@ -64,15 +64,38 @@ __global__ __launch_bounds__(kThreads) void q8_0_quantize_kernel(const float4 *_
 }
 
 // ------------------------------------------------------- per-token int8
-// One workgroup (four waves) per token. Stripe s holds elements 64s..64s+63;
-// wave w owns stripes wR .. wR+R-1 (K <= 256 R). Each lane loads its
-// element of each of its stripes at once, the token's absmax meets through
-// the waves and LDS, and each stripe's codes give, by eight ballots, its two
-// words of every plane (plane b, word m, bit j = bit b of the two's-
-// complement code of element 32m + j). The words are gathered into one
-// register per plane (lane 2i+h takes word h of stripe i) and each plane's
-// run of 2R words is written by one coalesced store. Past K the lanes vote
-// 0, and words past K/32 are not written.
+// One workgroup (four waves) per token. Chunk c holds elements 256c..256c+255,
+// lane l its four elements 256c + 4l .. +3 (one 16-byte load); wave w owns
+// chunks wR .. wR+R-1 (K <= 1024 R), all loaded at once. The token's absmax
+// meets through the waves and LDS. Codes are decided in f32 first: with
+// v32 = x * f32(127/absmax), |v32 - v| <= 1.5e-5 for the f64 product v the
+// rule rounds, so Math.round(v32) = Math.round(v) unless v32 lies within
+// kTieGuard of a half-integer, and only those elements are decided again in
+// f64 exactly as the rule states. Planes: lanes 8g .. 8g+7 of a chunk hold the
+// 32 elements of plane word 8c + g; each lane forms plane b's 4 bits of its
+// codes with one v_dot4_u32_u8 on the code bytes masked to bit b, places them
+// at bits 4(l%8).., the 8 lanes OR them together with three DPP steps, and
+// lane 8g + b keeps plane b's word, so one store per chunk writes all 64
+// words (plane b, word 8c + g at lane 8g + b).
+constexpr float kTieGuard = 6.4e-5f;   // 4x the f32 error bound above
+
+__device__ __forceinline__ uint32_t or8(uint32_t v) {   // OR over the 8 lanes of a half-row
+    v |= static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0xB1, 0xF, 0xF, false));   // quad [1,0,3,2]
+    v |= static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x4E, 0xF, 0xF, false));   // quad [2,3,0,1]
+    v |= static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x141, 0xF, 0xF, false));  // half-row mirror
+    return v;
+}
+
+__device__ __forceinline__ int32_t code_of(float x, float inv32, double inv) {
+    const float v = x * inv32;
+    const float fl = floorf(v);
+    const float fr = v - fl;
+    if (fabsf(fr - 0.5f) < kTieGuard) return round_code(static_cast<double>(x) * inv);   // near a tie: f64
+    float q = fl + (fr >= 0.5f ? 1.0f : 0.0f);
+    q = q > 127.0f ? 127.0f : (q < -127.0f ? -127.0f : q);
+    return static_cast<int32_t>(q);
+}
+
 __device__ __forceinline__ float token_absmax(float m, float *red, int wave, int lane) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
@@ -85,45 +108,43 @@ template <int R>
 __global__ __launch_bounds__(kThreads) void act_quant_kernel(const float *__restrict__ x,
                                                              uint32_t *__restrict__ planes,
                                                              float *__restrict__ scale, int64_t K) {
-    static_assert(2 * R <= 64, "a plane's words of one wave fit one register");
     __shared__ float red[kThreads / 64];
     const int64_t c = blockIdx.x;
     const float *xr = x + c * K;
     const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
-    const int64_t s0 = static_cast<int64_t>(wave) * R;
-    float v[R];
+    const int64_t c0 = static_cast<int64_t>(wave) * R;   // this wave's first chunk
+    const int64_t nq = K / 4;                            // float4s of the token
+    float4 v[R];
     float m = 0.0f;
 #pragma unroll
     for (int i = 0; i < R; i++) {
-        const int64_t e = (s0 + i) * 64 + lane;
-        v[i] = xr[e < K ? e : K - 1];   // clamped: every load issued, the extra ones unused
-        if (e < K) m = fmaxf(m, fabsf(v[i]));
+        const int64_t e4 = (c0 + i) * 64 + lane;
+        v[i] = reinterpret_cast<const float4 *>(xr)[e4 < nq ? e4 : nq - 1];   // clamped: issued, not used
+        if (e4 < nq) m = fmaxf(m, absmax4(v[i]));
     }
     const double amax = static_cast<double>(token_absmax(m, red, wave, lane));
     const double inv = amax > 0.0 ? 127.0 / amax : 0.0;
+    const float inv32 = static_cast<float>(inv);
     if (threadIdx.x == 0) scale[c] = amax > 0.0 ? static_cast<float>(amax / 127.0) : 0.0f;
-    uint32_t pw[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    const int64_t W = K / 32;
+    const int k8 = lane % 8, g = lane / 8;
 #pragma unroll
     for (int i = 0; i < R; i++) {
-        if ((s0 + i) * 64 < K) {   // uniform per wave
-            const int64_t e = (s0 + i) * 64 + lane;
-            const int32_t q = (e < K) ? round_code(static_cast<double>(v[i]) * inv) : 0;
-            const uint32_t u = static_cast<uint32_t>(q) & 0xffu;
-            const bool lo_here = lane == 2 * i, hi_here = lane == 2 * i + 1;
+        if ((c0 + i) * 256 < K) {   // uniform per wave
+            const float e[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+            uint32_t u = 0;
+#pragma unroll
+            for (int j = 0; j < 4; j++) u |= (static_cast<uint32_t>(code_of(e[j], inv32, inv)) & 0xffu) << (8 * j);
+            uint32_t mine = 0;
 #pragma unroll
             for (int b = 0; b < 8; b++) {
-                const uint64_t mb = __ballot((u >> b) & 1u);
-                pw[b] = lo_here ? static_cast<uint32_t>(mb) : pw[b];
-                pw[b] = hi_here ? static_cast<uint32_t>(mb >> 32) : pw[b];
+                const uint32_t nib = __builtin_amdgcn_udot4(u & (0x01010101u << b), 0x08040201u, 0u, false) >> b;
+                const uint32_t word = or8(nib << (4 * k8));
+                mine = (k8 == b) ? word : mine;
             }
+            const int64_t wi = (c0 + i) * 8 + g;   // plane word index of this lane's group
+            if (wi < W) planes[c * 8 * W + k8 * W + wi] = mine;
         }
-    }
-    const int64_t W = K / 32;
-    const int64_t w0 = 2 * s0;   // this wave's first word of each plane
-    if (lane < 2 * R && w0 + lane < W) {
-        uint32_t *pl = planes + c * 8 * W + w0 + lane;
-#pragma unroll
-        for (int b = 0; b < 8; b++) pl[b * W] = pw[b];
     }
 }
 
@@ -197,15 +218,15 @@ extern "C" int ternary_quantize_act(const float *x, int64_t count, int64_t K, ui
                "ternary_quantize_act: planes and x_scale must be 4-byte aligned");
     const dim3 grid(static_cast<uint32_t>(count)), block(kThreads);
     hipStream_t hs = as_stream(stream);
-    const int64_t per_lane = (K + kThreads - 1) / kThreads;   // elements each lane holds
-    if (per_lane <= 4)
+    const int64_t chunks_per_wave = (K + 1023) / 1024;   // 256-element chunks, four waves
+    if (chunks_per_wave <= 1)
+        hipLaunchKernelGGL(act_quant_kernel<1>, grid, block, 0, hs, x, planes, x_scale, K);
+    else if (chunks_per_wave <= 2)
+        hipLaunchKernelGGL(act_quant_kernel<2>, grid, block, 0, hs, x, planes, x_scale, K);
+    else if (chunks_per_wave <= 4)
         hipLaunchKernelGGL(act_quant_kernel<4>, grid, block, 0, hs, x, planes, x_scale, K);
-    else if (per_lane <= 8)
+    else if (chunks_per_wave <= 8)
         hipLaunchKernelGGL(act_quant_kernel<8>, grid, block, 0, hs, x, planes, x_scale, K);
-    else if (per_lane <= 16)
-        hipLaunchKernelGGL(act_quant_kernel<16>, grid, block, 0, hs, x, planes, x_scale, K);
-    else if (per_lane <= 32)
-        hipLaunchKernelGGL(act_quant_kernel<32>, grid, block, 0, hs, x, planes, x_scale, K);
     else
         hipLaunchKernelGGL(act_quant_long_kernel, grid, block, 0, hs, x, planes, x_scale, K);
     return check_launch("ternary_quantize_act");

@@ -105,6 +105,26 @@ def test_token_planes_and_scales(gd, count, K):
     assert np.array_equal(scale.cpu().numpy().view(np.uint32), s.view(np.uint32))
 
 
+@pytest.mark.parametrize("K", [256, 2560, 8192])
+def test_token_codes_at_ties(gd, K):
+    """Tokens whose scaled values sit exactly on half-integers, and one f32
+    ulp either side of them: the f32 decision must hand these to the exact
+    f64 rule (ties toward +infinity), bit for bit with the oracle."""
+    rng = np.random.default_rng(K)
+    base = rng.integers(-126, 126, size=(3, K)).astype(np.float64) + 0.5
+    x = base.astype(np.float32)
+    x[0, 0] = 127.0                                        # absmax 127: the reciprocal is exactly 1
+    x[1] = np.nextafter(x[1], np.float32(np.inf))          # just above the ties
+    x[1, 0] = 127.0
+    x[2] = np.nextafter(x[2], np.float32(-np.inf))         # just below
+    x[2, 0] = -127.0
+    planes, scale = run_act(gd, x)
+    q, s = oracle.quantize_absmax_int8(x)
+    assert np.array_equal(planes.cpu().numpy().view(np.uint32).reshape(3, 8, K // 32), planes_of(q))
+    assert np.array_equal(scale.cpu().numpy().view(np.uint32), s.view(np.uint32))
+    assert np.array_equal(q[0, 1:], np.floor(base[0, 1:] + 0.5).astype(np.int8))   # ties went up
+
+
 def test_zero_input(gd):
     x = np.zeros((2, 128), dtype=np.float32)
     assert not run_q8(gd, x).any()
