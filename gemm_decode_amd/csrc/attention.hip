@@ -11,9 +11,10 @@
 // each key and value row is read from HBM once for all of them. Keys come in
 // tiles of 64: the K and V tile are loaded with 16-byte coalesced loads into
 // registers one tile ahead, stored to LDS, and then wave w serves query head
-// 4i + w: lane t scores key t (scale*q . k over 128 dims, q pre-scaled in
-// LDS and read by broadcast, K rows padded to 132 floats so the lanes'
-// 16-byte reads hit distinct banks), the wave's maximum and sum of exp
+// 4i + w: lane t scores key t (scale * (q . k) over 128 dims, q read with
+// scalar loads since it is the same for the whole wave, K rows padded to 132
+// floats in LDS so the lanes' 16-byte reads hit distinct banks), the wave's
+// maximum and sum of exp
 // update the running state, and lane l accumulates output dims 2l, 2l+1
 // over the tile's keys, each key's weight taken from its lane with
 // v_readlane. The split writes its running output, maximum and denominator.
@@ -79,15 +80,11 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(const float *__res
     constexpr int P = (G + 3) / 4;   // query heads per wave
     __shared__ f32x4 ks[kT * kKPad / 4];
     __shared__ f32x2 vs[kT * kD / 2];
-    __shared__ f32x4 qs[G * kD / 4];
     const int64_t kvh = blockIdx.x, split = blockIdx.y;
-    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / 64);   // wave-uniform
+    const int lane = threadIdx.x % 64;
     const int64_t j0 = split * keys_per_split;
     const int64_t j1 = (j0 + keys_per_split) < kv_len ? (j0 + keys_per_split) : kv_len;
-    for (int i = threadIdx.x; i < G * kD / 4; i += kThreads) {
-        const f32x4 v = ((g_f4)(q + (kvh * G) * kD))[i];
-        qs[i] = v * scale;
-    }
     const float *kb = kc + kvh * kv_stride * kD;
     const float *vb = vc + kvh * kv_stride * kD;
     float m[P], l[P], acc[P][2];
@@ -116,11 +113,14 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(const float *__res
         for (int p = 0; p < P; p++) {
             const int h = 4 * p + wave;   // uniform per wave
             if (h < G) {
+                // q[h] is the same for every lane: a uniform address, read
+                // with scalar loads and used as scalar operands
+                const g_f4 qh = (g_f4)(q + (kvh * G + h) * kD);
                 float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
                 for (int c = 0; c < kD / 4; c += 2) {
                     const f32x4 k0 = ks[lane * (kKPad / 4) + c], k1 = ks[lane * (kKPad / 4) + c + 1];
-                    const f32x4 q0 = qs[h * (kD / 4) + c], q1 = qs[h * (kD / 4) + c + 1];
+                    const f32x4 q0 = qh[c], q1 = qh[c + 1];
                     s0 = __builtin_fmaf(q0[0], k0[0], s0);
                     s0 = __builtin_fmaf(q0[1], k0[1], s0);
                     s0 = __builtin_fmaf(q0[2], k0[2], s0);
@@ -130,7 +130,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(const float *__res
                     s1 = __builtin_fmaf(q1[2], k1[2], s1);
                     s1 = __builtin_fmaf(q1[3], k1[3], s1);
                 }
-                const float s = lane < nvalid ? s0 + s1 : -__builtin_inff();
+                const float s = lane < nvalid ? scale * (s0 + s1) : -__builtin_inff();
                 const float mnew = fmaxf(m[p], wave_max(s));   // finite: nvalid >= 1
                 const float pr = lane < nvalid ? expf(s - mnew) : 0.0f;
                 const float corr = expf(m[p] - mnew);         // 0 on the first tile
