@@ -62,6 +62,7 @@ struct TernArgs {
     float *y;
     int32_t *dot;
     float w_scale, x_scale;
+    const float *xs_dev;  // device activation scale (read in place of x_scale), or null
 };
 
 // Per-lane partial counts over words [w0, w0+4): cnt[b] += pc(bfi(B_b, P, N)),
@@ -83,6 +84,7 @@ __device__ __forceinline__ void count4(const uint4 &p4, const uint4 &n4, const u
 
 __device__ __forceinline__ void ternary_body(const TernArgs &a, uint32_t *xl, int64_t rows, int64_t W) {
     const int64_t W4 = (W + 3) / 4 * 4;
+    const float x_scale = a.xs_dev ? *a.xs_dev : a.x_scale;
     // stage the planes (zero-padded to a multiple of 4 words) into LDS
     for (int64_t i = threadIdx.x; i < 8 * W4; i += kThreads) {
         const int64_t b = i / W4, m = i % W4;
@@ -123,7 +125,7 @@ __device__ __forceinline__ void ternary_body(const TernArgs &a, uint32_t *xl, in
         part += __shfl_xor(part, 2, kLanesPerRow);
         part += __shfl_xor(part, 4, kLanesPerRow);
         if (lane == 0 && r < rows) {
-            const float s = a.w_scale * a.x_scale;
+            const float s = a.w_scale * x_scale;
             a.y[r] = static_cast<float>(part) * s;
             if (a.dot) a.dot[r] = part;
         }
@@ -131,17 +133,18 @@ __device__ __forceinline__ void ternary_body(const TernArgs &a, uint32_t *xl, in
 }
 
 __global__ __launch_bounds__(kThreads) void ternary_gemv_kernel(TernArgs a, int64_t rows, int64_t W) {
-    extern __shared__ uint32_t xl[];
+    extern __shared__ __align__(16) uint32_t xl[];
     ternary_body(a, xl, rows, W);
+}
+
+__device__ __forceinline__ TernArgs problem_args(const gd_ternary_problem &pr) {
+    return TernArgs{pr.w_pos, pr.w_neg, pr.x_planes, pr.y, pr.dot_out, pr.w_scale, pr.x_scale, pr.x_scale_dev};
 }
 
 __global__ __launch_bounds__(kThreads) void ternary_gemv_grouped_kernel(const gd_ternary_problem *probs,
                                                                         int64_t rows, int64_t W) {
-    extern __shared__ uint32_t xl[];
-    const gd_ternary_problem pr = probs[blockIdx.y];
-    TernArgs a{pr.w_pos, pr.w_neg, pr.x_planes, pr.y, pr.dot_out, pr.w_scale,
-               pr.x_scale_dev ? *pr.x_scale_dev : pr.x_scale};
-    ternary_body(a, xl, rows, W);
+    extern __shared__ __align__(16) uint32_t xl[];
+    ternary_body(problem_args(probs[blockIdx.y]), xl, rows, W);
 }
 
 // ----------------------------------------------------- held-row GEMV
@@ -154,9 +157,16 @@ __global__ __launch_bounds__(kThreads) void ternary_gemv_grouped_kernel(const gd
 constexpr int kHeldThreads = 512;
 constexpr int kHeldRows = kHeldThreads / kLanesPerRow;   // 64
 constexpr int kHeldMaxIt = 8;
+constexpr size_t kHeldStage = kHeldThreads * 16;   // LDS: one 16-byte plane piece per thread (8W*4 <= this)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef const u32x4 __attribute__((address_space(1))) *g_u4;
+
+// The planes (8W words = 2W sixteen-byte pieces, one per thread) are
+// loaded first: loads complete in the order they are issued, so the LDS
+// stage waits only for the plane load and runs while the weights are still
+// in flight.
+typedef const float __attribute__((address_space(1))) *g_f32;
 
 template <int NIT>
 __device__ __forceinline__ void ternary_held_body(const TernArgs &a, uint32_t *xl, int64_t rows, int64_t W) {
@@ -165,16 +175,23 @@ __device__ __forceinline__ void ternary_held_body(const TernArgs &a, uint32_t *x
     const int64_t r = static_cast<int64_t>(blockIdx.x) * kHeldRows + rsub;
     const int64_t rc = r < rows ? r : rows - 1;                 // clamped: loads valid, never stored
     const g_u4 Pr = (g_u4)(a.P + rc * W), Nr = (g_u4)(a.N + rc * W);
+    const int64_t np = 2 * W;                                   // plane pieces, <= kHeldThreads
+    const u32x4 xw = ((g_u4)a.X)[threadIdx.x < np ? threadIdx.x : np - 1];
     u32x4 pv[NIT], nv[NIT];
 #pragma unroll
-    for (int it = 0; it < NIT; it++) {                          // all loads first
+    for (int it = 0; it < NIT; it++) {                          // all weight loads next
         int64_t w4 = lane + kLanesPerRow * it;                  // 16-byte piece index in the row
         w4 = w4 < W / 4 ? w4 : W / 4 - 1;
         pv[it] = Pr[w4];
         nv[it] = Nr[w4];
     }
-    // stage the planes into LDS while the weight loads are in flight
-    for (int64_t i = threadIdx.x; i < 8 * W; i += kHeldThreads) xl[i] = a.X[i];
+    // the device scale, if any, is loaded last (it lands with the weights);
+    // the address is always valid and the value used only when set
+    const float xs = *(g_f32)(a.xs_dev ? a.xs_dev : reinterpret_cast<const float *>(a.X));
+    // every thread stores its piece: those past the 2W planes land in the
+    // stage's padding (kHeldStage bytes), so the load stays ahead of the weights'
+    *reinterpret_cast<u32x4 *>(xl + 4 * threadIdx.x) = xw;
+    const float x_scale = a.xs_dev ? xs : a.x_scale;
     __syncthreads();
     uint32_t cnt[8] = {0, 0, 0, 0, 0, 0, 0, 0}, cn = 0;
 #pragma unroll
@@ -201,7 +218,7 @@ __device__ __forceinline__ void ternary_held_body(const TernArgs &a, uint32_t *x
     part += __shfl_xor(part, 2, kLanesPerRow);
     part += __shfl_xor(part, 4, kLanesPerRow);
     if (lane == 0 && r < rows) {
-        const float s = a.w_scale * a.x_scale;
+        const float s = a.w_scale * x_scale;
         a.y[r] = static_cast<float>(part) * s;
         if (a.dot) a.dot[r] = part;
     }
@@ -209,45 +226,43 @@ __device__ __forceinline__ void ternary_held_body(const TernArgs &a, uint32_t *x
 
 template <int NIT>
 __global__ __launch_bounds__(kHeldThreads) void ternary_held_kernel(TernArgs a, int64_t rows, int64_t W) {
-    extern __shared__ uint32_t xl[];
+    extern __shared__ __align__(16) uint32_t xl[];
     ternary_held_body<NIT>(a, xl, rows, W);
 }
 
 template <int NIT>
 __global__ __launch_bounds__(kHeldThreads) void ternary_held_grouped_kernel(const gd_ternary_problem *probs,
                                                                             int64_t rows, int64_t W) {
-    extern __shared__ uint32_t xl[];
-    const gd_ternary_problem pr = probs[blockIdx.y];
-    TernArgs a{pr.w_pos, pr.w_neg, pr.x_planes, pr.y, pr.dot_out, pr.w_scale,
-               pr.x_scale_dev ? *pr.x_scale_dev : pr.x_scale};
-    ternary_held_body<NIT>(a, xl, rows, W);
+    extern __shared__ __align__(16) uint32_t xl[];
+    ternary_held_body<NIT>(problem_args(probs[blockIdx.y]), xl, rows, W);
 }
 
 // Launch the held-row kernel for W = K/32 (W % 4 == 0, W <= 256); false if
-// the shape does not qualify. `grouped` selects the problem-array form.
+// the shape does not qualify. `probs` null: the single-problem form with `a`;
+// else the problem-array form.
 template <int NIT>
-void launch_held_n(bool grouped, const TernArgs &a, const gd_ternary_problem *probs, int64_t count, int64_t rows,
-                   int64_t W, hipStream_t st) {
+void launch_held_n(const TernArgs &a, const gd_ternary_problem *probs, int64_t count, int64_t rows, int64_t W,
+                   hipStream_t st) {
     const dim3 grid(static_cast<uint32_t>((rows + kHeldRows - 1) / kHeldRows), static_cast<uint32_t>(count));
-    const size_t lds = static_cast<size_t>(8 * W * 4);
-    if (grouped)
-        hipLaunchKernelGGL(ternary_held_grouped_kernel<NIT>, grid, dim3(kHeldThreads), lds, st, probs, rows, W);
+    if (probs)
+        hipLaunchKernelGGL(ternary_held_grouped_kernel<NIT>, grid, dim3(kHeldThreads), kHeldStage, st, probs, rows,
+                           W);
     else
-        hipLaunchKernelGGL(ternary_held_kernel<NIT>, grid, dim3(kHeldThreads), lds, st, a, rows, W);
+        hipLaunchKernelGGL(ternary_held_kernel<NIT>, grid, dim3(kHeldThreads), kHeldStage, st, a, rows, W);
 }
 
-bool launch_held(bool grouped, const TernArgs &a, const gd_ternary_problem *probs, int64_t count, int64_t rows,
-                 int64_t W, hipStream_t st) {
+bool launch_held(const TernArgs &a, const gd_ternary_problem *probs, int64_t count, int64_t rows, int64_t W,
+                 hipStream_t st) {
     if (W % 4 != 0 || W > 32 * kHeldMaxIt) return false;
     switch ((W + 31) / 32) {
-        case 1: launch_held_n<1>(grouped, a, probs, count, rows, W, st); return true;
-        case 2: launch_held_n<2>(grouped, a, probs, count, rows, W, st); return true;
-        case 3: launch_held_n<3>(grouped, a, probs, count, rows, W, st); return true;
-        case 4: launch_held_n<4>(grouped, a, probs, count, rows, W, st); return true;
-        case 5: launch_held_n<5>(grouped, a, probs, count, rows, W, st); return true;
-        case 6: launch_held_n<6>(grouped, a, probs, count, rows, W, st); return true;
-        case 7: launch_held_n<7>(grouped, a, probs, count, rows, W, st); return true;
-        case 8: launch_held_n<8>(grouped, a, probs, count, rows, W, st); return true;
+        case 1: launch_held_n<1>(a, probs, count, rows, W, st); return true;
+        case 2: launch_held_n<2>(a, probs, count, rows, W, st); return true;
+        case 3: launch_held_n<3>(a, probs, count, rows, W, st); return true;
+        case 4: launch_held_n<4>(a, probs, count, rows, W, st); return true;
+        case 5: launch_held_n<5>(a, probs, count, rows, W, st); return true;
+        case 6: launch_held_n<6>(a, probs, count, rows, W, st); return true;
+        case 7: launch_held_n<7>(a, probs, count, rows, W, st); return true;
+        case 8: launch_held_n<8>(a, probs, count, rows, W, st); return true;
         default: return false;
     }
 }
@@ -293,8 +308,8 @@ extern "C" int ternary_gemv(const uint32_t *w_pos, const uint32_t *w_neg, float 
     const int64_t W = K / 32;
     const size_t lds = lds_bytes(K);
     GD_REQUIRE(lds <= 64 * 1024, GD_ERANGE, "ternary_gemv: K too large for the LDS plane stage");
-    TernArgs a{w_pos, w_neg, x_planes, y, dot_out, w_scale, x_scale};
-    if (launch_held(false, a, nullptr, 1, rows, W, as_stream(stream))) return check_launch("ternary_gemv");
+    TernArgs a{w_pos, w_neg, x_planes, y, dot_out, w_scale, x_scale, nullptr};
+    if (launch_held(a, nullptr, 1, rows, W, as_stream(stream))) return check_launch("ternary_gemv");
     const int64_t gx = (rows + kRowsPerWG - 1) / kRowsPerWG;
     hipLaunchKernelGGL(ternary_gemv_kernel, dim3(static_cast<uint32_t>(gx)), dim3(kThreads), lds,
                        as_stream(stream), a, rows, W);
@@ -312,7 +327,7 @@ extern "C" int ternary_gemv_grouped(const gd_ternary_problem *problems, int64_t 
     const int64_t W = K / 32;
     const size_t lds = lds_bytes(K);
     GD_REQUIRE(lds <= 64 * 1024, GD_ERANGE, "ternary_gemv_grouped: K too large for the LDS plane stage");
-    if (launch_held(true, TernArgs{}, problems, count, rows, W, as_stream(stream)))
+    if (launch_held(TernArgs{}, problems, count, rows, W, as_stream(stream)))
         return check_launch("ternary_gemv_grouped");
     const int64_t gx = (rows + kRowsPerWG - 1) / kRowsPerWG;
     hipLaunchKernelGGL(ternary_gemv_grouped_kernel, dim3(static_cast<uint32_t>(gx), static_cast<uint32_t>(count)),

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol(gd):
     lib = ctypes.CDLL(gd.LIB_PATH)
     missing = [n for n in declared_functions() if not hasattr(lib, n)]
     assert not missing, missing
-    assert lib.gemm_decode_abi_version() == 3
+    assert lib.gemm_decode_abi_version() == gd.ABI_VERSION == 3
 
 
 def test_status_strings(gd):
@@ -128,6 +128,11 @@ def test_validation_without_gpu(gd):
     assert L.ternary_gemv(FAKE, None, 1.0, FAKE, 1.0, FAKE, None, 4, 128, None) == E["inval"]
     assert L.ternary_gemv(FAKE, FAKE, 1.0, FAKE, 1.0, FAKE, None, 4, 1 << 20, None) == E["range"]
     assert L.ternary_gemv_grouped(FAKE, 0, 4, 128, None) == E["inval"]
+    assert L.ternary_gemv_grouped(None, 1, 4, 128, None) == E["inval"]
+    assert L.ternary_gemv_grouped(FAKE, 65536, 4, 128, None) == E["range"]
+    assert L.ternary_gemv_grouped(FAKE, 1, 4, 100, None) == E["shape"]
+    assert L.ternary_gemv_grouped(FAKE + 4, 1, 4, 128, None) == E["align"]
+    assert L.ternary_gemv_grouped(FAKE, 1, 4, 1 << 17, None) == E["range"]
     # activation quantization
     assert L.q8_0_quantize(None, FAKE, 1, 128, None) == E["inval"]
     assert L.q8_0_quantize(FAKE, FAKE, 0, 128, None) == E["inval"]
