@@ -43,8 +43,7 @@ METRIC = "Q1_0·q8_0 GEMV effective HBM GB/s (% of peak) + equiv tok/s, batch 1"
 # the kernel source they were measured on: reported only while its hash
 # matches, null after any change to it.
 _TRAFFIC = {
-    "q1": ("q1.hip", "e5f0ac1bd2ae5af4",
-           {"4096x4096": (37685.7, 512.0), "14336x4096": (129892.4, 1792.0)}),
+    "q1": ("q1.hip", "e5f0ac1bd2ae5af4", {"step": (37685.7 + 129892.4, 512.0 + 1792.0)}),
     "ternary": ("ternary.hip", "16436179a92f165c",
                 {"2560x2560": (97292.6, 1200.0), "6912x2560": (130263.3, 1620.0), "2560x6912": (65775.7, 300.0)}),
     "blockq8": ("blockq8.hip", "a0d67a1723d13bce", {"m1": (25974.9, 196.4), "m16": (26263.4, 3072.0)}),
@@ -148,19 +147,23 @@ def bench_q1(args, gd, torch):
         gd.q1_repack(torch.from_numpy(W.reshape(-1)).cuda(), s.rows, s.K, b, sc)
         base.append((b, sc))
     ys = [[torch.empty(s.rows, dtype=torch.float32, device="cuda") for _ in range(n_vec)] for s in shapes]
-    # slots[r]: the step's problems over the r-th set of plane copies, one
-    # grouped launch per weight shape (32 problems each)
+    # slots[r]: the step's 64 problems over the r-th set of plane copies, in
+    # one grouped launch: each problem carries its own row count, the launch
+    # the largest; the shorter problems come first, so the longer ones' work
+    # fills the launch's tail
+    max_rows = max(s.rows for s in shapes)
+    n_prob = len(shapes) * n_vec
     slots = []
     for r in range(ring):
         copies = [[(base[si][0].clone(), base[si][1].clone()) for _ in range(n_vec)] for si in range(len(shapes))]
-        per_shape = [gd.make_q1_problems([(copies[si][c][0], copies[si][c][1], a_dev[c], ys[si][c])
-                                          for c in range(n_vec)]) for si in range(len(shapes))]
-        slots.append({"shape": per_shape, "copies": copies})
+        order = sorted(range(len(shapes)), key=lambda si: shapes[si].rows)
+        probs = gd.make_q1_problems([(copies[si][c][0], copies[si][c][1], a_dev[c], ys[si][c], shapes[si].rows)
+                                     for si in order for c in range(n_vec)])
+        slots.append({"step": probs, "copies": copies})
     torch.cuda.synchronize()
 
     def step(r):
-        for si, s in enumerate(shapes):
-            gd.q1_q8_gemv_grouped(slots[r]["shape"][si], n_vec, s.rows, s.K)
+        gd.q1_q8_gemv_grouped(slots[r]["step"], n_prob, max_rows, K)
 
     # parity spot check (untimed): every output of the first ring slot
     step(0)
@@ -218,7 +221,7 @@ def bench_q1(args, gd, torch):
     wall = time.perf_counter() - wall0
     total_s = t0.elapsed_time(t1) / 1e3
 
-    # Roofline: mean duration of each shape's grouped kernel, from HIP events
+    # Roofline: mean duration of the step's grouped kernel, from HIP events
     # on the launch stream around `reps` back-to-back launches (ring slots in
     # turn), after the same number untimed.
     reps = 8 * ring
@@ -233,13 +236,9 @@ def bench_q1(args, gd, torch):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / 1e3 / reps
 
-    per_launch = [timed(lambda si=si, s=s: [gd.q1_q8_gemv_grouped(slots[j % ring]["shape"][si], n_vec, s.rows, s.K)
-                                            for j in range(reps)])
-                  for si, s in enumerate(shapes)]
-    launch_bytes = [n_vec * q1_gemv_bytes(s.rows, s.K) for s in shapes]
+    kern_s = timed(lambda: [step(j % ring) for j in range(reps)])
     q1_traffic = measured_traffic("q1")
-    kern_s = sum(per_launch)
-    achieved = sum(launch_bytes) / kern_s / 1e9
+    achieved = step_bytes / kern_s / 1e9
 
     gbps = step_bytes * args.steps / total_s / 1e9
     ms_per_step = total_s / args.steps * 1e3
@@ -300,8 +299,8 @@ def bench_q1(args, gd, torch):
         "data": "synthetic",
         "config": {
             "workload": "Q1_0.q8_0 GEMV batch 1: 32 activation vectors x {4096x4096, 14336x4096}, "
-                        "K=4096, 64 independent GEMVs per step in 2 grouped launches, distinct weight "
-                        "copies (ring > 1 GiB)",
+                        "K=4096, 64 independent GEMVs per step in one grouped launch (per-problem rows), "
+                        "distinct weight copies (ring > 1 GiB)",
             "rows": [s.rows for s in shapes], "K": K, "activation_vectors": n_vec,
             "step_bytes": step_bytes, "ring_sets": ring,
             "timed_as": (f"HIP graph replays ({ring} steps per graph)" if args.graph
@@ -315,10 +314,10 @@ def bench_q1(args, gd, torch):
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": None if q1_traffic is None else sum(q1_traffic.values()),
             "traffic_per_launch": q1_traffic,
-            "kernel": "q1_gemv_grouped_kernel",
-            "us_per_launch": {f"{s.rows}x{s.K}": round(per_launch[si] * 1e6, 2) for si, s in enumerate(shapes)},
-            "bytes_per_launch": {f"{s.rows}x{s.K}": launch_bytes[si] for si, s in enumerate(shapes)},
-            "timing": f"HIP events around {reps} back-to-back launches of one shape",
+            "kernel": "q1_gemv_grouped_kernel (one launch per step, 64 problems)",
+            "us_per_launch": round(kern_s * 1e6, 2),
+            "bytes_per_launch": step_bytes,
+            "timing": f"HIP events around {reps} back-to-back launches",
         },
         "parity_mismatches": mism,
         "serial_one_launch_per_gemv": serial,
@@ -347,10 +346,22 @@ def cpu_baseline_q1(Ws, A, shapes, budget_s: float):
         t_used += time.perf_counter() - t
         done_bytes += q1_gemv_bytes(s.rows, s.K)
         n_gemv += 1
+    # the same GEMVs on one thread, for a quarter of the budget
+    one_bytes, one_used, n_one = 0, 0.0, 0
+    while one_used < budget_s / 4:
+        c, si = order[n_one % len(order)]
+        s = shapes[si]
+        t = time.perf_counter()
+        oracle.q1_q8_gemv_aos(Ws[si], A[c], s.rows, s.K, 1, nthreads=1)
+        one_used += time.perf_counter() - t
+        one_bytes += q1_gemv_bytes(s.rows, s.K)
+        n_one += 1
     return {"value": round(done_bytes / t_used / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{n_gemv} batch-1 GEMVs of the step (vectors x {{4096x4096, 14336x4096}}, in order, "
-                      f"cycling), {t_used:.2f} s of oracle time, OpenMP over rows, {cpu_model()}"}
+                      f"cycling), {t_used:.2f} s of oracle time, OpenMP over rows, {cpu_model()}",
+            "single_thread": {"value": round(one_bytes / one_used / 1e9, 4), "unit": "GB/s", "cores": 1,
+                              "sample": f"{n_one} of the same GEMVs, {one_used:.2f} s"}}
 
 
 # ------------------------------------------- Q1 small-M (several columns)

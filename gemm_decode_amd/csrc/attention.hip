@@ -24,6 +24,7 @@
 // weights computed once per split into LDS.
 // A split with no keys writes max -inf, denominator 0 and output 0, and
 // contributes nothing.
+#include "gd_device.h"
 #include "gd_internal.h"
 
 namespace {
@@ -61,8 +62,8 @@ __device__ __forceinline__ void load_tile(const float *kb, const float *vb, int6
         const int row = e / (kD / 4), c4 = e % (kD / 4);
         const int64_t t = t0 + row;
         if (t < t_end) {
-            rk[i] = ((g_f4)(kb + t * kD))[c4];
-            rv[i] = ((g_f4)(vb + t * kD))[c4];
+            rk[i] = gd::ld_stream(&((g_f4)(kb + t * kD))[c4]);   // each K/V row is read once
+            rv[i] = gd::ld_stream(&((g_f4)(vb + t * kD))[c4]);
         } else {
             rk[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
             rv[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};

@@ -12,6 +12,7 @@
 // This regroups the page's f32 order (16-element pieces instead of
 // 32-element blocks, a different final sum order); the results agree with
 // that order within 1e-5 of ||y||_inf.
+#include "gd_device.h"
 #include "gd_internal.h"
 
 namespace {
@@ -136,8 +137,8 @@ __global__ __launch_bounds__(kGemvThreads) void blockq8_gemv_kernel(const float 
         for (int t = 0; t < kCPL; t++) {
             int c = lane + kLPR * t;
             c = c < chunks ? c : chunks - 1;                     // masked by x = 0 below
-            b.q[t] = quants[r * chunks + c];
-            b.s[t] = scales[r * bpr + c / 2];
+            b.q[t] = gd::ld_stream(&quants[r * chunks + c]);
+            b.s[t] = gd::ld_stream(&scales[r * bpr + c / 2]);
         }
     };
     // x once per workgroup into LDS (read before the quant loads, which the
@@ -299,7 +300,7 @@ __global__ __launch_bounds__(kMfmaThreads) void blockq8_mfma_kernel(const float 
     const int64_t row = n0 + j < n ? n0 + j : n - 1;
     auto wload = [&](int b) {
         const int bc = b < nb ? b : nb - 1;
-        return quants[row * (k / 8) + 4 * bc + g];
+        return quants[row * (k / 8) + 4 * bc + g];   // plain: the line's other 24 bytes come later
     };
     u32x2 wq[NB];
 #pragma unroll

@@ -30,4 +30,13 @@ __device__ __forceinline__ uint32_t grp(uint32_t w) {
     return r;
 }
 
+// A load of data read exactly once (weights), with the non-temporal hint:
+// streamed past the caches that way, such data arrives measurably faster
+// than through plain loads. Reused data (activations, tables) takes plain
+// loads.
+template <typename T>
+__device__ __forceinline__ T ld_stream(const T __attribute__((address_space(1))) *p) {
+    return __builtin_nontemporal_load(p);
+}
+
 }  // namespace gd

@@ -3,8 +3,11 @@
 // then a read pass streams 16-byte words through an XOR into a sink).
 //
 // The read kernel gives each wave a contiguous span of the buffer and walks
-// it with 16-byte loads, four in flight per lane, so the measured figure is
-// the chip's streaming-read ceiling rather than a latency bound.
+// it with 16-byte non-temporal loads, eight in flight per lane: of the
+// patterns tried on this chip (grid-stride or per-wave spans, four or eight
+// loads in flight, with or without the hint, 1024 to 8192 workgroups) it
+// read fastest, so the figure is the chip's streaming-read ceiling rather
+// than a latency bound.
 #include "gd_internal.h"
 
 namespace {
@@ -18,29 +21,34 @@ __global__ void fill_kernel(uint4 *__restrict__ d, int64_t n, uint32_t seed) {
 }
 
 constexpr int kReadThreads = 256;
+constexpr int kReadUnroll = 8;                    // loads in flight per lane
+constexpr int kReadStep = 64 * kReadUnroll;       // 16-byte words per wave step
 
-__global__ __launch_bounds__(kReadThreads) void stream_read_kernel(const uint4 *__restrict__ d, int64_t n,
-                                                                   int32_t passes, uint32_t *__restrict__ sink,
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef const u32x4 __attribute__((address_space(1))) *gptr_u4;
+
+// Wave w reads words [w*span, min((w+1)*span, n)); span is a multiple of
+// kReadStep with waves*span >= n, so whole steps need no bounds check.
+__global__ __launch_bounds__(kReadThreads) void stream_read_kernel(const uint4 *__restrict__ dp, int64_t n,
+                                                                   int64_t span, int32_t passes,
+                                                                   uint32_t *__restrict__ sink,
                                                                    int64_t sink_words) {
+    const gptr_u4 d = (gptr_u4)dp;
     const int64_t tid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    const int64_t nthreads = static_cast<int64_t>(gridDim.x) * blockDim.x;
-    uint4 acc = make_uint4(0, 0, 0, 0);
+    const int64_t lane = threadIdx.x % 64;
+    const int64_t b = (tid / 64) * span;
+    const int64_t e = b + span < n ? b + span : n;
+    u32x4 acc = {0u, 0u, 0u, 0u};
     for (int32_t p = 0; p < passes; p++) {
-        int64_t i = tid;
-        for (; i + 3 * nthreads < n; i += 4 * nthreads) {
-            const uint4 a = d[i], b = d[i + nthreads], c = d[i + 2 * nthreads], e = d[i + 3 * nthreads];
-            acc.x ^= a.x ^ b.x ^ c.x ^ e.x;
-            acc.y ^= a.y ^ b.y ^ c.y ^ e.y;
-            acc.z ^= a.z ^ b.z ^ c.z ^ e.z;
-            acc.w ^= a.w ^ b.w ^ c.w ^ e.w;
+        int64_t j = b;
+        for (; j + kReadStep <= e; j += kReadStep) {
+            u32x4 v[kReadUnroll];
+#pragma unroll
+            for (int u = 0; u < kReadUnroll; u++) v[u] = __builtin_nontemporal_load(&d[j + 64 * u + lane]);
+#pragma unroll
+            for (int u = 0; u < kReadUnroll; u++) acc ^= v[u];
         }
-        for (; i < n; i += nthreads) {
-            const uint4 a = d[i];
-            acc.x ^= a.x;
-            acc.y ^= a.y;
-            acc.z ^= a.z;
-            acc.w ^= a.w;
-        }
+        for (int64_t i = j + lane; i < e; i += 64) acc ^= d[i];
     }
     sink[tid % sink_words] = acc.x ^ acc.y ^ acc.z ^ acc.w;
 }
@@ -69,10 +77,11 @@ extern "C" int gemm_decode_stream_read(const void *buf, size_t bytes, int32_t pa
     GD_REQUIRE(bytes % 16 == 0, GD_ESHAPE, "gemm_decode_stream_read: bytes must be a multiple of 16");
     GD_REQUIRE(aligned(buf, 16) && aligned(sink, 4), GD_EALIGN, "gemm_decode_stream_read: misaligned pointer");
     const int64_t n = static_cast<int64_t>(bytes / 16);
-    // 8 workgroups of 256 per CU on 256 CUs keeps every SIMD busy.
-    int64_t blocks = 2048;
-    if (blocks * kReadThreads > n) blocks = (n + kReadThreads - 1) / kReadThreads;
+    // four workgroups of 256 per CU on 256 CUs
+    const int64_t blocks = 1024, waves = blocks * (kReadThreads / 64);
+    int64_t span = (n + waves - 1) / waves;
+    span = (span + kReadStep - 1) / kReadStep * kReadStep;
     hipLaunchKernelGGL(stream_read_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kReadThreads), 0,
-                       as_stream(stream), static_cast<const uint4 *>(buf), n, passes, sink, sink_words);
+                       as_stream(stream), static_cast<const uint4 *>(buf), n, span, passes, sink, sink_words);
     return check_launch("gemm_decode_stream_read");
 }

@@ -52,6 +52,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef const u32x2 __attribute__((address_space(1))) *gptr_u2;
 typedef const u32x4 __attribute__((address_space(1))) *gptr_u4;
 
+using gd::ld_stream;
+
 
 // Exact f16 -> f32 (the conversion is exact for every f16 value, subnormals
 // included, under the default denormal mode).
@@ -231,8 +233,8 @@ struct RowPtrs {
 
 __device__ __forceinline__ void load_group(const RowPtrs &rp, int64_t g, u32x2 (&wb)[8], u32x4 &s8) {
 #pragma unroll
-    for (int u = 0; u < 8; u++) wb[u] = rp.bits[(8 * g + u) * 128];
-    s8 = rp.sc[g * 64];
+    for (int u = 0; u < 8; u++) wb[u] = ld_stream(&rp.bits[(8 * g + u) * 128]);
+    s8 = ld_stream(&rp.sc[g * 64]);
 }
 
 // Eight blocks U0..U0+7 of the chunk: table reads of block u+1 are issued
@@ -245,7 +247,7 @@ __device__ __forceinline__ void group8(const char *tab, u32x2 (&wb)[8], u32x4 &s
                                        const RowPtrs &rp, int64_t gn) {
     float va[16], vb[16];
     auto refill = [&](int u) {
-        if constexpr (REFILL) wb[u] = rp.bits[(8 * gn + u) * 128];
+        if constexpr (REFILL) wb[u] = ld_stream(&rp.bits[(8 * gn + u) * 128]);
     };
     half_reads<H, U0 + 0>(tab, wb[0], va);
     refill(0);
@@ -271,7 +273,7 @@ __device__ __forceinline__ void group8(const char *tab, u32x2 (&wb)[8], u32x4 &s
     refill(7);
     half_math(va, d0_half<6>(s8), acc);
     half_math(vb, d0_half<7>(s8), acc);
-    if constexpr (REFILL) s8 = rp.sc[gn * 64];
+    if constexpr (REFILL) s8 = ld_stream(&rp.sc[gn * 64]);
 }
 
 
@@ -346,10 +348,10 @@ __device__ __forceinline__ void half_row(float *tab, const Q1Args &p, const RowP
             table_store<NT>(tab, raw, static_cast<int>(nb - it0));
             __syncthreads();
         }
-        const u32x4 s8 = rp.sc[(it0 >> 3) * 64];
+        const u32x4 s8 = ld_stream(&rp.sc[(it0 >> 3) * 64]);
         const char *tabc = reinterpret_cast<const char *>(tab);
         for (int64_t i = it0; i < nb; i++) {
-            const u32x2 wbv = rp.bits[i * 128];
+            const u32x2 wbv = ld_stream(&rp.bits[i * 128]);
             tail_block<H>(tabc + (i - c0) * 2048, wbv, d0_of(s8, static_cast<int>(i & 7)), acc);
         }
     }
@@ -478,7 +480,7 @@ __device__ __forceinline__ void mc_load(const RowPtrs &rp, int64_t j, int64_t nb
     for (int u = 0; u < CB; u++) {
         int64_t i = j * CB + u;
         i = i < nb ? i : nb - 1;
-        b.w[u] = rp.bits[i * 128];
+        b.w[u] = rp.bits[i * 128];   // plain: other column groups re-read these weights
     }
     const int64_t ng = (nb + 7) / 8;
 #pragma unroll

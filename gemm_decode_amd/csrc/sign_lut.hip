@@ -123,7 +123,7 @@ __global__ __launch_bounds__(kGvThreads) void sign_gemv_kernel(const float *__re
         for (int p = 0; p < kGvPairsPerWave; p++) {
             int64_t pg = c0 + p0 + p;
             pg = pg < G2 ? pg : G2 - 1;   // clamped: loaded, never used
-            v[p] = wv[pg * N + nl];
+            v[p] = gd::ld_stream(&wv[pg * N + nl]);   // read once (the LUT4 kernel's re-reads stay plain)
         }
         if (c0 > 0) __syncthreads();   // the previous chunk's reads are done
         for (int q = threadIdx.x; q < cp * 16; q += kGvThreads) build_group(tab, q, xr, c0 * 64 + 4 * q, K);

@@ -19,6 +19,7 @@
 // copied once per workgroup into LDS, where the eight lanes of a row read
 // eight consecutive 16-byte pieces and the eight rows of a wave read the same
 // addresses (broadcast).
+#include "gd_device.h"
 #include "gd_internal.h"
 
 namespace {
@@ -157,6 +158,10 @@ __global__ __launch_bounds__(kThreads) void ternary_gemv_grouped_kernel(const gd
 constexpr int kHeldThreads = 512;
 constexpr int kHeldRows = kHeldThreads / kLanesPerRow;   // 64
 constexpr int kHeldMaxIt = 8;
+// The weight planes take streaming (non-temporal) loads up to this many
+// pieces per lane: measured faster at K = 2560 (3 pieces), slower at
+// K = 6912 (7 pieces).
+constexpr int kHeldStreamMaxIt = 4;
 constexpr size_t kHeldStage = kHeldThreads * 16;   // LDS: one 16-byte plane piece per thread (8W*4 <= this)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -182,8 +187,13 @@ __device__ __forceinline__ void ternary_held_body(const TernArgs &a, uint32_t *x
     for (int it = 0; it < NIT; it++) {                          // all weight loads next
         int64_t w4 = lane + kLanesPerRow * it;                  // 16-byte piece index in the row
         w4 = w4 < W / 4 ? w4 : W / 4 - 1;
-        pv[it] = Pr[w4];
-        nv[it] = Nr[w4];
+        if constexpr (NIT <= kHeldStreamMaxIt) {
+            pv[it] = gd::ld_stream(&Pr[w4]);
+            nv[it] = gd::ld_stream(&Nr[w4]);
+        } else {
+            pv[it] = Pr[w4];
+            nv[it] = Nr[w4];
+        }
     }
     // the device scale, if any, is loaded last (it lands with the weights);
     // the address is always valid and the value used only when set
