@@ -43,21 +43,21 @@ METRIC = "Q1_0·q8_0 GEMV effective HBM GB/s (% of peak) + equiv tok/s, batch 1"
 # the kernel source they were measured on: reported only while its hash
 # matches, null after any change to it.
 _TRAFFIC = {
-    "q1": ("q1.hip", "e5f0ac1bd2ae5af4", {"step": (37685.7 + 129892.4, 512.0 + 1792.0)}),
-    "ternary": ("ternary.hip", "16436179a92f165c",
-                {"2560x2560": (97292.6, 1200.0), "6912x2560": (130263.3, 1620.0), "2560x6912": (65775.7, 300.0)}),
-    "blockq8": ("blockq8.hip", "a0d67a1723d13bce", {"m1": (25974.9, 196.4), "m16": (26263.4, 3072.0)}),
+    "q1": ("q1.hip", "5f2b0e44b61658d8", {"step": (167385.4, 2304.0)}),
+    "ternary": ("ternary.hip", "8f60006b03cd5750",
+                {"2560x2560": (102109.9, 1200.0), "6912x2560": (137509.5, 1620.1), "2560x6912": (65808.1, 300.0)}),
+    "blockq8": ("blockq8.hip", "d8731b70978dd345", {"m1": (27716.0, 192.2), "m16": (27465.0, 3072.0)}),
     "sign": ("sign_gemm.hip", "1122664298d09035",
              {"split": (4128.8, 8208.0), "wpack": (2074.7, 4096.0), "gemm": (21355.4, 9728.0)}),
-    "sign_lut": ("sign_lut.hip", "65e2776a84a05262",
-                 {"4096x4096": (2170.1, 16.0), "14336x4096": (7290.0, 56.0), "lut4": (35128.6, 8192.0)}),
-    "quant": ("quantize.hip", "a7b47e9235f09149",
-              {"q8_0_decode": (266.9, 136.0), "q8_0_batch_256MiB": (131083.7, 69633.8),
-               "int8_planes_decode_step": (538.4 + 559.6, 227.8 + 203.4),
-               "int8_planes_batch_256MiB": (131167.0, 66048.0)}),
+    "sign_lut": ("sign_lut.hip", "c9273fa6aeb445b1",
+                 {"4096x4096": (2170.0, 16.0), "14336x4096": (7290.0, 56.0), "lut4": (35127.5, 8192.0)}),
+    "quant": ("quantize.hip", "aa440e939b0b9a5a",
+              {"q8_0_decode": (266.5, 136.0), "q8_0_batch_256MiB": (131082.5, 69632.0),
+               "int8_planes_decode_step": (522.6 + 536.5, 227.8 + 203.4),
+               "int8_planes_batch_256MiB": (131147.4, 66072.4)}),
     # per call: split kernel + merge kernel
-    "attention": ("attention.hip", "fb26b5a8fcf1f977",
-                  {"kv4096": (16464.3 + 597.0, 1040.0 + 16.0), "kv32768": (131153.7 + 597.0, 1040.0 + 16.0)}),
+    "attention": ("attention.hip", "3f3480fee0cca0a4",
+                  {"kv4096": (16477.0 + 597.0, 1040.0 + 16.0), "kv32768": (131165.0 + 597.0, 1040.0 + 16.0)}),
 }
 
 
