@@ -409,9 +409,13 @@ extern "C" int blockq8_matmul_nt(const float *x, const uint32_t *quants, const f
     hipStream_t st = as_stream(stream);
     const int mi = static_cast<int>(m);
     if (m == 1 && k <= 16 * kLPR * kCPL) {
-        // steps per wave (a multiple of 4) chosen for ~20 waves per CU on 256 CUs
+        // steps per wave (a multiple of 4) for about 2048 waves: eight per CU
+        // (two workgroups of four) on 256 CUs. Measured at k=960, n=49152:
+        // 12 steps per wave 10.9 us; 8 steps (12 waves per CU) 12.1 us, the
+        // per-wave prologue (x staging, the first three steps' loads) then
+        // weighing more; 16 steps (six waves per CU, uneven) 12.2 us.
         const int64_t pairs = (n + 1) / 2;                        // 2 rows per wave step
-        int64_t spw = (pairs + 5119) / 5120;
+        int64_t spw = (pairs + 2047) / 2048;
         spw = (spw + 3) / 4 * 4;
         const int64_t waves = (pairs + spw - 1) / spw;
         const int64_t blocks = (waves * 64 + kGemvThreads - 1) / kGemvThreads;
