@@ -364,6 +364,75 @@ def cpu_baseline_q1(Ws, A, shapes, budget_s: float):
                               "sample": f"{n_one} of the same GEMVs, {one_used:.2f} s"}}
 
 
+# ---------------------------------------- Q1 correctness-sized (256 x 1024)
+
+def bench_q1_small(args, gd, torch):
+    """Q1_0.q8_0 GEMV rows=256, K=1024, batch 1 (the correctness-sized
+    config; 38,976 algorithmic bytes per GEMV). (S): one launch per GEMV,
+    back to back from a HIP graph: the latency figure. (G): independent
+    problems in grouped launches, each reading its own copy of the planes,
+    the copies rotating over a ring > 1 GiB: the streaming figure."""
+    import oracle
+    cfg = wl.Q1_SMALL
+    rows, K = cfg.rows, cfg.K
+    W = wl.q1_weights_aos(rows, K, cfg.weight_seed)
+    A = wl.q8_acts_aos(K, cfg.act_seeds[0])
+    bb, sb = gd.q1_planes_bytes(rows, K)
+    b0, s0 = gd.q1_alloc_planes(rows, K)
+    gd.q1_repack(torch.from_numpy(W.reshape(-1)).cuda(), rows, K, b0, s0)
+    a = torch.from_numpy(np.ascontiguousarray(A.reshape(-1))).cuda()
+    gemv_bytes = q1_gemv_bytes(rows, K)
+    sets = 4
+    count = int(np.ceil(1.05 * (1 << 30) / (sets * (bb + sb))))      # problems per launch
+    bits = [b0.repeat(count) for _ in range(sets)]
+    scl = [s0.repeat(count) for _ in range(sets)]
+    ys = [torch.empty(count * rows, device="cuda") for _ in range(sets)]
+    probs = [gd.make_q1_problems([(bits[t][i * bb:(i + 1) * bb], scl[t][i * sb:(i + 1) * sb], a,
+                                   ys[t][i * rows:(i + 1) * rows]) for i in range(count)]) for t in range(sets)]
+    torch.cuda.synchronize()
+
+    def grouped(kk):
+        gd.q1_q8_gemv_grouped(probs[kk % sets], count, rows, K)
+    per_g, _ = _time_launches(torch, grouped, max(4, args.aux_steps // 4), sets)
+    # every output of two problems of each set, bit for bit
+    want = oracle.q1_q8_gemv_aos(W, A, rows, K).view(np.uint32)
+    mism = 0
+    for t in range(sets):
+        for i in (0, count - 1):
+            got = ys[t][i * rows:(i + 1) * rows].cpu().numpy().view(np.uint32)
+            mism += int((got != want).sum())
+    ys1 = torch.empty(rows, device="cuda")
+    stride = max(1, count // 64)
+
+    def single(kk):
+        t, i = kk % sets, (kk * stride) % count
+        gd.q1_q8_gemv(bits[t][i * bb:(i + 1) * bb], scl[t][i * sb:(i + 1) * sb], a, ys1, rows, K, 1)
+    per_s, _ = _time_launches(torch, single, 64, 4)
+    mism += int((ys1.cpu().numpy().view(np.uint32) != want).sum())
+    g_gbps = count * gemv_bytes / per_g / 1e9
+    threads = cpu_cores()
+    t_used, n_g = 0.0, 0
+    while t_used < args.aux_cpu_seconds:
+        t = time.perf_counter()
+        oracle.q1_q8_gemv_aos(W, A, rows, K, nthreads=threads)
+        t_used += time.perf_counter() - t
+        n_g += 1
+    return {
+        "workload": "Q1_0.q8_0 GEMV rows=256, K=1024, batch 1",
+        "metric": "effective HBM GB/s (grouped: independent problems, ring > 1 GiB)",
+        "value": round(g_gbps, 1), "unit": "GB/s", "problems_per_launch": count, "ring_copies": sets * count,
+        "us_per_launch": round(per_g * 1e6, 2),
+        "single_launch": {"us_per_gemv": round(per_s * 1e6, 3), "GB_per_s": round(gemv_bytes / per_s / 1e9, 1),
+                          "timing": "HIP graph of 64 back-to-back single-GEMV launches"},
+        "roofline": {"bound": "hbm", "achieved": round(g_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(g_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "q1_gemv_grouped_kernel", "bytes_per_launch": count * gemv_bytes},
+        "parity_mismatches": mism,
+        "cpu_baseline": {"value": round(n_g * gemv_bytes / t_used / 1e9, 4), "unit": "GB/s", "cores": threads,
+                         "kind": "oracle", "sample": f"{n_g} GEMVs of 256x1024, {t_used:.2f} s"},
+    }
+
+
 # ------------------------------------------- Q1 small-M (several columns)
 
 def bench_q1_mm(args, gd, torch):
@@ -902,7 +971,7 @@ def main():
     ap.add_argument("--min-warmup-s", type=float, default=0.2,
                     help="untimed warmup continues until this much sustained load has run")
     ap.add_argument("--workload", default="all",
-                    choices=["all", "q1", "q1mm", "sign", "blockq8", "ternary", "quant", "attention"],
+                    choices=["all", "q1", "q1small", "q1mm", "sign", "blockq8", "ternary", "quant", "attention"],
                     help="all (default): the Q1 metric line plus the other paths under 'workloads'")
     ap.add_argument("--aux-steps", type=int, default=20, help="timed launches for the other paths")
     ap.add_argument("--aux-cpu-seconds", type=float, default=4.0)
@@ -944,6 +1013,9 @@ def main():
         if args.workload in ("all", "blockq8"):
             log("[bench] block-Q8 matmul_nt")
             extra["blockq8"] = bench_blockq8(args, gd, torch)
+        if args.workload in ("all", "q1small"):
+            log("[bench] Q1 256x1024 GEMV")
+            extra["q1_256x1024"] = bench_q1_small(args, gd, torch)
         if args.workload in ("all", "q1mm"):
             log("[bench] Q1 small-M (several columns)")
             extra["q1_small_m"] = bench_q1_mm(args, gd, torch)
