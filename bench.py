@@ -46,7 +46,7 @@ _TRAFFIC = {
     "q1": ("q1.hip", "5f2b0e44b61658d8", {"step": (167385.4, 2304.0)}),
     "ternary": ("ternary.hip", "8f60006b03cd5750",
                 {"2560x2560": (102109.9, 1200.0), "6912x2560": (137509.5, 1620.1), "2560x6912": (65808.1, 300.0)}),
-    "blockq8": ("blockq8.hip", "d8731b70978dd345", {"m1": (27716.0, 192.2), "m16": (27465.0, 3072.0)}),
+    "blockq8": ("blockq8.hip", "123bb6b095593ab2", {"m1": (26533.5, 192.4), "m16": (27472.9, 3072.0)}),
     "sign": ("sign_gemm.hip", "1122664298d09035",
              {"split": (4128.8, 8208.0), "wpack": (2074.7, 4096.0), "gemm": (21355.4, 9728.0)}),
     "sign_lut": ("sign_lut.hip", "c9273fa6aeb445b1",
@@ -59,6 +59,23 @@ _TRAFFIC = {
     "attention": ("attention.hip", "3f3480fee0cca0a4",
                   {"kv4096": (16477.0 + 597.0, 1040.0 + 16.0), "kv32768": (131165.0 + 597.0, 1040.0 + 16.0)}),
 }
+
+
+# Hardware MFMA busy fraction (rocprofv3 SQ_VALU_MFMA_BUSY_CYCLES over the
+# dispatch's duration x 1024 SIMDs at 2.4 GHz), for the kernel source measured.
+_MFMA_BUSY = {
+    "sign_gemm_kernel": ("sign_gemm.hip", "1122664298d09035", 0.284),
+    "blockq8_mfma_kernel": ("blockq8.hip", "123bb6b095593ab2", 0.085),
+}
+
+
+def measured_mfma_busy(kernel: str):
+    """The counter-measured MFMA busy fraction of a kernel, or None if its
+    source has changed since."""
+    import hashlib
+    src, sha, frac = _MFMA_BUSY[kernel]
+    with open(os.path.join(ROOT, "gemm_decode_amd", "csrc", src), "rb") as f:
+        return frac if hashlib.sha256(f.read()).hexdigest()[:16] == sha else None
 
 
 def measured_traffic(path: str):
@@ -603,7 +620,8 @@ def bench_sign(args, gd, torch):
                      "traffic": None if sg_traffic is None else sum(sg_traffic.values()),
                      "traffic_per_kernel": sg_traffic,
                      "kernel": "q1_sign_gemm call (sign_split, sign_wpack, sign_gemm kernels)",
-                     "flops_per_launch": flops},
+                     "flops_per_launch": flops,
+                     "mfma_busy_hw": measured_mfma_busy("sign_gemm_kernel")},
         "parity_rel_err_sampled": rel,
         "cpu_baseline": {"value": round(cpu_gflops / 1e3, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
                          "sample": f"{rows_done} of 512 rows x all 4096 columns (f64 oracle), {t_used:.2f} s"},
@@ -704,7 +722,8 @@ def bench_blockq8(args, gd, torch):
                          "frac": round(gbps / HBM_PEAK_GBPS, 4),
                          "traffic": None if bq_traffic is None else bq_traffic[f"m{m}"],
                          "kernel": "blockq8_gemv_kernel" if m == 1 else "blockq8_mfma_kernel<32>",
-                         "bytes_per_launch": bytes_},
+                         "bytes_per_launch": bytes_,
+                         "mfma_busy_hw": None if m == 1 else measured_mfma_busy("blockq8_mfma_kernel")},
             "parity_rel_err_sampled": rel,
             "cpu_baseline": {"value": round(cpu_bytes / t_used / 1e9, 4), "unit": "GB/s", "cores": threads,
                              "kind": "oracle",
