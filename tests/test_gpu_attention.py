@@ -106,3 +106,20 @@ def test_split_counts_agree(gd):
     want = oracle.attention_decode(q, k, v, 0.1)
     for s in (1, 7, 64, 0):
         assert rel_err(run(gd, q, k, v, Hq, Hkv, L, L, 0.1, s), want) <= tol(q, k, 0.1, Hkv), s
+
+
+def test_workspace_reuse_across_shapes(gd):
+    """One workspace serves calls of different shapes and split counts in
+    turn, each meeting the bar (nothing in it carries over between calls)."""
+    cases = [(32, 8, 4096, 0), (16, 2, 777, 5), (8, 8, 130, 3), (16, 16, 1000, 0), (64, 8, 2049, 0),
+             (32, 8, 4096, 0)]
+    need = max(gd.attn_decode_workspace_bytes(Hq, Hkv, D, L, s) for Hq, Hkv, L, s in cases)
+    ws = torch.full((need,), 0xA5, dtype=torch.uint8, device="cuda")
+    for n, (Hq, Hkv, L, s) in enumerate(cases):
+        q, k, v = inputs(Hq, Hkv, L, L, seed=100 + n)
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+        out = torch.full((Hq * D,), float("nan"), device="cuda")
+        gd.attn_decode_splitk(dev(q), dev(k), dev(v), out, Hq, Hkv, D, L, L, 0.1, s, ws)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().reshape(Hq, D)
+        assert rel_err(got, oracle.attention_decode(q, k, v, 0.1)) <= tol(q, k, 0.1, Hkv), (Hq, Hkv, L, s)
