@@ -237,15 +237,17 @@ __device__ __forceinline__ void load_group(const RowPtrs &rp, int64_t g, u32x2 (
     s8 = ld_stream(&rp.sc[g * 64]);
 }
 
-// Eight blocks U0..U0+7 of the chunk: table reads of block u+1 are issued
-// before the arithmetic of block u consumes its own. With REFILL, block u's
-// register is reloaded with block u of group gn as soon as its table offsets
-// have been extracted, and the scales once the last d0 has been read, so the
-// next loads leave one block at a time instead of after the whole group.
+// Eight blocks U0..U0+7 of the chunk: table reads run two blocks ahead of the
+// arithmetic (three register sets of 16 values), which hides more LDS latency
+// than one block ahead at the same register budget as a third set of weight
+// registers would cost. With REFILL, block u's register is reloaded with
+// block u of group gn as soon as its table offsets have been extracted, and
+// the scales once the last d0 has been read, so the next loads leave one
+// block at a time instead of after the whole group.
 template <int H, int U0, bool REFILL>
 __device__ __forceinline__ void group8(const char *tab, u32x2 (&wb)[8], u32x4 &s8, float (&acc)[4],
                                        const RowPtrs &rp, int64_t gn) {
-    float va[16], vb[16];
+    float va[16], vb[16], vc[16];
     auto refill = [&](int u) {
         if constexpr (REFILL) wb[u] = ld_stream(&rp.bits[(8 * gn + u) * 128]);
     };
@@ -253,24 +255,24 @@ __device__ __forceinline__ void group8(const char *tab, u32x2 (&wb)[8], u32x4 &s
     refill(0);
     half_reads<H, U0 + 1>(tab, wb[1], vb);
     refill(1);
-    half_math(va, d0_half<0>(s8), acc);
-    half_reads<H, U0 + 2>(tab, wb[2], va);
+    half_reads<H, U0 + 2>(tab, wb[2], vc);
     refill(2);
-    half_math(vb, d0_half<1>(s8), acc);
-    half_reads<H, U0 + 3>(tab, wb[3], vb);
+    half_math(va, d0_half<0>(s8), acc);
+    half_reads<H, U0 + 3>(tab, wb[3], va);
     refill(3);
-    half_math(va, d0_half<2>(s8), acc);
-    half_reads<H, U0 + 4>(tab, wb[4], va);
+    half_math(vb, d0_half<1>(s8), acc);
+    half_reads<H, U0 + 4>(tab, wb[4], vb);
     refill(4);
-    half_math(vb, d0_half<3>(s8), acc);
-    half_reads<H, U0 + 5>(tab, wb[5], vb);
+    half_math(vc, d0_half<2>(s8), acc);
+    half_reads<H, U0 + 5>(tab, wb[5], vc);
     refill(5);
-    half_math(va, d0_half<4>(s8), acc);
+    half_math(va, d0_half<3>(s8), acc);
     half_reads<H, U0 + 6>(tab, wb[6], va);
     refill(6);
-    half_math(vb, d0_half<5>(s8), acc);
+    half_math(vb, d0_half<4>(s8), acc);
     half_reads<H, U0 + 7>(tab, wb[7], vb);
     refill(7);
+    half_math(vc, d0_half<5>(s8), acc);
     half_math(va, d0_half<6>(s8), acc);
     half_math(vb, d0_half<7>(s8), acc);
     if constexpr (REFILL) s8 = ld_stream(&rp.sc[gn * 64]);
@@ -278,9 +280,10 @@ __device__ __forceinline__ void group8(const char *tab, u32x2 (&wb)[8], u32x4 &s
 
 
 // One chunk of up to 32 blocks starting at group g0 (n4 full groups), with
-// the chunk's tables built in LDS. Straight-line code: three register
-// buffers, each group's loads issued two groups before it is consumed
-// (group indices clamped to the last full group, so every load is issued).
+// the chunk's tables built in LDS. Straight-line code: two register
+// buffers; the first two groups refill them with groups g0+2 and g0+3 as
+// they are consumed (group indices clamped to the last full group, so every
+// load is issued).
 template <int H, int NT>
 __device__ __forceinline__ void chunk(float *tab, const Q1Args &p, const RowPtrs &rp, int64_t g0, int64_t n4,
                                       int64_t ng, int64_t nb, float (&acc)[4]) {
@@ -291,18 +294,17 @@ __device__ __forceinline__ void chunk(float *tab, const Q1Args &p, const RowPtrs
     TableRawN<NT> raw;
     table_loads<NT>(raw, p.a, i0, cb);
     asm volatile("" ::: "memory");   // keep the table loads ahead of the prefetch
-    u32x2 w0[8], w1[8], w2[8];
-    u32x4 s0, s1, s2;
+    u32x2 w0[8], w1[8];
+    u32x4 s0, s1;
     load_group(rp, g0, w0, s0);
     load_group(rp, (g0 + 1 < gl) ? g0 + 1 : gl, w1, s1);
-    load_group(rp, (g0 + 2 < gl) ? g0 + 2 : gl, w2, s2);
     if (g0 > 0) __syncthreads();
     table_store<NT>(tab, raw, cb);
     __syncthreads();
-    group8<H, 0, true>(tabc, w0, s0, acc, rp, (g0 + 3 < gl) ? g0 + 3 : gl);
-    if (n4 > 1) group8<H, 8, false>(tabc, w1, s1, acc, rp, 0);
-    if (n4 > 2) group8<H, 16, false>(tabc, w2, s2, acc, rp, 0);
-    if (n4 > 3) group8<H, 24, false>(tabc, w0, s0, acc, rp, 0);
+    group8<H, 0, true>(tabc, w0, s0, acc, rp, (g0 + 2 < gl) ? g0 + 2 : gl);
+    if (n4 > 1) group8<H, 8, true>(tabc, w1, s1, acc, rp, (g0 + 3 < gl) ? g0 + 3 : gl);
+    if (n4 > 2) group8<H, 16, false>(tabc, w0, s0, acc, rp, 0);
+    if (n4 > 3) group8<H, 24, false>(tabc, w1, s1, acc, rp, 0);
 }
 
 // One block of half H at a run-time position (tail blocks past the last full
