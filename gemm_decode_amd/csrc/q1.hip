@@ -231,10 +231,20 @@ struct RowPtrs {
     gptr_u4 sc;            // scales of blocks 0..7 of this row; + (i/8)*64
 };
 
-__device__ __forceinline__ void load_group(const RowPtrs &rp, int64_t g, u32x2 (&wb)[8], u32x4 &s8) {
+// Streaming loads when every group is read once; plain loads when a chunk's
+// clamped prefetch will read the same group again (rows shorter than four
+// groups, a partial last chunk), so that the repeats find it in L2 instead
+// of fetching it from HBM again. `stream` is uniform.
+__device__ __forceinline__ void load_group(const RowPtrs &rp, int64_t g, u32x2 (&wb)[8], u32x4 &s8, bool stream) {
+    if (stream) {
 #pragma unroll
-    for (int u = 0; u < 8; u++) wb[u] = ld_stream(&rp.bits[(8 * g + u) * 128]);
-    s8 = ld_stream(&rp.sc[g * 64]);
+        for (int u = 0; u < 8; u++) wb[u] = ld_stream(&rp.bits[(8 * g + u) * 128]);
+        s8 = ld_stream(&rp.sc[g * 64]);
+    } else {
+#pragma unroll
+        for (int u = 0; u < 8; u++) wb[u] = rp.bits[(8 * g + u) * 128];
+        s8 = rp.sc[g * 64];
+    }
 }
 
 // Eight blocks U0..U0+7 of the chunk: table reads run two blocks ahead of the
@@ -296,13 +306,18 @@ __device__ __forceinline__ void chunk(float *tab, const Q1Args &p, const RowPtrs
     asm volatile("" ::: "memory");   // keep the table loads ahead of the prefetch
     u32x2 w0[8], w1[8];
     u32x4 s0, s1;
-    load_group(rp, g0, w0, s0);
-    load_group(rp, (g0 + 1 < gl) ? g0 + 1 : gl, w1, s1);
+    // Prefetch indices past the last group are redirected to this chunk's
+    // second group, which such a chunk loads with plain loads: the repeats
+    // then hit L2.
+    const bool stream = g0 + 3 <= gl;   // no prefetch index below is clamped
+    const int64_t g1 = (g0 + 1 < gl) ? g0 + 1 : gl;
+    load_group(rp, g0, w0, s0, stream);
+    load_group(rp, g1, w1, s1, stream);
     if (g0 > 0) __syncthreads();
     table_store<NT>(tab, raw, cb);
     __syncthreads();
-    group8<H, 0, true>(tabc, w0, s0, acc, rp, (g0 + 2 < gl) ? g0 + 2 : gl);
-    if (n4 > 1) group8<H, 8, true>(tabc, w1, s1, acc, rp, (g0 + 3 < gl) ? g0 + 3 : gl);
+    group8<H, 0, true>(tabc, w0, s0, acc, rp, (g0 + 2 <= gl) ? g0 + 2 : g1);
+    if (n4 > 1) group8<H, 8, true>(tabc, w1, s1, acc, rp, (g0 + 3 <= gl) ? g0 + 3 : g1);
     if (n4 > 2) group8<H, 16, false>(tabc, w0, s0, acc, rp, 0);
     if (n4 > 3) group8<H, 24, false>(tabc, w1, s1, acc, rp, 0);
 }
