@@ -43,7 +43,8 @@ METRIC = "Q1_0·q8_0 GEMV effective HBM GB/s (% of peak) + equiv tok/s, batch 1"
 # the kernel source they were measured on: reported only while its hash
 # matches, null after any change to it.
 _TRAFFIC = {
-    "q1": ("q1.hip", "5f2b0e44b61658d8", {"step": (167385.4, 2304.0)}),
+    "q1": ("q1.hip", "461193bb5b3e7ae6", {"step": (167478.6, 2304.0)}),
+    "q1_small": ("q1.hip", "461193bb5b3e7ae6", {"7646 x 256x1024": (138455.6, 7646.0)}),
     "ternary": ("ternary.hip", "8f60006b03cd5750",
                 {"2560x2560": (102109.9, 1200.0), "6912x2560": (137509.5, 1620.1), "2560x6912": (65808.1, 300.0)}),
     "blockq8": ("blockq8.hip", "123bb6b095593ab2", {"m1": (26533.5, 192.4), "m16": (27472.9, 3072.0)}),
@@ -427,6 +428,7 @@ def bench_q1_small(args, gd, torch):
     per_s, _ = _time_launches(torch, single, 64, 4)
     mism += int((ys1.cpu().numpy().view(np.uint32) != want).sum())
     g_gbps = count * gemv_bytes / per_g / 1e9
+    small_traffic = measured_traffic("q1_small")
     threads = cpu_cores()
     t_used, n_g = 0.0, 0
     while t_used < args.aux_cpu_seconds:
@@ -442,7 +444,9 @@ def bench_q1_small(args, gd, torch):
         "single_launch": {"us_per_gemv": round(per_s * 1e6, 3), "GB_per_s": round(gemv_bytes / per_s / 1e9, 1),
                           "timing": "HIP graph of 64 back-to-back single-GEMV launches"},
         "roofline": {"bound": "hbm", "achieved": round(g_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(g_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(g_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": (None if small_traffic is None or count != 7646
+                                 else small_traffic["7646 x 256x1024"]),
                      "kernel": "q1_gemv_grouped_kernel", "bytes_per_launch": count * gemv_bytes},
         "parity_mismatches": mism,
         "cpu_baseline": {"value": round(n_g * gemv_bytes / t_used / 1e9, 4), "unit": "GB/s", "cores": threads,
