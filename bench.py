@@ -43,30 +43,31 @@ METRIC = "Q1_0·q8_0 GEMV effective HBM GB/s (% of peak) + equiv tok/s, batch 1"
 # the kernel source they were measured on: reported only while its hash
 # matches, null after any change to it.
 _TRAFFIC = {
-    "q1": ("q1.hip", "461193bb5b3e7ae6", {"step": (167478.6, 2304.0)}),
-    "q1_small": ("q1.hip", "461193bb5b3e7ae6", {"7646 x 256x1024": (138455.6, 7646.0)}),
+    "q1": ("q1.hip", "461193bb5b3e7ae6", {"step": (167480.0, 2304.0)}),
+    "q1_small": ("q1.hip", "461193bb5b3e7ae6", {"7646 x 256x1024": (138455.5, 7646.0)}),
     "ternary": ("ternary.hip", "8f60006b03cd5750",
-                {"2560x2560": (102109.9, 1200.0), "6912x2560": (137509.5, 1620.1), "2560x6912": (65808.1, 300.0)}),
-    "blockq8": ("blockq8.hip", "123bb6b095593ab2", {"m1": (26533.5, 192.4), "m16": (27472.9, 3072.0)}),
+                {"2560x2560": (102218.2, 1200.0), "6912x2560": (137580.6, 1620.0), "2560x6912": (65781.3, 300.0)}),
+    "blockq8": ("blockq8.hip", "123bb6b095593ab2", {"m1": (26540.9, 192.4), "m16": (27469.0, 3072.0)}),
     "sign": ("sign_gemm.hip", "1122664298d09035",
-             {"split": (4128.8, 8208.0), "wpack": (2074.7, 4096.0), "gemm": (21355.4, 9728.0)}),
+             {"split": (4128.5, 8208.0), "wpack": (2074.1, 4096.0), "gemm": (21355.0, 9728.0)}),
     "sign_lut": ("sign_lut.hip", "c9273fa6aeb445b1",
                  {"4096x4096": (2170.0, 16.0), "14336x4096": (7290.0, 56.0), "lut4": (35127.5, 8192.0)}),
     "quant": ("quantize.hip", "aa440e939b0b9a5a",
               {"q8_0_decode": (266.5, 136.0), "q8_0_batch_256MiB": (131082.5, 69632.0),
                "int8_planes_decode_step": (522.6 + 536.5, 227.8 + 203.4),
-               "int8_planes_batch_256MiB": (131147.4, 66072.4)}),
+               "int8_planes_batch_256MiB": (131147.4, 66073.7)}),
     # per call: split kernel + merge kernel
     "attention": ("attention.hip", "3f3480fee0cca0a4",
-                  {"kv4096": (16477.0 + 597.0, 1040.0 + 16.0), "kv32768": (131165.0 + 597.0, 1040.0 + 16.0)}),
+                  {"kv4096": (16477.0 + 597.0, 1040.0 + 16.0),
+                   "kv32768": (131165.0 + 597.0, 1040.0 + 16.0)}),
 }
 
 
 # Hardware MFMA busy fraction (rocprofv3 SQ_VALU_MFMA_BUSY_CYCLES over the
 # dispatch's duration x 1024 SIMDs at 2.4 GHz), for the kernel source measured.
 _MFMA_BUSY = {
-    "sign_gemm_kernel": ("sign_gemm.hip", "1122664298d09035", 0.284),
-    "blockq8_mfma_kernel": ("blockq8.hip", "123bb6b095593ab2", 0.085),
+    "sign_gemm_kernel": ("sign_gemm.hip", "1122664298d09035", 0.289),
+    "blockq8_mfma_kernel": ("blockq8.hip", "123bb6b095593ab2", 0.088),
 }
 
 
