@@ -9,19 +9,21 @@
 // Split kernel. A workgroup (four waves) owns one KV head and one split:
 // the G = Hq/Hkv query heads that read that KV head are served together, so
 // each key and value row is read from HBM once for all of them. Keys come in
-// tiles of 64: the K and V tile are loaded with 16-byte coalesced loads into
-// registers one tile ahead, stored to LDS, and then wave w serves query head
-// 4i + w: lane t scores key t (scale * (q . k) over 128 dims, q read with
-// scalar loads since it is the same for the whole wave, K rows padded to 132
-// floats in LDS so the lanes' 16-byte reads hit distinct banks), the wave's
-// maximum and sum of exp
-// update the running state, and lane l accumulates output dims 2l, 2l+1
-// over the tile's keys, each key's weight taken from its lane with
-// v_readlane. The split writes its running output, maximum and denominator.
+// tiles of 64: the K tile and then the V tile are loaded with 16-byte
+// coalesced loads into registers, K is stored to LDS and scored while V is
+// still arriving, then V is stored; wave w serves query head 4i + w: lane t
+// scores key t (scale * (q . k) over 128 dims, q read with scalar loads since
+// it is the same for the whole wave, K rows padded to 132 floats in LDS so
+// the lanes' 16-byte reads hit distinct banks), the wave's maximum and sum
+// of exp update the running state, and lane l accumulates output dims 2l,
+// 2l+1 over the tile's keys, each key's weight taken from its lane with
+// v_readlane. The next tile's K and V loads go out as soon as this tile's
+// registers are in LDS. The split writes its running output, maximum and
+// denominator.
 //
-// Merge kernel. One workgroup per query head: the global maximum over the
-// splits, then sum_s exp(m_s - max) o_s[d] / sum_s exp(m_s - max) l_s, the
-// weights computed once per split into LDS.
+// Merge kernel. One workgroup per query head computes
+// sum_s exp(m_s - max) o_s[d] / sum_s exp(m_s - max) l_s over the splits,
+// 64 splits at a time under a running maximum.
 // A split with no keys writes max -inf, denominator 0 and output 0, and
 // contributes nothing.
 #include "gd_device.h"
@@ -52,22 +54,19 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-// Loads of one K and one V tile (rows t0.. of this KV head; rows past the
-// split end read as zero and are masked out of the scores).
-__device__ __forceinline__ void load_tile(const float *kb, const float *vb, int64_t t0, int64_t t_end,
-                                          f32x4 (&rk)[kLoadsPerThread], f32x4 (&rv)[kLoadsPerThread]) {
+// Loads of one K (or V) tile: rows t0.. of this KV head, each read once.
+// Rows past the split end are clamped to its last row, so every load is
+// issued unconditionally (no branch between the loads, so the wait for the
+// K tile need not include the V tile behind it); such keys are masked out of
+// the scores and get weight 0, and the row they repeat is finite.
+__device__ __forceinline__ void load_rows(const float *base, int64_t t0, int64_t t_end,
+                                          f32x4 (&r)[kLoadsPerThread]) {
 #pragma unroll
     for (int i = 0; i < kLoadsPerThread; i++) {
         const int e = threadIdx.x + kThreads * i;
         const int row = e / (kD / 4), c4 = e % (kD / 4);
-        const int64_t t = t0 + row;
-        if (t < t_end) {
-            rk[i] = gd::ld_stream(&((g_f4)(kb + t * kD))[c4]);   // each K/V row is read once
-            rv[i] = gd::ld_stream(&((g_f4)(vb + t * kD))[c4]);
-        } else {
-            rk[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            rv[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        }
+        const int64_t t = (t0 + row) < t_end ? (t0 + row) : t_end - 1;
+        r[i] = gd::ld_stream(&((g_f4)(base + t * kD))[c4]);
     }
 }
 
@@ -95,24 +94,30 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(const float *__res
         l[p] = 0.0f;
         acc[p][0] = acc[p][1] = 0.0f;
     }
+    // The K tile is loaded before the V tile, so the scores can start as soon
+    // as K is in (loads complete in order) while V is still arriving; the next
+    // tile's K goes out once this K is in LDS, its V once this V is.
     f32x4 rk[kLoadsPerThread], rv[kLoadsPerThread];
-    if (j0 < j1) load_tile(kb, vb, j0, j1, rk, rv);
+    if (j0 < j1) {
+        load_rows(kb, j0, j1, rk);
+        load_rows(vb, j0, j1, rv);
+    }
     for (int64_t t0 = j0; t0 < j1; t0 += kT) {
-        __syncthreads();   // the previous tile's LDS reads are done (and q is stored)
+        const bool more = t0 + kT < j1;
+        __syncthreads();   // the previous tile's LDS reads are done
 #pragma unroll
         for (int i = 0; i < kLoadsPerThread; i++) {
             const int e = threadIdx.x + kThreads * i;
-            const int row = e / (kD / 4), c4 = e % (kD / 4);
-            ks[row * (kKPad / 4) + c4] = rk[i];
-            vs[row * (kD / 2) + 2 * c4] = f32x2{rv[i][0], rv[i][1]};
-            vs[row * (kD / 2) + 2 * c4 + 1] = f32x2{rv[i][2], rv[i][3]};
+            ks[(e / (kD / 4)) * (kKPad / 4) + e % (kD / 4)] = rk[i];
         }
         __syncthreads();
-        if (t0 + kT < j1) load_tile(kb, vb, t0 + kT, j1, rk, rv);   // next tile, in flight during this one
+        if (more) load_rows(kb, t0 + kT, j1, rk);
         const int nvalid = static_cast<int>((j1 - t0) < kT ? (j1 - t0) : kT);
+        float pr[P];
 #pragma unroll
         for (int p = 0; p < P; p++) {
             const int h = 4 * p + wave;   // uniform per wave
+            pr[p] = 0.0f;
             if (h < G) {
                 // q[h] is the same for every lane: a uniform address, read
                 // with scalar loads and used as scalar operands
@@ -131,17 +136,34 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(const float *__res
                     s1 = __builtin_fmaf(q1[2], k1[2], s1);
                     s1 = __builtin_fmaf(q1[3], k1[3], s1);
                 }
-                const float s = lane < nvalid ? scale * (s0 + s1) : -__builtin_inff();
-                const float mnew = fmaxf(m[p], wave_max(s));   // finite: nvalid >= 1
-                const float pr = lane < nvalid ? expf(s - mnew) : 0.0f;
-                const float corr = expf(m[p] - mnew);         // 0 on the first tile
-                l[p] = l[p] * corr + wave_sum(pr);
+                const float sc = lane < nvalid ? scale * (s0 + s1) : -__builtin_inff();
+                const float mnew = fmaxf(m[p], wave_max(sc));   // finite: nvalid >= 1
+                pr[p] = lane < nvalid ? expf(sc - mnew) : 0.0f;
+                const float corr = expf(m[p] - mnew);          // 0 on the first tile
+                l[p] = l[p] * corr + wave_sum(pr[p]);
                 m[p] = mnew;
-                float a0 = acc[p][0] * corr, a1 = acc[p][1] * corr;
+                acc[p][0] *= corr;
+                acc[p][1] *= corr;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kLoadsPerThread; i++) {
+            const int e = threadIdx.x + kThreads * i;
+            const int row = e / (kD / 4), c4 = e % (kD / 4);
+            vs[row * (kD / 2) + 2 * c4] = f32x2{rv[i][0], rv[i][1]};
+            vs[row * (kD / 2) + 2 * c4 + 1] = f32x2{rv[i][2], rv[i][3]};
+        }
+        __syncthreads();
+        if (more) load_rows(vb, t0 + kT, j1, rv);
+#pragma unroll
+        for (int p = 0; p < P; p++) {
+            const int h = 4 * p + wave;
+            if (h < G) {
+                float a0 = acc[p][0], a1 = acc[p][1];
 #pragma unroll
                 for (int t = 0; t < kT; t++) {
                     const float pt = __builtin_bit_cast(
-                        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pr), t));
+                        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pr[p]), t));
                     const f32x2 v2 = vs[t * (kD / 2) + lane];
                     a0 = __builtin_fmaf(pt, v2[0], a0);
                     a1 = __builtin_fmaf(pt, v2[1], a1);
@@ -166,52 +188,64 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(const float *__res
     }
 }
 
-constexpr int kMergeChunk = 1024;   // split weights staged in LDS at a time
+constexpr int kMergeChunk = 64;                          // splits per step: one per lane of a wave
+constexpr int kMergeGroups = 4;                          // thread groups of kD, each a quarter of a step
+constexpr int kMergeThreads = kD * kMergeGroups;
+constexpr int kMergePerGroup = kMergeChunk / kMergeGroups;
 
-__device__ __forceinline__ float block_reduce(float v, bool is_max, float *red) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        const float u = __shfl_xor(v, o);
-        v = is_max ? fmaxf(v, u) : v + u;
-    }
-    __syncthreads();   // red is free (a previous reduction's reads are done)
-    if (threadIdx.x % 64 == 0) red[threadIdx.x / 64] = v;
-    __syncthreads();
-    return is_max ? fmaxf(red[0], red[1]) : red[0] + red[1];
-}
-
-// One workgroup (two waves, one output dim per thread) per query head: the
-// splits' maxima are reduced to the global maximum, each split's weight
-// exp(m_s - max) is computed once into LDS, and every dim's weighted sum
-// runs over the splits with eight loads in flight.
-__global__ __launch_bounds__(kD) void attn_merge_kernel(const float *__restrict__ part_o,
-                                                        const float *__restrict__ part_ml, float *__restrict__ out,
-                                                        int64_t Hq, int64_t S) {
-    static_assert(kD == 128, "two waves");
-    __shared__ float w[kMergeChunk];
-    __shared__ float red[kD / 64];
+// One workgroup per query head: kMergeGroups groups of kD threads, one
+// output dim per thread. The splits are taken 64 at a time: lane i of every
+// wave loads split c0 + i's maximum and denominator (one vector load), and
+// group g loads its dim of the partial outputs of splits c0 + 16g .. +15,
+// all issued before any is used (one memory latency per step). Every wave
+// sees all 64 maxima, so all groups follow the same running maximum: the
+// step's maximum raises it, the running sums are rescaled by exp(old - new),
+// and split i adds w_i = exp(m_i - max) times its denominator and output,
+// w_i computed once by lane i and read with v_readlane. The groups' sums
+// meet in LDS at the end. Splits past S and splits without keys (max -inf)
+// weigh 0.
+__global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(const float *__restrict__ part_o,
+                                                                   const float *__restrict__ part_ml,
+                                                                   float *__restrict__ out, int64_t Hq, int64_t S) {
+    static_assert(kD == 128 && kMergeChunk == 64, "lanes of a wave index the splits of a step");
+    __shared__ float part[kMergeGroups][kD];
     const int64_t h = blockIdx.x;
-    const int d = threadIdx.x;
-    float mx = -__builtin_inff();
-    for (int64_t s = d; s < S; s += kD) mx = fmaxf(mx, part_ml[(s * Hq + h) * 2]);
-    mx = block_reduce(mx, true, red);   // finite: some split has keys
-    float den = 0.0f, num = 0.0f;
+    const int d = threadIdx.x % kD;
+    const int grp = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kD);   // wave-uniform
+    const int lane = threadIdx.x % 64;
+    float mx = -__builtin_inff(), den = 0.0f, num = 0.0f;
     for (int64_t c0 = 0; c0 < S; c0 += kMergeChunk) {
-        const int cn = static_cast<int>((S - c0) < kMergeChunk ? (S - c0) : kMergeChunk);
-        __syncthreads();   // the previous chunk's weights are read
-        for (int i = d; i < cn; i += kD) {
-            const float ms = part_ml[((c0 + i) * Hq + h) * 2];
-            const float wi = ms == -__builtin_inff() ? 0.0f : expf(ms - mx);   // an empty split weighs 0
-            w[i] = wi;
-            den = __builtin_fmaf(part_ml[((c0 + i) * Hq + h) * 2 + 1], wi, den);
+        const int64_t mine = (c0 + lane) < S ? (c0 + lane) : S - 1;   // clamped: weighed 0 below
+        const f32x2 ml = *(const f32x2 *)(part_ml + (mine * Hq + h) * 2);
+        const int64_t g0 = c0 + kMergePerGroup * grp;
+        float o[kMergePerGroup];
+#pragma unroll
+        for (int i = 0; i < kMergePerGroup; i++) {
+            const int64_t sp = (g0 + i) < S ? (g0 + i) : S - 1;
+            o[i] = part_o[(sp * Hq + h) * kD + d];
         }
-        __syncthreads();
-        const float *po = part_o + (c0 * Hq + h) * kD + d;
-#pragma unroll 8
-        for (int i = 0; i < cn; i++) num = __builtin_fmaf(po[static_cast<int64_t>(i) * Hq * kD], w[i], num);
+        __builtin_amdgcn_sched_barrier(0);   // every load of the step is issued before any is used
+        // cm is finite: split 0 (in the first step) always has keys
+        const float mi = (c0 + lane) < S ? ml[0] : -__builtin_inff();
+        const float cm = fmaxf(mx, wave_max(mi));
+        const float corr = mx == -__builtin_inff() ? 0.0f : expf(mx - cm);
+        const float wi = mi == -__builtin_inff() ? 0.0f : expf(mi - cm);
+        den = den * corr + wave_sum(wi * ((c0 + lane) < S ? ml[1] : 0.0f));
+        num *= corr;
+#pragma unroll
+        for (int i = 0; i < kMergePerGroup; i++) {
+            const float w = __builtin_bit_cast(
+                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wi), kMergePerGroup * grp + i));
+            num = __builtin_fmaf(o[i], w, num);
+        }
+        mx = cm;
     }
-    den = block_reduce(den, false, red);
-    out[h * kD + d] = num / den;
+    part[grp][d] = num;
+    __syncthreads();
+    if (grp == 0) {
+        const float t = (part[0][d] + part[1][d]) + (part[2][d] + part[3][d]);
+        out[h * kD + d] = t / den;   // den > 0: split 0 always has keys
+    }
 }
 
 int plan(int64_t n_heads, int64_t n_kv_heads, int64_t head_dim, int64_t kv_len, int64_t num_splits,
@@ -288,7 +322,7 @@ extern "C" int attn_decode_splitk(const float *q, const float *k_cache, const fl
     else
         GD_ATTN(8);
 #undef GD_ATTN
-    hipLaunchKernelGGL(attn_merge_kernel, dim3(static_cast<uint32_t>(n_heads)), dim3(kD), 0, hs, part_o, part_ml,
-                       out, n_heads, s);
+    hipLaunchKernelGGL(attn_merge_kernel, dim3(static_cast<uint32_t>(n_heads)), dim3(kMergeThreads), 0, hs, part_o,
+                       part_ml, out, n_heads, s);
     return check_launch("attn_decode_splitk");
 }
