@@ -441,14 +441,14 @@ struct McShape {
 // per thread), for chunk blocks i0 .. i0+CB-1 of columns c0 .. c0+MC-1.
 // Columns past ncols and blocks past nb read clamped positions; their
 // entries are never used.
-template <int MC>
-__device__ __forceinline__ void mc_table_loads(TableRaw &raw, const uint16_t *a_generic, int64_t col_halves,
+template <int MC, int NT>
+__device__ __forceinline__ void mc_table_loads(TableRawN<NT> &raw, const uint16_t *a_generic, int64_t col_halves,
                                                int ncols, int64_t i0, int cb) {
     constexpr int CB = McShape<MC>::CB;
     const auto a = (const uint16_t __attribute__((address_space(1))) *)a_generic;
 #pragma unroll
-    for (int j = 0; j < kGroupsPerThread; j++) {
-        const int g = threadIdx.x + kThreads * j;
+    for (int j = 0; j < TableRawN<NT>::NG; j++) {
+        const int g = threadIdx.x + NT * j;
         const int c = g / (CB * 32), rem = g % (CB * 32);
         int u = rem >> 5;
         const int k = (rem >> 3) & 3, l = rem & 7;
@@ -533,7 +533,7 @@ __device__ __forceinline__ void mc_compute(const char *tab, const McChunk<MC> &b
     }
 }
 
-template <int H, int MC>
+template <int H, int MC, int NT>
 __device__ __forceinline__ void mc_half_row(float *tab, const uint16_t *a, int64_t col_halves, int ncols,
                                             const RowPtrs &rp, int64_t nb, float (&acc)[MC][4]) {
     constexpr int CB = McShape<MC>::CB;
@@ -544,33 +544,34 @@ __device__ __forceinline__ void mc_half_row(float *tab, const uint16_t *a, int64
     for (int64_t j = 0; j < nch; j += 2) {
         {   // chunk j (even), weights in ba
             const int cb = static_cast<int>((nb - j * CB) < CB ? (nb - j * CB) : CB);
-            TableRaw raw;
-            mc_table_loads<MC>(raw, a, col_halves, ncols, j * CB, cb);
+            TableRawN<NT> raw;
+            mc_table_loads<MC, NT>(raw, a, col_halves, ncols, j * CB, cb);
             asm volatile("" ::: "memory");   // table loads ahead of the next chunk's weights
             mc_load<MC>(rp, j + 1, nb, bb);
             if (j > 0) __syncthreads();
-            table_store(tab, raw, kChunkBlocks);
+            table_store<NT>(tab, raw, kChunkBlocks);
             __syncthreads();
             mc_compute<H, MC, 0>(tabc, ba, cb, acc);
         }
         if (j + 1 < nch) {   // chunk j+1 (odd), weights in bb
             const int cb = static_cast<int>((nb - (j + 1) * CB) < CB ? (nb - (j + 1) * CB) : CB);
-            TableRaw raw;
-            mc_table_loads<MC>(raw, a, col_halves, ncols, (j + 1) * CB, cb);
+            TableRawN<NT> raw;
+            mc_table_loads<MC, NT>(raw, a, col_halves, ncols, (j + 1) * CB, cb);
             asm volatile("" ::: "memory");
             mc_load<MC>(rp, j + 2, nb, ba);
             __syncthreads();
-            table_store(tab, raw, kChunkBlocks);
+            table_store<NT>(tab, raw, kChunkBlocks);
             __syncthreads();
             mc_compute<H, MC, (CB < 8 ? 1 : 0)>(tabc, bb, cb, acc);
         }
     }
 }
 
-template <int MC>
-__global__ __launch_bounds__(kThreads) void q1_gemv_mc_kernel(const uint32_t *bits, const uint4 *scales,
-                                                              const uint16_t *a, float *y, int64_t rows, int64_t nb,
-                                                              int64_t nb8, int64_t n_act) {
+// NT threads: NT/128 tiles of 64 rows, two waves (halves) each.
+template <int MC, int NT>
+__global__ __launch_bounds__(NT) void q1_gemv_mc_kernel(const uint32_t *bits, const uint4 *scales, const uint16_t *a,
+                                                        float *y, int64_t rows, int64_t nb, int64_t nb8,
+                                                        int64_t n_act) {
     __shared__ float tab[kTableFloats];
     const int64_t c0 = static_cast<int64_t>(blockIdx.y) * MC;     // first column of this group
     const int ncols = static_cast<int>((n_act - c0) < MC ? (n_act - c0) : MC);
@@ -578,7 +579,7 @@ __global__ __launch_bounds__(kThreads) void q1_gemv_mc_kernel(const uint32_t *bi
     const uint16_t *ag = a + c0 * col_halves;
     const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
     const int tl = wave >> 1, h = wave & 1;
-    const int64_t r = static_cast<int64_t>(blockIdx.x) * kRowsPerWG + tl * 64 + lane;
+    const int64_t r = static_cast<int64_t>(blockIdx.x) * (NT / 2) + tl * 64 + lane;
     const int64_t r64 = (rows + 63) / 64 * 64;
     const int64_t rl = r < r64 ? r : r64 - 1;
     const int64_t t = rl / 64, ln = rl % 64;
@@ -589,9 +590,9 @@ __global__ __launch_bounds__(kThreads) void q1_gemv_mc_kernel(const uint32_t *bi
 #pragma unroll
         for (int q = 0; q < 4; q++) acc[c][q] = 0.0f;
     if (h == 0)
-        mc_half_row<0, MC>(tab, ag, col_halves, ncols, rp, nb, acc);
+        mc_half_row<0, MC, NT>(tab, ag, col_halves, ncols, rp, nb, acc);
     else
-        mc_half_row<1, MC>(tab, ag, col_halves, ncols, rp, nb, acc);
+        mc_half_row<1, MC, NT>(tab, ag, col_halves, ncols, rp, nb, acc);
     // The high half hands lanes 4..7 of every column to the low half through LDS.
     __syncthreads();
     float4 *xch = reinterpret_cast<float4 *>(tab) + (tl * 64 + lane) * MC;
@@ -871,6 +872,11 @@ extern "C" int q1_q8_gemv(const void *bits_plane, const void *scale_plane, const
         // The largest group (8, 4, 2 columns) that still gives about three
         // quarters of the 256 CUs a workgroup; fewer workgroups leave CUs
         // idle, while more groups only re-read the weights (mostly from L2).
+        // When 2-column groups of 256 rows would occupy at most half of the
+        // CUs, they take 128 rows instead: twice as many table builds per
+        // row, twice as many CUs at work. Measured at 14336 x 4096: 3 and 4
+        // columns 16.7 -> 13.3 us; at 5 to 8 columns (168 to 224 workgroups of
+        // 256 rows) 128-row workgroups were slower (18 - 20 us against 16.7).
         int mc = 2;
         for (int cand : {8, 4}) {
             if (n_act >= cand / 2 + 1 && gx * ((n_act + cand - 1) / cand) >= 192) {
@@ -878,13 +884,21 @@ extern "C" int q1_q8_gemv(const void *bits_plane, const void *scale_plane, const
                 break;
             }
         }
-        const dim3 grid(static_cast<uint32_t>(gx), static_cast<uint32_t>((n_act + mc - 1) / mc));
-        if (mc == 2)
-            hipLaunchKernelGGL(q1_gemv_mc_kernel<2>, grid, dim3(kThreads), 0, hs, bp, sp, ap, y, rows, nb, nb8, n_act);
+        const bool narrow = mc == 2 && gx * ((n_act + 1) / 2) <= 128;
+        const int64_t tiles = narrow ? (rows + kRowsPerWG / 2 - 1) / (kRowsPerWG / 2) : gx;
+        const dim3 grid(static_cast<uint32_t>(tiles), static_cast<uint32_t>((n_act + mc - 1) / mc));
+        if (narrow)
+            hipLaunchKernelGGL((q1_gemv_mc_kernel<2, kThreads / 2>), grid, dim3(kThreads / 2), 0, hs, bp, sp, ap, y,
+                               rows, nb, nb8, n_act);
+        else if (mc == 2)
+            hipLaunchKernelGGL((q1_gemv_mc_kernel<2, kThreads>), grid, dim3(kThreads), 0, hs, bp, sp, ap, y, rows,
+                               nb, nb8, n_act);
         else if (mc == 4)
-            hipLaunchKernelGGL(q1_gemv_mc_kernel<4>, grid, dim3(kThreads), 0, hs, bp, sp, ap, y, rows, nb, nb8, n_act);
+            hipLaunchKernelGGL((q1_gemv_mc_kernel<4, kThreads>), grid, dim3(kThreads), 0, hs, bp, sp, ap, y, rows,
+                               nb, nb8, n_act);
         else
-            hipLaunchKernelGGL(q1_gemv_mc_kernel<8>, grid, dim3(kThreads), 0, hs, bp, sp, ap, y, rows, nb, nb8, n_act);
+            hipLaunchKernelGGL((q1_gemv_mc_kernel<8, kThreads>), grid, dim3(kThreads), 0, hs, bp, sp, ap, y, rows,
+                               nb, nb8, n_act);
         return check_launch("q1_q8_gemv");
     }
 

@@ -113,10 +113,14 @@ def test_multi_column_bit_exact(gd, n_act, rows, K):
     (14329, 4096, 29),   # groups of 8, the last one partial (5 columns)
     (12289, 1152, 16),   # 49 row blocks, 9 blocks per row: groups of 4, short chunks
     (12289, 1152, 40),   # groups of 8, short chunks
+    (14336, 4096, 4),    # 128-row workgroups (256-row ones would fill 112 CUs), groups of 2
+    (10000, 1152, 6),    # 128-row workgroups, three groups of 2, short chunks
+    (12545, 1152, 6),    # 150 workgroups of 256 rows: kept
 ])
 def test_multi_column_wide_groups(gd, rows, K, n_act):
     """Shapes whose row count makes the 4- and 8-column kernels the ones
-    chosen; every column bit-exact with its own batch-1 GEMV."""
+    chosen, and shapes on either side of the switch to 128-row workgroups; every column
+    bit-exact with its own batch-1 GEMV."""
     W = wl.q1_weights_aos(rows, K, 11 + n_act)
     A = np.concatenate([wl.q8_acts_aos(K, 9000 + c) for c in range(n_act)])
     got = run_gemv(gd, W, A, rows, K, n_act)
