@@ -43,11 +43,11 @@ METRIC = "Q1_0·q8_0 GEMV effective HBM GB/s (% of peak) + equiv tok/s, batch 1"
 # the kernel source they were measured on: reported only while its hash
 # matches, null after any change to it.
 _TRAFFIC = {
-    "q1": ("q1.hip", "461193bb5b3e7ae6", {"step": (167480.0, 2304.0)}),
-    "q1_small": ("q1.hip", "461193bb5b3e7ae6", {"7646 x 256x1024": (138455.5, 7646.0)}),
+    "q1": ("q1.hip", "b014ec4793f1a6e3", {"step": (167503.0, 2304.0)}),
+    "q1_small": ("q1.hip", "b014ec4793f1a6e3", {"7646 x 256x1024": (138460.6, 7646.0)}),
     "ternary": ("ternary.hip", "8f60006b03cd5750",
-                {"2560x2560": (102218.2, 1200.0), "6912x2560": (137580.6, 1620.0), "2560x6912": (65781.3, 300.0)}),
-    "blockq8": ("blockq8.hip", "123bb6b095593ab2", {"m1": (26540.9, 192.4), "m16": (27469.0, 3072.0)}),
+                {"2560x2560": (102163.2, 1200.0), "6912x2560": (137534.8, 1620.0), "2560x6912": (65763.5, 300.0)}),
+    "blockq8": ("blockq8.hip", "123bb6b095593ab2", {"m1": (26540.7, 192.4), "m16": (27467.3, 3072.0)}),
     "sign": ("sign_gemm.hip", "1122664298d09035",
              {"split": (4128.5, 8208.0), "wpack": (2074.1, 4096.0), "gemm": (21355.0, 9728.0)}),
     "sign_lut": ("sign_lut.hip", "c9273fa6aeb445b1",
@@ -55,11 +55,11 @@ _TRAFFIC = {
     "quant": ("quantize.hip", "aa440e939b0b9a5a",
               {"q8_0_decode": (266.5, 136.0), "q8_0_batch_256MiB": (131082.5, 69632.0),
                "int8_planes_decode_step": (522.6 + 536.5, 227.8 + 203.4),
-               "int8_planes_batch_256MiB": (131147.4, 66073.7)}),
+               "int8_planes_batch_256MiB": (131147.4, 66074.8)}),
     # per call: split kernel + merge kernel
-    "attention": ("attention.hip", "3f3480fee0cca0a4",
-                  {"kv4096": (16477.0 + 597.0, 1040.0 + 16.0),
-                   "kv32768": (131165.0 + 597.0, 1040.0 + 16.0)}),
+    "attention": ("attention.hip", "90a47144e8c51bc0",
+                  {"kv4096": (16453.5 + 605.0, 1040.0 + 16.0),
+                   "kv32768": (131141.5 + 605.0, 1040.0 + 16.0)}),
 }
 
 
@@ -67,7 +67,7 @@ _TRAFFIC = {
 # dispatch's duration x 1024 SIMDs at 2.4 GHz), for the kernel source measured.
 _MFMA_BUSY = {
     "sign_gemm_kernel": ("sign_gemm.hip", "1122664298d09035", 0.289),
-    "blockq8_mfma_kernel": ("blockq8.hip", "123bb6b095593ab2", 0.088),
+    "blockq8_mfma_kernel": ("blockq8.hip", "123bb6b095593ab2", 0.087),
 }
 
 
