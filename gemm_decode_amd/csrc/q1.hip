@@ -423,6 +423,105 @@ __global__ __launch_bounds__(NT) void q1_gemv_grouped_kernel(const gd_q1_problem
     q1_gemv_body<NT>(p, tab, prow, nb, nb8);
 }
 
+// Grouped problems with K <= 1024: one group of at most eight blocks per
+// row, so one table build per workgroup and no chunk loop. Each workgroup
+// (NT threads: NT/2 rows, two waves per 64-row tile as above) stages its
+// problem's activation into a 16 KiB table, loads its rows' blocks once and
+// runs the same table reads and arithmetic (group8 for eight blocks, the
+// tail steps for fewer), so the bits are those of the general kernel; the
+// smaller table and register set let more workgroups share a CU, which
+// hides the latency that a workgroup's single short pass otherwise exposes.
+constexpr int kSmallBlocks = 8;
+constexpr int kSmallThreads = 256;   // 128 rows per workgroup
+
+template <int NT>
+__global__ __launch_bounds__(NT) void q1_gemv_grouped_small_kernel(const gd_q1_problem *probs, int64_t rows,
+                                                                   int64_t nb) {
+    static_assert(NT >= 256, "one table group per thread at most");
+    __shared__ __attribute__((aligned(16))) float tab[kSmallBlocks * 512];
+    const gd_q1_problem pr = probs[blockIdx.y];
+    const int64_t prow = (pr.rows >= 1 && pr.rows <= rows) ? pr.rows : rows;
+    if (static_cast<int64_t>(blockIdx.x) * (NT / 2) >= prow) return;   // uniform: before any barrier
+    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+    const int tl = wave >> 1, h = wave & 1;
+    const int64_t r = static_cast<int64_t>(blockIdx.x) * (NT / 2) + tl * 64 + lane;
+    const int64_t r64 = (prow + 63) / 64 * 64;
+    const int64_t rl = r < r64 ? r : r64 - 1;   // padded rows: same work, never stored
+    const int64_t t = rl / 64, ln = rl % 64;
+    // nb <= 8: the scale plane holds one 8-block group per row
+    const RowPtrs rp{(gptr_u2)pr.bits_plane + ((t * nb) * 2 + h) * 64 + ln,
+                     (gptr_u4)pr.scale_plane + t * 64 + ln};
+    // 1. the activation's table groups first (one per thread), so the table
+    //    build waits for them only
+    const int ng = static_cast<int>(nb) * 32;
+    const auto a = (const uint16_t __attribute__((address_space(1))) *)pr.a_q8;
+    const int g = static_cast<int>(threadIdx.x) < ng ? static_cast<int>(threadIdx.x) : ng - 1;
+    const auto blk = a + ((g >> 5) * 4 + ((g >> 3) & 3)) * 17;   // 34 bytes = 17 halves
+    const uint32_t rd = blk[0], rq01 = blk[1 + 2 * (g & 7)], rq23 = blk[2 + 2 * (g & 7)];
+    asm volatile("" ::: "memory");
+    // 2. this row half's blocks (each read once when there are eight; fewer
+    //    repeat the last one, which plain loads then find in cache)
+    u32x2 wb[kSmallBlocks];
+    u32x4 s8;
+    if (nb == kSmallBlocks) {
+        load_group(rp, 0, wb, s8, true);
+    } else {
+#pragma unroll
+        for (int u = 0; u < kSmallBlocks; u++) wb[u] = rp.bits[(u < nb ? u : nb - 1) * 128];
+        s8 = rp.sc[0];
+    }
+    // 3. the table: T[n] for group g (see table_store)
+    if (static_cast<int>(threadIdx.x) < ng) {
+        const float d1 = f16_to_f32(static_cast<uint16_t>(rd));
+        const int32_t q[4] = {static_cast<int8_t>(rq01 & 0xff), static_cast<int8_t>(rq01 >> 8),
+                              static_cast<int8_t>(rq23 & 0xff), static_cast<int8_t>(rq23 >> 8)};
+        int32_t base = 0;
+        float dlt[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++) {
+            const int32_t neg = (q[jj] == -128) ? -128 : -q[jj];   // int8 wrapping negation
+            base += neg;
+            dlt[jj] = d1 * static_cast<float>(q[jj] - neg);         // exact: |q - neg| <= 255
+        }
+        float v[16];
+        v[0] = d1 * static_cast<float>(base);                        // exact: |base| <= 512
+#pragma unroll
+        for (int n = 1; n < 16; n++) v[n] = v[n & (n - 1)] + dlt[__builtin_ctz(n)];
+        float4 *dst = reinterpret_cast<float4 *>(tab + threadIdx.x * 16);
+#pragma unroll
+        for (int m = 0; m < 4; m++) dst[m] = make_float4(v[4 * m], v[4 * m + 1], v[4 * m + 2], v[4 * m + 3]);
+    }
+    __syncthreads();
+    // 4. the blocks, in order
+    const char *tabc = reinterpret_cast<const char *>(tab);
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (nb == kSmallBlocks) {
+        if (h == 0)
+            group8<0, 0, false>(tabc, wb, s8, acc, rp, 0);
+        else
+            group8<1, 0, false>(tabc, wb, s8, acc, rp, 0);
+    } else {
+#pragma unroll
+        for (int u = 0; u < kSmallBlocks; u++) {
+            if (u < nb) {   // uniform
+                if (h == 0)
+                    tail_block<0>(tabc + u * 2048, wb[u], d0_of(s8, u), acc);
+                else
+                    tail_block<1>(tabc + u * 2048, wb[u], d0_of(s8, u), acc);
+            }
+        }
+    }
+    // 5. the high half hands lanes 4..7 to the low half through LDS
+    __syncthreads();
+    float4 *xch = reinterpret_cast<float4 *>(tab) + tl * 64 + lane;
+    if (h == 1) *xch = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    __syncthreads();
+    if (h == 0 && r < prow) {
+        const float4 hi = *xch;
+        pr.y[r] = ((acc[0] + hi.x) + (acc[2] + hi.z)) + ((acc[1] + hi.y) + (acc[3] + hi.w));
+    }
+}
+
 // ------------------------------------------------------- several columns
 // Small-M product (P1's multi-column Q1_MM): MC activation columns against
 // the same weights in one workgroup, every column's chains in the stated
@@ -919,6 +1018,14 @@ extern "C" int q1_q8_gemv_grouped(const gd_q1_problem *problems, int64_t count, 
     GD_REQUIRE(count <= 65535, GD_ERANGE, "q1_q8_gemv_grouped: count (%lld) above 65535", (long long)count);
     GD_REQUIRE(aligned(problems, 8), GD_EALIGN, "q1_q8_gemv_grouped: problems must be 8-byte aligned");
     const int64_t nb = K / 128, nb8 = (nb + 7) / 8 * 8;
+    if (nb <= kSmallBlocks) {   // one group of blocks per row
+        constexpr int NT = kSmallThreads;
+        const int64_t gx = (rows + NT / 2 - 1) / (NT / 2);
+        hipLaunchKernelGGL(q1_gemv_grouped_small_kernel<NT>,
+                           dim3(static_cast<uint32_t>(gx), static_cast<uint32_t>(count)), dim3(NT), 0,
+                           as_stream(stream), problems, rows, nb);
+        return check_launch("q1_q8_gemv_grouped");
+    }
     constexpr int NT = kGroupedThreads;
     const int64_t gx = (rows + NT / 2 - 1) / (NT / 2);
     hipLaunchKernelGGL(q1_gemv_grouped_kernel<NT>, dim3(static_cast<uint32_t>(gx), static_cast<uint32_t>(count)),

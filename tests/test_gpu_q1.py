@@ -239,16 +239,19 @@ def test_deterministic_repeat(gd):
     assert_bits_equal(outs[2], outs[0], "repeat 2")
 
 
-def test_grouped_mixed_rows(gd):
+@pytest.mark.parametrize("K", [128, 640, 1024, 1152])
+def test_grouped_mixed_rows(gd, K):
     """One grouped launch over problems of different row counts (common K):
     each output bit-exact with the oracle for its own shape, nothing written
-    past a problem's rows, and rows = 0 meaning the launch's rows."""
-    K, rows_max = 1024, 1000
+    past a problem's rows, and rows = 0 meaning the launch's rows. K up to
+    1024 (one block, a partial and a full group of eight) takes the one-group
+    kernel, 1152 the general one."""
+    rows_max = 1000
     shapes = [(1000, 1000), (300, 300), (65, 65), (1000, 0), (1, 1), (257, 257)]   # (rows, field)
     entries, keep, wants = [], [], []
     for i, (rows, field) in enumerate(shapes):
-        W = wl.q1_weights_aos(rows, K, 40 + i)
-        A = wl.q8_acts_aos(K, 4000 + i)
+        W = wl.q1_weights_aos(rows, K, 40 + i + K)
+        A = wl.q8_acts_aos(K, 4000 + i + K)
         b, s = planes_on_gpu(gd, W, rows, K)
         a = dev(A.reshape(-1))
         y = torch.full((rows + 64,), float("nan"), device="cuda")      # 64 guard elements
