@@ -306,3 +306,27 @@ def test_validation_errors_raise(gd):
     with pytest.raises(gd.GemmDecodeError, match="GD_EALIGN"):
         gd._check(gd.lib().q1_q8_gemv(b.data_ptr() + 4, s.data_ptr(), a.data_ptr(), y.data_ptr(), 64, 128, 1,
                                       None))
+
+
+def test_small_config_grouped_as_benchmarked(gd):
+    """The 256x1024 config in the launch the benchmark times: 7,646
+    independent problems in one grouped launch (the one-group kernel).
+    Problem p reads weight set p % 4 and activation (p // 4) % 3, so a
+    problem mapped to the wrong planes, activation or output shows; every
+    output bit-exact with the oracle."""
+    cfg = wl.Q1_SMALL
+    rows, K, count = cfg.rows, cfg.K, 7646
+    Ws = [wl.q1_weights_aos(rows, K, cfg.weight_seed + w) for w in range(4)]
+    As = [wl.q8_acts_aos(K, cfg.act_seeds[0] + a) for a in range(3)]
+    planes = [planes_on_gpu(gd, W, rows, K) for W in Ws]
+    acts = [dev(A.reshape(-1)) for A in As]
+    y = torch.full((count * rows,), float("nan"), device="cuda")
+    entries = [(planes[p % 4][0], planes[p % 4][1], acts[(p // 4) % 3], y[p * rows:(p + 1) * rows])
+               for p in range(count)]
+    probs = gd.make_q1_problems(entries)
+    gd.q1_q8_gemv_grouped(probs, count, rows, K)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy().reshape(count, rows)
+    want = {(w, a): oracle.q1_q8_gemv_aos(Ws[w], As[a], rows, K).reshape(-1) for w in range(4) for a in range(3)}
+    for p in range(count):
+        assert_bits_equal(got[p], want[(p % 4, (p // 4) % 3)], f"problem {p}")

@@ -141,3 +141,48 @@ def test_batched_bitplanes(gd):
     got = xp.cpu().numpy().view(np.uint32).reshape(count, 8, K // 32)
     for c in range(count):
         assert np.array_equal(got[c], planes_ref(xq[c]))
+
+
+def test_full_decode_step_as_benchmarked(gd):
+    """The whole 30-layer decode step (210 GEMVs) in the launch configuration
+    the benchmark times: one weight per shape shared by its GEMVs, one
+    activation per GEMV, the bit planes of every token of a K in one launch,
+    then one grouped launch per shape (120, 60 and 30 problems). Every dot
+    and output bit-exact with the oracle."""
+    shapes = wl.bitnet_step_shapes()
+    assert len(shapes) == 210
+    groups = {}
+    for j, sh in enumerate(shapes):
+        groups.setdefault(sh, []).append(j)
+    base = {sh: wl.ternary_inputs(sh[0], sh[1], wl.TERNARY_SEED_BASE + 1000 + sh[0] + sh[1])[:3] for sh in groups}
+    xq, xsc = {}, {}
+    for j, (rows, K) in enumerate(shapes):
+        rng = np.random.default_rng(wl.TERNARY_SEED_BASE + j)
+        xq[j], xsc[j] = wl.absmax_int8(rng.standard_normal(K))
+    planes, where = {}, {}
+    for K in sorted({sh[1] for sh in shapes}):
+        js = [j for j, sh in enumerate(shapes) if sh[1] == K]
+        xs_dev = dev(np.stack([xq[j] for j in js]))
+        planes[K] = torch.empty(len(js) * 8 * (K // 32), dtype=torch.int32, device="cuda")
+        gd.ternary_act_bitplanes(xs_dev, len(js), K, planes[K])
+        for pos, j in enumerate(js):
+            where[j] = (K, pos)
+    wdev = {sh: (dev(i32(base[sh][0])), dev(i32(base[sh][1]))) for sh in groups}
+    ys = {j: torch.full((shapes[j][0],), float("nan"), device="cuda") for j in range(len(shapes))}
+    ds = {j: torch.full((shapes[j][0],), -7, dtype=torch.int32, device="cuda") for j in range(len(shapes))}
+    probs = {}
+    for sh, idx in groups.items():
+        entries = []
+        for j in idx:
+            K, pos = where[j]
+            W = K // 32
+            entries.append((wdev[sh][0], wdev[sh][1], planes[K][pos * 8 * W:(pos + 1) * 8 * W], ys[j], ds[j],
+                            base[sh][2], xsc[j]))
+        probs[sh] = gd.make_ternary_problems(entries)
+        gd.ternary_gemv_grouped(probs[sh], len(idx), sh[0], sh[1])
+    torch.cuda.synchronize()
+    for j, sh in enumerate(shapes):
+        P, N, ws = base[sh]
+        yo, do = oracle.ternary_gemv(P, N, ws, xq[j], xsc[j], nthreads=oracle.max_threads())
+        assert np.array_equal(ds[j].cpu().numpy(), do), f"GEMV {j} {sh}: dot"
+        assert np.array_equal(ys[j].cpu().numpy().view(np.uint32), yo.view(np.uint32)), f"GEMV {j} {sh}: y"
