@@ -624,7 +624,7 @@ def bench_sign(args, gd, torch):
                      "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
                      "traffic": None if sg_traffic is None else sum(sg_traffic.values()),
                      "traffic_per_kernel": sg_traffic,
-                     "kernel": "q1_sign_gemm call (sign_split, sign_wpack, sign_gemm kernels)",
+                     "kernel": "q1_sign_gemm call (sign_prep: split + weight regroup in one launch; sign_gemm)",
                      "flops_per_launch": flops,
                      "mfma_busy_hw": measured_mfma_busy("sign_gemm_kernel")},
         "parity_rel_err_sampled": rel,

@@ -15,7 +15,8 @@
 // The result is within ~1e-7 of ||y||_inf of the f64 definition for any
 // finite x.
 //
-// Three launches.
+// Three steps; a call on unpacked weights runs split and wpack as one launch
+// (independent work, side by side), a call on packed weights split alone.
 //  split: one workgroup per row (rows padded to a multiple of 16) finds e_m
 //         and writes the row's hi/lo halves to the workspace, each 32-weight
 //         group as one 128-byte line (its 32 hi halves, then its 32 lo
@@ -76,12 +77,13 @@ constexpr int kStep = 2;                  // groups per load step
 // 64 outputs, each pair a contiguous 1 KiB run.
 constexpr int kPackRows = 64, kPackGroups = 32;
 
-__global__ __launch_bounds__(kPrepThreads) void sign_wpack_kernel(const uint32_t *bits_g, const float *scales_g,
-                                                                  int64_t N, int64_t G, u32x4 *__restrict__ wv) {
+// Tile (bx, by): rows 64*bx.., groups 32*by..
+__device__ __forceinline__ void wpack_tile(const uint32_t *bits_g, const float *scales_g, int64_t N, int64_t G,
+                                           u32x4 *__restrict__ wv, int64_t bx, int64_t by) {
     __shared__ uint32_t tb[kPackRows][kPackGroups + 1];
     __shared__ uint32_t ts[kPackRows][kPackGroups + 1];
-    const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kPackRows;
-    const int64_t g0 = static_cast<int64_t>(blockIdx.y) * kPackGroups;
+    const int64_t n0 = bx * kPackRows;
+    const int64_t g0 = by * kPackGroups;
     const int tid = threadIdx.x;
 #pragma unroll
     for (int k = 0; k < kPackRows * kPackGroups / kPrepThreads; k++) {   // 8 words per thread
@@ -104,18 +106,21 @@ __global__ __launch_bounds__(kPrepThreads) void sign_wpack_kernel(const uint32_t
     }
 }
 
+__global__ __launch_bounds__(kPrepThreads) void sign_wpack_kernel(const uint32_t *bits_g, const float *scales_g,
+                                                                  int64_t N, int64_t G, u32x4 *__restrict__ wv) {
+    wpack_tile(bits_g, scales_g, N, G, wv, blockIdx.x, blockIdx.y);
+}
+
 // sign_split_kernel splits one padded row of x per workgroup; for
 // K <= 32 * kSplitItems * kPrepThreads / 4 the row stays in registers
 // between finding its largest |x| and converting it.
 constexpr int kSplitItems = 4;   // (group, quarter) items per thread held in registers
 
-__global__ __launch_bounds__(kPrepThreads) void sign_split_kernel(const float *x_g, int64_t M, int64_t K,
-                                                                  uint32_t *__restrict__ xs,
-                                                                  int32_t *__restrict__ rexp) {
+__device__ __forceinline__ void split_row(const float *x_g, int64_t M, int64_t K, uint32_t *__restrict__ xs,
+                                          int32_t *__restrict__ rexp, int64_t m) {
     const int64_t G = K / 32;
     const int tid = threadIdx.x;
     __shared__ float red[kPrepThreads / 64];
-    const int64_t m = blockIdx.x;
     const bool live = m < M;
     const g_f4 row = (g_f4)(x_g + (live ? m : 0) * K);
     const int64_t items = G * 4;                       // item (g, q): weights 4q.. and 16+4q.. of group g
@@ -183,6 +188,30 @@ __global__ __launch_bounds__(kPrepThreads) void sign_split_kernel(const float *x
             }
             emit(it, a, b);
         }
+    }
+}
+
+__global__ __launch_bounds__(kPrepThreads) void sign_split_kernel(const float *x_g, int64_t M, int64_t K,
+                                                                  uint32_t *__restrict__ xs,
+                                                                  int32_t *__restrict__ rexp) {
+    split_row(x_g, M, K, xs, rexp, blockIdx.x);
+}
+
+// Both per-call preparations in one launch (they are independent): the first
+// n_split workgroups split one padded row of x each, the rest regroup one
+// 64 x 32 tile of the weights each (tile index = blockIdx.x - n_split, rows
+// fastest), so the two run side by side instead of one after the other.
+__global__ __launch_bounds__(kPrepThreads) void sign_prep_kernel(const float *x_g, int64_t M, int64_t K,
+                                                                 uint32_t *__restrict__ xs, int32_t *__restrict__ rexp,
+                                                                 int64_t n_split, const uint32_t *bits_g,
+                                                                 const float *scales_g, int64_t N,
+                                                                 u32x4 *__restrict__ wv, int64_t wpack_x) {
+    const int64_t b = blockIdx.x;
+    if (b < n_split) {
+        split_row(x_g, M, K, xs, rexp, b);
+    } else {
+        const int64_t t = b - n_split;
+        wpack_tile(bits_g, scales_g, N, K / 32, wv, t % wpack_x, t / wpack_x);
     }
 }
 
@@ -413,7 +442,7 @@ int packed_size(int64_t N, int64_t K, int64_t *bytes) {
 
 // Launches split + GEMM against weights already in the packed layout.
 int split_and_gemm(const float *x, const u32x4 *wv, float *y, int64_t M, int64_t N, int64_t K, void *workspace,
-                   hipStream_t s, const char *who) {
+                   hipStream_t s, const char *who, bool split_done = false) {
     const int64_t G = K / 32;
     const int64_t m16 = (M + 15) / 16;
     uint32_t *xs = static_cast<uint32_t *>(workspace);
@@ -422,8 +451,9 @@ int split_and_gemm(const float *x, const u32x4 *wv, float *y, int64_t M, int64_t
     const int64_t tiles = tiles_m * tiles_n;
     const int64_t per_xcd = (tiles + 7) / 8;
     GD_REQUIRE(per_xcd * 8 <= INT64_C(0xffffffff), GD_ERANGE, "%s: grid too large", who);
-    hipLaunchKernelGGL(sign_split_kernel, dim3(static_cast<uint32_t>(m16 * 16)), dim3(kPrepThreads), 0, s, x, M, K,
-                       xs, rexp);
+    if (!split_done)
+        hipLaunchKernelGGL(sign_split_kernel, dim3(static_cast<uint32_t>(m16 * 16)), dim3(kPrepThreads), 0, s, x, M,
+                           K, xs, rexp);
     hipLaunchKernelGGL(sign_gemm_kernel, dim3(static_cast<uint32_t>(per_xcd * 8)), dim3(kThreads), 0, s, xs, rexp,
                        wv, y, M, N, G, tiles_n, tiles, per_xcd);
     return check_launch(who);
@@ -497,8 +527,12 @@ extern "C" int q1_sign_gemm(const float *x, const uint32_t *w_bits, const float 
     u32x4 *wv = reinterpret_cast<u32x4 *>(static_cast<char *>(workspace) + m16 * 16 * K * 4 + m16 * 16 * 4);
     const int64_t wpack_x = (N + kPackRows - 1) / kPackRows, wpack_y = (G + kPackGroups - 1) / kPackGroups;
     GD_REQUIRE(wpack_x <= INT64_C(0xffffffff) && wpack_y <= 65535, GD_ERANGE, "q1_sign_gemm: grid too large");
+    const int64_t n_prep = m16 * 16 + wpack_x * wpack_y;
+    GD_REQUIRE(n_prep <= INT64_C(0xffffffff), GD_ERANGE, "q1_sign_gemm: grid too large");
     hipStream_t s = as_stream(stream);
-    hipLaunchKernelGGL(sign_wpack_kernel, dim3(static_cast<uint32_t>(wpack_x), static_cast<uint32_t>(wpack_y)),
-                       dim3(kPrepThreads), 0, s, w_bits, w_scales, N, G, wv);
-    return split_and_gemm(x, wv, y, M, N, K, workspace, s, "q1_sign_gemm");
+    uint32_t *xs = static_cast<uint32_t *>(workspace);
+    int32_t *rexp = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + m16 * 16 * K * 4);
+    hipLaunchKernelGGL(sign_prep_kernel, dim3(static_cast<uint32_t>(n_prep)), dim3(kPrepThreads), 0, s, x, M, K, xs,
+                       rexp, m16 * 16, w_bits, w_scales, N, wv, wpack_x);
+    return split_and_gemm(x, wv, y, M, N, K, workspace, s, "q1_sign_gemm", true);
 }
