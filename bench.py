@@ -1014,8 +1014,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures one GPU only (the kernels run on one MI355X; "
-              "multi-GPU sharding is a design note, not built) -- run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: the library runs each product on one MI355X, and sharding "
+              "across GPUs is described, not implemented -- run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
