@@ -43,11 +43,11 @@ METRIC = "Q1_0·q8_0 GEMV effective HBM GB/s (% of peak) + equiv tok/s, batch 1"
 # the kernel source they were measured on: reported only while its hash
 # matches, null after any change to it.
 _TRAFFIC = {
-    "q1": ("q1.hip", "4ab4ceb2cc1b3d51", {"step": (167498.2, 2304.0)}),
-    "q1_small": ("q1.hip", "4ab4ceb2cc1b3d51", {"7646 x 256x1024": (139144.0, 7646.0)}),
+    "q1": ("q1.hip", "d26001046218be80", {"step": (167527.9, 2304.0)}),
+    "q1_small": ("q1.hip", "d26001046218be80", {"7646 x 256x1024": (139143.5, 7646.0)}),
     "ternary": ("ternary.hip", "8f60006b03cd5750",
-                {"2560x2560": (102238.1, 1200.0), "6912x2560": (137605.3, 1620.1), "2560x6912": (65779.3, 300.0)}),
-    "blockq8": ("blockq8.hip", "123bb6b095593ab2", {"m1": (26541.1, 192.4), "m16": (27466.7, 3072.0)}),
+                {"2560x2560": (101998.1, 1200.0), "6912x2560": (137366.5, 1620.1), "2560x6912": (65806.6, 300.0)}),
+    "blockq8": ("blockq8.hip", "123bb6b095593ab2", {"m1": (26534.5, 192.4), "m16": (27477.1, 3072.0)}),
     "sign": ("sign_gemm.hip", "8079002f8fe77553",
              {"prep": (6201.5, 12304.0), "gemm": (21352.5, 9728.0)}),
     "sign_lut": ("sign_lut.hip", "c9273fa6aeb445b1",
@@ -55,7 +55,7 @@ _TRAFFIC = {
     "quant": ("quantize.hip", "aa440e939b0b9a5a",
               {"q8_0_decode": (266.5, 136.0), "q8_0_batch_256MiB": (131082.5, 69632.0),
                "int8_planes_decode_step": (522.6 + 536.5, 227.8 + 203.4),
-               "int8_planes_batch_256MiB": (131147.5, 66073.1)}),
+               "int8_planes_batch_256MiB": (131147.4, 66074.8)}),
     # per call: split kernel + merge kernel
     "attention": ("attention.hip", "90a47144e8c51bc0",
                   {"kv4096": (16453.5 + 605.0, 1040.0 + 16.0),
@@ -66,8 +66,8 @@ _TRAFFIC = {
 # Hardware MFMA busy fraction (rocprofv3 SQ_VALU_MFMA_BUSY_CYCLES over the
 # dispatch's duration x 1024 SIMDs at 2.4 GHz), for the kernel source measured.
 _MFMA_BUSY = {
-    "sign_gemm_kernel": ("sign_gemm.hip", "8079002f8fe77553", 0.293),
-    "blockq8_mfma_kernel": ("blockq8.hip", "123bb6b095593ab2", 0.087),
+    "sign_gemm_kernel": ("sign_gemm.hip", "8079002f8fe77553", 0.286),
+    "blockq8_mfma_kernel": ("blockq8.hip", "123bb6b095593ab2", 0.086),
 }
 
 

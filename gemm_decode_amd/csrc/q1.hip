@@ -140,35 +140,38 @@ __device__ __forceinline__ void table_loads(TableRawN<NT> &raw, const uint16_t *
 // Entries: T[0] = d1*s(0) and T[n] = T[n without its lowest set bit] +
 // d1*delta(lowest bit). Every partial value is d1 times an integer of
 // magnitude <= 512, so each add is exact and T[n] = d1*s(n) bit for bit.
+// One group's 16 entries from its raw halves (d1, quants 0-1, quants 2-3).
+__device__ __forceinline__ void table_group(float *dst_g, uint32_t rd, uint32_t rq01, uint32_t rq23) {
+    const float d1 = f16_to_f32(static_cast<uint16_t>(rd));
+    const int32_t q[4] = {static_cast<int8_t>(rq01 & 0xff), static_cast<int8_t>(rq01 >> 8),
+                          static_cast<int8_t>(rq23 & 0xff), static_cast<int8_t>(rq23 >> 8)};
+    int32_t base = 0;
+    float dlt[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; jj++) {
+        const int32_t neg = (q[jj] == -128) ? -128 : -q[jj];   // int8 wrapping negation
+        base += neg;
+        dlt[jj] = d1 * static_cast<float>(q[jj] - neg);         // exact: |q - neg| <= 255
+    }
+    float v[16];
+    v[0] = d1 * static_cast<float>(base);                        // exact: |base| <= 512
+#pragma unroll
+    for (int n = 1; n < 16; n++) {
+        const int low = __builtin_ctz(n);
+        v[n] = v[n & (n - 1)] + dlt[low];
+    }
+    float4 *dst = reinterpret_cast<float4 *>(dst_g);
+#pragma unroll
+    for (int m = 0; m < 4; m++) dst[m] = make_float4(v[4 * m], v[4 * m + 1], v[4 * m + 2], v[4 * m + 3]);
+}
+
 template <int NT = kThreads>
 __device__ __forceinline__ void table_store(float *tab, const TableRawN<NT> &raw, int cb) {
     const int ng = cb * 32;
 #pragma unroll
     for (int j = 0; j < TableRawN<NT>::NG; j++) {
         const int g = threadIdx.x + NT * j;
-        const float d1 = f16_to_f32(static_cast<uint16_t>(raw.d[j]));
-        const int32_t q[4] = {static_cast<int8_t>(raw.q01[j] & 0xff), static_cast<int8_t>(raw.q01[j] >> 8),
-                              static_cast<int8_t>(raw.q23[j] & 0xff), static_cast<int8_t>(raw.q23[j] >> 8)};
-        int32_t base = 0;
-        float dlt[4];
-#pragma unroll
-        for (int jj = 0; jj < 4; jj++) {
-            const int32_t neg = (q[jj] == -128) ? -128 : -q[jj];   // int8 wrapping negation
-            base += neg;
-            dlt[jj] = d1 * static_cast<float>(q[jj] - neg);         // exact: |q - neg| <= 255
-        }
-        float v[16];
-        v[0] = d1 * static_cast<float>(base);                        // exact: |base| <= 512
-#pragma unroll
-        for (int n = 1; n < 16; n++) {
-            const int low = __builtin_ctz(n);
-            v[n] = v[n & (n - 1)] + dlt[low];
-        }
-        if (g < ng) {
-            float4 *dst = reinterpret_cast<float4 *>(tab + g * 16);
-#pragma unroll
-            for (int m = 0; m < 4; m++) dst[m] = make_float4(v[4 * m], v[4 * m + 1], v[4 * m + 2], v[4 * m + 3]);
-        }
+        if (g < ng) table_group(tab + g * 16, raw.d[j], raw.q01[j], raw.q23[j]);
     }
 }
 
@@ -470,27 +473,8 @@ __global__ __launch_bounds__(NT) void q1_gemv_grouped_small_kernel(const gd_q1_p
         for (int u = 0; u < kSmallBlocks; u++) wb[u] = rp.bits[(u < nb ? u : nb - 1) * 128];
         s8 = rp.sc[0];
     }
-    // 3. the table: T[n] for group g (see table_store)
-    if (static_cast<int>(threadIdx.x) < ng) {
-        const float d1 = f16_to_f32(static_cast<uint16_t>(rd));
-        const int32_t q[4] = {static_cast<int8_t>(rq01 & 0xff), static_cast<int8_t>(rq01 >> 8),
-                              static_cast<int8_t>(rq23 & 0xff), static_cast<int8_t>(rq23 >> 8)};
-        int32_t base = 0;
-        float dlt[4];
-#pragma unroll
-        for (int jj = 0; jj < 4; jj++) {
-            const int32_t neg = (q[jj] == -128) ? -128 : -q[jj];   // int8 wrapping negation
-            base += neg;
-            dlt[jj] = d1 * static_cast<float>(q[jj] - neg);         // exact: |q - neg| <= 255
-        }
-        float v[16];
-        v[0] = d1 * static_cast<float>(base);                        // exact: |base| <= 512
-#pragma unroll
-        for (int n = 1; n < 16; n++) v[n] = v[n & (n - 1)] + dlt[__builtin_ctz(n)];
-        float4 *dst = reinterpret_cast<float4 *>(tab + threadIdx.x * 16);
-#pragma unroll
-        for (int m = 0; m < 4; m++) dst[m] = make_float4(v[4 * m], v[4 * m + 1], v[4 * m + 2], v[4 * m + 3]);
-    }
+    // 3. the table
+    if (static_cast<int>(threadIdx.x) < ng) table_group(tab + threadIdx.x * 16, rd, rq01, rq23);
     __syncthreads();
     // 4. the blocks, in order
     const char *tabc = reinterpret_cast<const char *>(tab);
