@@ -90,10 +90,11 @@ __global__ __launch_bounds__(kThreads) void blockq8_valu_kernel(const float *__r
 // ---------------------------------------------------------------- m = 1
 // Decode GEMV (one activation row). Thirty-two lanes share an output
 // feature; lane j owns chunks c = j + 32t (t < kCPL) of 16 quants, the same
-// positions in every row, so its slice of x (up to 32 floats) and each
-// chunk's sum of x stay in registers for all its rows. Quant bytes are
-// read as unsigned u = q + 128 (q xor 0x80, then v_cvt_f32_ubyte) and the
-// bias is removed once per chunk: sum x*q = sum x*u - 128*sum x. x is read
+// positions in every row, so its slice of x (up to 32 floats) stays in
+// registers for all its rows. Each quant byte is
+// converted sign-extended (one v_cvt_f32_i32 with an SDWA byte select and
+// sext, as the page's quant_at reads it) and multiplied into the chunk's
+// sum, so the f32 error follows sum |x*q| whatever the mean of x. x is read
 // from HBM once per workgroup into LDS. A wave covers two rows per step and
 // keeps the loads of the next three steps in flight (four register sets
 // rotated by name).
@@ -151,21 +152,17 @@ __global__ __launch_bounds__(kGemvThreads) void blockq8_gemv_kernel(const float 
     load(2, b2);
     __syncthreads();
 
-    float xv[kCPL][16], xs[kCPL];
+    float xv[kCPL][16];
 #pragma unroll
     for (int t = 0; t < kCPL; t++) {
         const int c = lane + kLPR * t;
         const int cc = c < chunks ? c : chunks - 1;
         const float keep = c < chunks ? 1.0f : 0.0f;
-        xs[t] = 0.0f;
 #pragma unroll
         for (int v = 0; v < 4; v++) {
             const f32x4 w = xl[cc * 4 + v];
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-                xv[t][4 * v + e] = w[e] * keep;
-                xs[t] += xv[t][4 * v + e];
-            }
+            for (int e = 0; e < 4; e++) xv[t][4 * v + e] = w[e] * keep;
         }
     }
     auto row_dot = [&](const RowBuf &b) {
@@ -175,13 +172,12 @@ __global__ __launch_bounds__(kGemvThreads) void blockq8_gemv_kernel(const float 
             float s = 0.0f;
 #pragma unroll
             for (int wq = 0; wq < 4; wq++) {
-                const uint32_t u = b.q[t][wq] ^ 0x80808080u;    // q + 128 per byte
-                s = __builtin_fmaf(xv[t][4 * wq + 0], static_cast<float>(u & 0xffu), s);
-                s = __builtin_fmaf(xv[t][4 * wq + 1], static_cast<float>((u >> 8) & 0xffu), s);
-                s = __builtin_fmaf(xv[t][4 * wq + 2], static_cast<float>((u >> 16) & 0xffu), s);
-                s = __builtin_fmaf(xv[t][4 * wq + 3], static_cast<float>(u >> 24), s);
+                const uint32_t w = b.q[t][wq];
+                s = __builtin_fmaf(xv[t][4 * wq + 0], sbyte(w, 0), s);
+                s = __builtin_fmaf(xv[t][4 * wq + 1], sbyte(w, 1), s);
+                s = __builtin_fmaf(xv[t][4 * wq + 2], sbyte(w, 2), s);
+                s = __builtin_fmaf(xv[t][4 * wq + 3], sbyte(w, 3), s);
             }
-            s = __builtin_fmaf(-128.0f, xs[t], s);
             acc = __builtin_fmaf(b.s[t], s, acc);
         }
         acc += __shfl_xor(acc, 1, kLPR);
