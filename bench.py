@@ -143,6 +143,23 @@ def cpu_model() -> str:
 
 # --------------------------------------------------------- Q1 workload
 
+def q1_step_problems(gd, shapes, copies, a_dev, ys):
+    """The decode step's problems in the order of its one grouped launch:
+    shapes by increasing row count (the longer problems' work then fills the
+    launch's tail), activation vector c against each. copies[si][c] are the
+    (bits, scales) planes of problem (shape si, vector c), ys[si][c] its
+    output; each problem carries its own row count."""
+    order = sorted(range(len(shapes)), key=lambda si: shapes[si].rows)
+    return gd.make_q1_problems([(copies[si][c][0], copies[si][c][1], a_dev[c], ys[si][c], shapes[si].rows)
+                                for si in order for c in range(len(a_dev))])
+
+
+def q1_step_launch(gd, problems, shapes, n_vec):
+    """One decode step: its len(shapes) * n_vec problems in one grouped
+    launch, the launch's rows the largest problem's."""
+    gd.q1_q8_gemv_grouped(problems, len(shapes) * n_vec, max(s.rows for s in shapes), shapes[0].K)
+
+
 def bench_q1(args, gd, torch):
     shapes = wl.Q1_DECODE
     K = shapes[0].K
@@ -170,19 +187,14 @@ def bench_q1(args, gd, torch):
     # one grouped launch: each problem carries its own row count, the launch
     # the largest; the shorter problems come first, so the longer ones' work
     # fills the launch's tail
-    max_rows = max(s.rows for s in shapes)
-    n_prob = len(shapes) * n_vec
     slots = []
     for r in range(ring):
         copies = [[(base[si][0].clone(), base[si][1].clone()) for _ in range(n_vec)] for si in range(len(shapes))]
-        order = sorted(range(len(shapes)), key=lambda si: shapes[si].rows)
-        probs = gd.make_q1_problems([(copies[si][c][0], copies[si][c][1], a_dev[c], ys[si][c], shapes[si].rows)
-                                     for si in order for c in range(n_vec)])
-        slots.append({"step": probs, "copies": copies})
+        slots.append({"step": q1_step_problems(gd, shapes, copies, a_dev, ys), "copies": copies})
     torch.cuda.synchronize()
 
     def step(r):
-        gd.q1_q8_gemv_grouped(slots[r]["step"], n_prob, max_rows, K)
+        q1_step_launch(gd, slots[r]["step"], shapes, n_vec)
 
     # parity spot check (untimed): every output of the first ring slot
     step(0)

@@ -67,6 +67,7 @@ def tol(q, k, scale, Hkv):
     (64, 8, 2049, 0),      # groups of 8
     (32, 8, 300, 64),      # more splits than keys allow: trailing splits empty
     (32, 8, 5000, 1),      # one split over every tile
+    (32, 8, 32768, 0),     # the long-context decode shape the benchmark times
 ])
 def test_parity(gd, Hq, Hkv, L, splits):
     q, k, v = inputs(Hq, Hkv, L, L, seed=Hq + L + splits)

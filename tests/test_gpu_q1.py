@@ -223,6 +223,34 @@ def test_decode_shapes_grouped_full(gd, idx):
     assert_bits_equal(y.cpu().numpy().reshape(n, rows), want, "n_act=32")
 
 
+def test_decode_step_as_benchmarked(gd):
+    """The decode step exactly as the benchmark builds and launches it: 32
+    activation vectors against 4096x4096 and 14336x4096 (K = 4096), the 64
+    problems in ONE grouped launch, each with its own copy of the planes and
+    its own row count, the launch's rows 14336. Every output of all 64
+    problems bit-exact with the oracle, and nothing written past a
+    problem's rows."""
+    import bench
+    shapes = wl.Q1_DECODE
+    K, n = shapes[0].K, len(shapes[0].act_seeds)
+    Ws = [wl.q1_weights_aos(s.rows, s.K, s.weight_seed) for s in shapes]
+    A = np.concatenate([wl.q8_acts_aos(K, sd) for sd in shapes[0].act_seeds])
+    a_dev = [dev(A[c]) for c in range(n)]
+    base = [planes_on_gpu(gd, W, s.rows, K) for s, W in zip(shapes, Ws)]
+    copies = [[(b.clone(), sc.clone()) for _ in range(n)] for (b, sc) in base]
+    guard = 64
+    bufs = [[torch.full((s.rows + guard,), float("nan"), device="cuda") for _ in range(n)] for s in shapes]
+    ys = [[bufs[si][c][:s.rows] for c in range(n)] for si, s in enumerate(shapes)]
+    probs = bench.q1_step_problems(gd, shapes, copies, a_dev, ys)
+    bench.q1_step_launch(gd, probs, shapes, n)
+    torch.cuda.synchronize()
+    for si, (s, W) in enumerate(zip(shapes, Ws)):
+        got = np.stack([bufs[si][c].cpu().numpy() for c in range(n)])
+        want = oracle.q1_q8_gemv_aos(W, A, s.rows, K, n_act=n, nthreads=oracle.max_threads())
+        assert_bits_equal(got[:, :s.rows], want.reshape(n, s.rows), f"decode step {s.rows}x{K}")
+        assert np.all(np.isnan(got[:, s.rows:])), f"{s.rows}x{K}: wrote past a problem's rows"
+
+
 def test_deterministic_repeat(gd):
     rows, K = 4096, 4096
     W = wl.q1_weights_aos(rows, K, 1)
