@@ -4,18 +4,25 @@
 Default workload (the headline metric): Q1_0.q8_0 GEMV at 8B-class decode
 shapes, batch 1 -- weights 4096x4096 and 14336x4096 (K=4096), each applied to
 32 seeded q8_0 activation vectors as separate batch-1 GEMVs. One step is those
-64 GEMVs, run as two grouped launches (one per weight shape, 32 independent
-problems each). Every problem reads its own copy of the repacked weight
+64 GEMVs, run as ONE grouped launch (64 independent problems, each with its
+own row count). Every problem reads its own copy of the repacked weight
 planes, and successive steps rotate through a ring of copies totalling more
 than 1 GiB, so no weight byte is served from cache (MI355X has a 256 MB
 last-level cache): each step streams 342 MB of algorithmic bytes from HBM.
 
-Printed: one JSON line with the metric, the roofline of the dominant kernel
-(algorithmic bytes per launch / mean launch time from HIP events on the
-launch stream) and the CPU oracle timed on a bounded sample of the same
-workload on the host.
+Timing: after the warmup, R batches (--batches) of exactly K steps
+(--steps), each batch between two HIP events on the launch stream with a
+device synchronisation on both sides; the reported value and ms_per_step
+come from the median batch (min and max are printed beside it). The other
+paths are timed the same way: R batches of graph replays, median.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload q1]
+Printed: ONE compact JSON line on stdout (the metric, the roofline of the
+dominant kernel, the CPU oracle timed on a bounded sample of the same
+workload, and one short entry per other path under "workloads"); the full
+record, with the samples' descriptions, goes to stderr and to --detail-out.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--batches R]
+                       [--workload all|q1|...]
 """
 from __future__ import annotations
 
@@ -34,14 +41,19 @@ if ROOT not in sys.path:
 import workloads as wl  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0          # MI355X published HBM3E bandwidth, decimal GB/s
+MFMA_F16_PEAK_TFLOPS = 2500.0    # MI355X dense fp16 matrix peak
 MODEL_8B_Q1_BYTES = 8e9 * 18 / 128   # 8B weights at 18 bytes per 128 -> bytes per token
 METRIC = "Q1_0·q8_0 GEMV effective HBM GB/s (% of peak) + equiv tok/s, batch 1"
+TRAFFIC_SOURCE = ("copied from profiles/hbm_traffic_all_paths.md: rocprofv3 --pmc FETCH_SIZE then WRITE_SIZE "
+                  "on this kernel source, scaled by a streaming read and a fill of known size")
+MIN_SPIN_S = 0.1       # sustained load before each short-kernel timing
+MIN_BATCH_S = 0.02     # GPU time per timed batch of the other paths
 
 
 # HBM bytes per launch from rocprofv3 counters (2 x FETCH_SIZE + WRITE_SIZE,
-# the factors read off a streaming read and a fill of known size), valid for
-# the kernel source they were measured on: reported only while its hash
-# matches, null after any change to it.
+# in KiB, the factors read off a streaming read and a fill of known size),
+# valid for the kernel source they were measured on: reported only while its
+# hash matches, null after any change to it.
 _TRAFFIC = {
     "q1": ("q1.hip", "d26001046218be80", {"step": (167527.9, 2304.0)}),
     "q1_small": ("q1.hip", "d26001046218be80", {"7646 x 256x1024": (139143.5, 7646.0)}),
@@ -62,7 +74,6 @@ _TRAFFIC = {
                    "kv32768": (131141.5 + 605.0, 1040.0 + 16.0)}),
 }
 
-
 # Hardware MFMA busy fraction (rocprofv3 SQ_VALU_MFMA_BUSY_CYCLES over the
 # dispatch's duration x 1024 SIMDs at 2.4 GHz), for the kernel source measured.
 _MFMA_BUSY = {
@@ -71,22 +82,24 @@ _MFMA_BUSY = {
 }
 
 
+def _src_sha(src: str) -> str:
+    import hashlib
+    with open(os.path.join(ROOT, "gemm_decode_amd", "csrc", src), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
 def measured_mfma_busy(kernel: str):
     """The counter-measured MFMA busy fraction of a kernel, or None if its
     source has changed since."""
-    import hashlib
     src, sha, frac = _MFMA_BUSY[kernel]
-    with open(os.path.join(ROOT, "gemm_decode_amd", "csrc", src), "rb") as f:
-        return frac if hashlib.sha256(f.read()).hexdigest()[:16] == sha else None
+    return frac if _src_sha(src) == sha else None
 
 
 def measured_traffic(path: str):
     """{launch: HBM bytes} for one path, or None if its source has changed."""
-    import hashlib
     src, sha, launches = _TRAFFIC[path]
-    with open(os.path.join(ROOT, "gemm_decode_amd", "csrc", src), "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest()[:16] != sha:
-            return None
+    if _src_sha(src) != sha:
+        return None
     return {k: int(round((2.0 * fetch + write) * 1024)) for k, (fetch, write) in launches.items()}
 
 
@@ -100,7 +113,105 @@ def q1_gemv_bytes(rows: int, K: int) -> int:
     return rows * (K // 128) * 18 + (K // 32) * 34 + rows * 4
 
 
-# ----------------------------------------------------------------- helpers
+def _r(v, nd=2):
+    return None if v is None else round(float(v), nd)
+
+
+def roofline(achieved, peak, unit, bound, traffic=None, **extra):
+    out = {"bound": bound, "achieved": _r(achieved, 2), "peak": peak, "unit": unit,
+           "frac": _r(achieved / peak, 4), "traffic": traffic}
+    out.update(extra)
+    return out
+
+
+def compact(full: dict) -> dict:
+    """The short form of one path's record for the stdout line: value, unit,
+    time, roofline fraction, traffic, parity, CPU baseline."""
+    rf = full.get("roofline") or {}
+    cpu = full.get("cpu_baseline") or {}
+    out = {"value": full.get("value"), "unit": full.get("unit"), "us": full.get("us"),
+           "bound": rf.get("bound"), "frac": rf.get("frac"), "traffic": rf.get("traffic")}
+    if rf.get("mfma_busy_hw") is not None:
+        out["mfma_busy_hw"] = rf["mfma_busy_hw"]
+    for k in ("parity_mismatches", "parity_rel_err"):
+        if k in full:
+            out[k] = full[k]
+    if cpu:
+        out["cpu"] = {"value": cpu.get("value"), "unit": cpu.get("unit"), "cores": cpu.get("cores")}
+    for k in ("spread_us", "extra"):
+        if k in full:
+            out[k] = full[k]
+    return out
+
+
+# ----------------------------------------------------------------- timing
+
+def _events(torch):
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def spin_up(torch, run, n_min, min_s):
+    """Runs run(n_min), then run(n_min) again until at least min_s seconds of
+    GPU work have passed; returns the number of run() units done (untimed)."""
+    done = 0
+    t = time.perf_counter()
+    while True:
+        run(n_min)
+        torch.cuda.synchronize()
+        done += n_min
+        if time.perf_counter() - t >= min_s:
+            return done
+
+
+def time_batches(torch, run_batch, units, batches):
+    """Seconds per unit of `batches` timed batches: each batch is run_batch()
+    (which enqueues `units` units of work on the current stream) between two
+    HIP events on that stream, with a device synchronisation on both sides.
+    Returns (median, min, max, all) in seconds per unit."""
+    per = []
+    for _ in range(batches):
+        torch.cuda.synchronize()
+        e0, e1 = _events(torch)
+        e0.record()
+        run_batch()
+        e1.record()
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1) / 1e3 / units)
+    arr = np.array(per)
+    return float(np.median(arr)), float(arr.min()), float(arr.max()), per
+
+
+def _time_launches(torch, launch, n, warmup, batches):
+    """Per-launch time of n launches captured in one HIP graph (replayed on
+    the launch stream, so the launches run back to back whatever the host's
+    launch rate). The graph is replayed untimed for MIN_SPIN_S first (the
+    clocks leave idle); then `batches` timed batches, each of as many
+    replays as make up MIN_BATCH_S of GPU time. Returns (median s per launch,
+    {"min_us", "max_us", "batches", "launches_per_batch"})."""
+    for w in range(warmup):
+        launch(w)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+        for k in range(n):
+            launch(warmup + k)
+    spin_up(torch, lambda _n: g.replay(), 1, MIN_SPIN_S)
+    e0, e1 = _events(torch)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    one = e0.elapsed_time(e1) / 1e3
+    reps = max(1, int(np.ceil(MIN_BATCH_S / max(one, 1e-7))))
+
+    def batch():
+        for _ in range(reps):
+            g.replay()
+    med, lo, hi, _ = time_batches(torch, batch, reps * n, batches)
+    del g
+    return med, {"min_us": _r(lo * 1e6, 3), "max_us": _r(hi * 1e6, 3), "batches": batches,
+                 "launches_per_batch": reps * n}
+
 
 def measured_read_ceiling(gd, torch, gib: float = 2.0, passes: int = 8, reps: int = 5):
     """Streaming-read ceiling (page "roofline.html" method): fill a buffer far
@@ -113,8 +224,7 @@ def measured_read_ceiling(gd, torch, gib: float = 2.0, passes: int = 8, reps: in
     gd.gemm_decode_stream_read(buf, 2, sink)   # warm-up
     best = float("inf")
     for _ in range(reps):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
+        e0, e1 = _events(torch)
         e0.record()
         gd.gemm_decode_stream_read(buf, passes, sink)
         e1.record()
@@ -183,10 +293,6 @@ def bench_q1(args, gd, torch):
         gd.q1_repack(torch.from_numpy(W.reshape(-1)).cuda(), s.rows, s.K, b, sc)
         base.append((b, sc))
     ys = [[torch.empty(s.rows, dtype=torch.float32, device="cuda") for _ in range(n_vec)] for s in shapes]
-    # slots[r]: the step's 64 problems over the r-th set of plane copies, in
-    # one grouped launch: each problem carries its own row count, the launch
-    # the largest; the shorter problems come first, so the longer ones' work
-    # fills the launch's tail
     slots = []
     for r in range(ring):
         copies = [[(base[si][0].clone(), base[si][1].clone()) for _ in range(n_vec)] for si in range(len(shapes))]
@@ -196,7 +302,7 @@ def bench_q1(args, gd, torch):
     def step(r):
         q1_step_launch(gd, slots[r]["step"], shapes, n_vec)
 
-    # parity spot check (untimed): every output of the first ring slot
+    # parity check (untimed): every output of the first ring slot
     step(0)
     torch.cuda.synchronize()
     mism = None
@@ -226,53 +332,31 @@ def bench_q1(args, gd, torch):
         slot_graphs = [capture(lambda r=r: step(r)) for r in range(ring)]
         torch.cuda.synchronize()
 
+    pos = [0]   # ring position, carried across batches
+
     def run_steps(n):
         if not args.graph:
-            for k in range(n):
-                step(k % ring)
+            for _ in range(n):
+                step(pos[0] % ring)
+                pos[0] += 1
             return
         for _ in range(n // ring):
             ring_graph.replay()
-        for r in range(n % ring):
-            slot_graphs[r].replay()
+        for _ in range(n % ring):
+            slot_graphs[pos[0] % ring].replay()
+            pos[0] += 1
 
     # Untimed warmup: at least W steps, and at least --min-warmup-s of
     # sustained load (the clocks take tens of milliseconds to ramp from idle;
     # a warmup of a few steps would time that ramp).
     warm_steps = spin_up(torch, run_steps, max(args.warmup, ring), args.min_warmup_s)
 
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    # R batches of exactly K steps; the median batch is the result.
     wall0 = time.perf_counter()
-    t0.record()
-    run_steps(args.steps)
-    t1.record()
-    torch.cuda.synchronize()
+    med, lo, hi, per_batch = time_batches(torch, lambda: run_steps(args.steps), args.steps, args.batches)
     wall = time.perf_counter() - wall0
-    total_s = t0.elapsed_time(t1) / 1e3
-
-    # Roofline: mean duration of the step's grouped kernel, from HIP events
-    # on the launch stream around `reps` back-to-back launches (ring slots in
-    # turn), after the same number untimed.
-    reps = 8 * ring
-
-    def timed(fn):
-        fn()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        fn()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / 1e3 / reps
-
-    kern_s = timed(lambda: [step(j % ring) for j in range(reps)])
+    gbps = step_bytes / med / 1e9
     q1_traffic = measured_traffic("q1")
-    achieved = step_bytes / kern_s / 1e9
-
-    gbps = step_bytes * args.steps / total_s / 1e9
-    ms_per_step = total_s / args.steps * 1e3
 
     # serial mode: one launch per GEMV (the decode schedule), the step's 64
     # launches captured in a HIP graph per ring slot and replayed back to back
@@ -292,18 +376,18 @@ def bench_q1(args, gd, torch):
                 one_step(r)
             sgraphs.append(g)
         spin_up(torch, lambda n: [sgraphs[k % ring].replay() for k in range(n)], ring, MIN_SPIN_S)
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for k in range(args.serial_steps):
-            sgraphs[k % ring].replay()
-        e1.record()
-        torch.cuda.synchronize()
-        ser_s = e0.elapsed_time(e1) / 1e3
-        serial = {"GBps": round(step_bytes * args.serial_steps / ser_s / 1e9, 1),
-                  "us_per_gemv": round(ser_s / (args.serial_steps * 2 * n_vec) * 1e6, 3),
-                  "launches": args.serial_steps * 2 * n_vec,
-                  "timing": "one HIP graph of the step's 64 single-GEMV launches per ring slot"}
+        spos = [0]
+
+        def sbatch():
+            for _ in range(args.serial_steps):
+                sgraphs[spos[0] % ring].replay()
+                spos[0] += 1
+        smed, slo, shi, _ = time_batches(torch, sbatch, args.serial_steps, args.batches)
+        serial = {"value": _r(step_bytes / smed / 1e9, 1), "unit": "GB/s",
+                  "us_per_gemv": _r(smed / (2 * n_vec) * 1e6, 3),
+                  "us_per_gemv_min_max": [_r(slo / (2 * n_vec) * 1e6, 3), _r(shi / (2 * n_vec) * 1e6, 3)],
+                  "timing": f"one HIP graph of the step's 64 single-GEMV launches per ring slot; "
+                            f"median of {args.batches} batches of {args.serial_steps} steps"}
         del sgraphs
 
     ceiling = (measured_read_ceiling(gd, torch, gib=args.ceiling_gib, passes=args.ceiling_passes,
@@ -315,14 +399,12 @@ def bench_q1(args, gd, torch):
 
     out = {
         "metric": METRIC,
-        "value": round(gbps, 1),
+        "value": _r(gbps, 1),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "warmup_note": f"{warm_steps} untimed steps ran (at least --warmup, and at least "
-                       f"{args.min_warmup_s} s of sustained load) before the {args.steps} timed ones",
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": _r(med * 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -330,32 +412,34 @@ def bench_q1(args, gd, torch):
         "data": "synthetic",
         "config": {
             "workload": "Q1_0.q8_0 GEMV batch 1: 32 activation vectors x {4096x4096, 14336x4096}, "
-                        "K=4096, 64 independent GEMVs per step in one grouped launch (per-problem rows), "
+                        "K=4096, 64 independent GEMVs per step in one grouped launch, "
                         "distinct weight copies (ring > 1 GiB)",
-            "rows": [s.rows for s in shapes], "K": K, "activation_vectors": n_vec,
             "step_bytes": step_bytes, "ring_sets": ring,
             "timed_as": (f"HIP graph replays ({ring} steps per graph)" if args.graph
-                         else "launches queued back to back, events only at the ends"),
+                         else "launches queued back to back, events only at a batch's ends"),
         },
-        "pct_of_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
-        "equiv_tok_s": round(gbps * 1e9 / MODEL_8B_Q1_BYTES, 1),
-        "rows_K_per_s": round(sum(n_vec * s.rows * s.K for s in shapes) * args.steps / total_s, 1),
-        "roofline": {
-            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None if q1_traffic is None else sum(q1_traffic.values()),
-            "traffic_per_launch": q1_traffic,
-            "kernel": "q1_gemv_grouped_kernel (one launch per step, 64 problems)",
-            "us_per_launch": round(kern_s * 1e6, 2),
-            "bytes_per_launch": step_bytes,
-            "timing": f"HIP events around {reps} back-to-back launches",
-        },
+        "batches": {"n": args.batches, "steps_each": args.steps, "ms_per_step_median": _r(med * 1e3, 5),
+                    "ms_per_step_min": _r(lo * 1e3, 5), "ms_per_step_max": _r(hi * 1e3, 5),
+                    "GBps_min_max": [_r(step_bytes / hi / 1e9, 1), _r(step_bytes / lo / 1e9, 1)]},
+        "warmup_steps_run": warm_steps,
+        "pct_of_peak": _r(100 * gbps / HBM_PEAK_GBPS, 2),
+        "equiv_tok_s": _r(gbps * 1e9 / MODEL_8B_Q1_BYTES, 1),
+        "rows_K_per_s": _r(sum(n_vec * s.rows * s.K for s in shapes) / med, 1),
+        "roofline": roofline(gbps, HBM_PEAK_GBPS, "GB/s", "hbm",
+                             None if q1_traffic is None else q1_traffic["step"],
+                             traffic_source=TRAFFIC_SOURCE if q1_traffic else None,
+                             kernel="q1_gemv_grouped_kernel", us_per_launch=_r(med * 1e6, 2),
+                             bytes_per_launch=step_bytes,
+                             timing=f"HIP events on the launch stream around each batch of {args.steps} "
+                                    f"back-to-back launches (one per step); median of {args.batches} batches"),
         "parity_mismatches": mism,
         "serial_one_launch_per_gemv": serial,
-        "measured_read_ceiling_GBps": None if ceiling is None else round(ceiling, 1),
+        "read_ceiling_GBps": _r(ceiling, 1),
         "cpu_baseline": cpu,
-        "wall_s_timed": round(wall, 4),
+        "wall_s_timed": _r(wall, 4),
     }
+    log(f"[bench] q1: {gbps:.1f} GB/s median ({step_bytes / hi / 1e9:.1f}-{step_bytes / lo / 1e9:.1f}), "
+        f"{med * 1e6:.2f} us per step; batches (us/step): " + ", ".join(f"{p * 1e6:.2f}" for p in per_batch))
     return out
 
 
@@ -387,22 +471,22 @@ def cpu_baseline_q1(Ws, A, shapes, budget_s: float):
         one_used += time.perf_counter() - t
         one_bytes += q1_gemv_bytes(s.rows, s.K)
         n_one += 1
-    return {"value": round(done_bytes / t_used / 1e9, 4), "unit": "GB/s", "cores": threads,
+    return {"value": _r(done_bytes / t_used / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{n_gemv} batch-1 GEMVs of the step (vectors x {{4096x4096, 14336x4096}}, in order, "
-                      f"cycling), {t_used:.2f} s of oracle time, OpenMP over rows, {cpu_model()}",
-            "single_thread": {"value": round(one_bytes / one_used / 1e9, 4), "unit": "GB/s", "cores": 1,
-                              "sample": f"{n_one} of the same GEMVs, {one_used:.2f} s"}}
+            "sample": f"{n_gemv} batch-1 GEMVs of the step, {t_used:.1f} s, OpenMP over rows",
+            "cpu_model": cpu_model(),
+            "single_thread": {"value": _r(one_bytes / one_used / 1e9, 4), "unit": "GB/s", "cores": 1,
+                              "sample": f"{n_one} of the same GEMVs, {one_used:.1f} s"}}
 
 
 # ---------------------------------------- Q1 correctness-sized (256 x 1024)
 
 def bench_q1_small(args, gd, torch):
     """Q1_0.q8_0 GEMV rows=256, K=1024, batch 1 (the correctness-sized
-    config; 38,976 algorithmic bytes per GEMV). (S): one launch per GEMV,
-    back to back from a HIP graph: the latency figure. (G): independent
-    problems in grouped launches, each reading its own copy of the planes,
-    the copies rotating over a ring > 1 GiB: the streaming figure."""
+    config; 38,976 algorithmic bytes per GEMV). (G): independent problems in
+    grouped launches, each reading its own copy of the planes, the copies
+    rotating over a ring > 1 GiB: the streaming figure. (S): one launch per
+    GEMV, back to back from a HIP graph: the latency figure."""
     import oracle
     cfg = wl.Q1_SMALL
     rows, K = cfg.rows, cfg.K
@@ -424,21 +508,20 @@ def bench_q1_small(args, gd, torch):
 
     def grouped(kk):
         gd.q1_q8_gemv_grouped(probs[kk % sets], count, rows, K)
-    per_g, _ = _time_launches(torch, grouped, max(4, args.aux_steps // 4), sets)
-    # every output of two problems of each set, bit for bit
-    want = oracle.q1_q8_gemv_aos(W, A, rows, K).view(np.uint32)
+    per_g, st_g = _time_launches(torch, grouped, sets, sets, args.batches)
+    # every output of every problem, bit for bit
+    want = oracle.q1_q8_gemv_aos(W, A, rows, K).view(np.uint32).reshape(-1)
     mism = 0
     for t in range(sets):
-        for i in (0, count - 1):
-            got = ys[t][i * rows:(i + 1) * rows].cpu().numpy().view(np.uint32)
-            mism += int((got != want).sum())
+        got = ys[t].cpu().numpy().view(np.uint32).reshape(count, rows)
+        mism += int((got != want[None, :]).sum())
     ys1 = torch.empty(rows, device="cuda")
     stride = max(1, count // 64)
 
     def single(kk):
         t, i = kk % sets, (kk * stride) % count
         gd.q1_q8_gemv(bits[t][i * bb:(i + 1) * bb], scl[t][i * sb:(i + 1) * sb], a, ys1, rows, K, 1)
-    per_s, _ = _time_launches(torch, single, 64, 4)
+    per_s, st_s = _time_launches(torch, single, 64, 4, args.batches)
     mism += int((ys1.cpu().numpy().view(np.uint32) != want).sum())
     g_gbps = count * gemv_bytes / per_g / 1e9
     small_traffic = measured_traffic("q1_small")
@@ -452,17 +535,17 @@ def bench_q1_small(args, gd, torch):
     return {
         "workload": "Q1_0.q8_0 GEMV rows=256, K=1024, batch 1",
         "metric": "effective HBM GB/s (grouped: independent problems, ring > 1 GiB)",
-        "value": round(g_gbps, 1), "unit": "GB/s", "problems_per_launch": count, "ring_copies": sets * count,
-        "us_per_launch": round(per_g * 1e6, 2),
-        "single_launch": {"us_per_gemv": round(per_s * 1e6, 3), "GB_per_s": round(gemv_bytes / per_s / 1e9, 1),
-                          "timing": "HIP graph of 64 back-to-back single-GEMV launches"},
-        "roofline": {"bound": "hbm", "achieved": round(g_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(g_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": (None if small_traffic is None or count != 7646
-                                 else small_traffic["7646 x 256x1024"]),
-                     "kernel": "q1_gemv_grouped_small_kernel", "bytes_per_launch": count * gemv_bytes},
+        "value": _r(g_gbps, 1), "unit": "GB/s", "us": _r(per_g * 1e6, 2),
+        "problems_per_launch": count, "ring_copies": sets * count, "timing": st_g,
+        "extra": {"single_launch_us": _r(per_s * 1e6, 3)},
+        "single_launch": {"us_per_gemv": _r(per_s * 1e6, 3), "GB_per_s": _r(gemv_bytes / per_s / 1e9, 1),
+                          "timing": st_s, "note": "64 launches in a graph; latency-bound (a 39 KB GEMV)"},
+        "roofline": roofline(g_gbps, HBM_PEAK_GBPS, "GB/s", "hbm",
+                             (None if small_traffic is None or count != 7646
+                              else small_traffic["7646 x 256x1024"]),
+                             kernel="q1_gemv_grouped_small_kernel", bytes_per_launch=count * gemv_bytes),
         "parity_mismatches": mism,
-        "cpu_baseline": {"value": round(n_g * gemv_bytes / t_used / 1e9, 4), "unit": "GB/s", "cores": threads,
+        "cpu_baseline": {"value": _r(n_g * gemv_bytes / t_used / 1e9, 4), "unit": "GB/s", "cores": threads,
                          "kind": "oracle", "sample": f"{n_g} GEMVs of 256x1024, {t_used:.2f} s"},
     }
 
@@ -473,7 +556,8 @@ def bench_q1_mm(args, gd, torch):
     """Q1_0.q8_0 with several activation columns (P1's multi-column Q1_MM,
     the prompt side of the same method) on the 14336x4096 decode weight: the
     columns share one read of the weights and keep the bits of their own
-    batch-1 GEMVs. Weight copies rotate over a ring > 1 GiB."""
+    batch-1 GEMVs. Weight copies rotate over a ring > 1 GiB (one graph of
+    launches covers the whole ring, so no copy is read again from cache)."""
     import oracle
     cfg = wl.Q1_DECODE[1]
     rows, K = cfg.rows, cfg.K
@@ -484,6 +568,7 @@ def bench_q1_mm(args, gd, torch):
     ring = max(2, int(np.ceil(1.05 * (1 << 30) / plane)))
     copies = [(b0.clone(), s0.clone()) for _ in range(ring)]
     w_bytes = rows * (K // 128) * 18
+    threads = cpu_cores()
     out = {}
     for M in (2, 4, 8):
         A = np.concatenate([wl.q8_acts_aos(K, sd) for sd in cfg.act_seeds[:M]])
@@ -493,83 +578,29 @@ def bench_q1_mm(args, gd, torch):
         def launch(k, a=a, y=y, M=M):
             bb, ss = copies[k % ring]
             gd.q1_q8_gemv(bb, ss, a, y, rows, K, M)
-        per, _ = _time_launches(torch, launch, args.aux_steps, 3)
+        per, st = _time_launches(torch, launch, ring, 3, args.batches)
         got = y.cpu().numpy().reshape(M, rows)
-        sample = np.arange(0, rows, 37)
-        want = oracle.q1_q8_gemv_aos(W[sample], A, len(sample), K, n_act=M, nthreads=cpu_cores())
-        mism = int((got[:, sample].view(np.uint32) != want.reshape(M, -1).view(np.uint32)).sum())
-        launch_bytes = w_bytes + M * ((K // 32) * 34 + rows * 4)
-        threads = cpu_cores()
         t = time.perf_counter()
-        n_cpu = 512
-        oracle.q1_q8_gemv_aos(W[:n_cpu], A, n_cpu, K, n_act=M, nthreads=threads)
+        want = oracle.q1_q8_gemv_aos(W, A, rows, K, n_act=M, nthreads=threads)   # every output
         t_cpu = time.perf_counter() - t
+        mism = int((got.view(np.uint32) != want.reshape(M, -1).view(np.uint32)).sum())
+        launch_bytes = w_bytes + M * ((K // 32) * 34 + rows * 4)
         out[f"m{M}"] = {
             "workload": f"Q1_0.q8_0 small-M: {M} activation columns x 14336x4096 weight",
-            "metric": "HBM GB/s (weights read once)", "value": round(launch_bytes / per / 1e9, 1), "unit": "GB/s",
-            "us_per_launch": round(per * 1e6, 2),
-            "gemv_equivalent_GBps": round(M * q1_gemv_bytes(rows, K) / per / 1e9, 1),
-            "token_rows_K_per_s": round(M * rows * K / per, 1),
-            "roofline": {"bound": "hbm", "achieved": round(launch_bytes / per / 1e9, 1), "peak": HBM_PEAK_GBPS,
-                         "unit": "GB/s", "frac": round(launch_bytes / per / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None,
-                         "kernel": f"q1_gemv_mc_kernel<{2 if M <= 2 else 4 if M <= 4 else 8}>",
-                         "bytes_per_launch": launch_bytes},
-            "parity_mismatches_sampled": mism, "parity_sample": f"every 37th row ({len(sample)} rows) x {M} columns",
-            "cpu_baseline": {"value": round(M * n_cpu * (K // 128) * 18 / t_cpu / 1e9, 4), "unit": "GB/s (GEMV-equivalent)",
-                             "cores": threads, "kind": "oracle",
-                             "sample": f"first {n_cpu} rows x {M} columns, {t_cpu:.2f} s"},
+            "metric": "HBM GB/s (weights read once)", "value": _r(launch_bytes / per / 1e9, 1), "unit": "GB/s",
+            "us": _r(per * 1e6, 2), "timing": st,
+            "gemv_equivalent_GBps": _r(M * q1_gemv_bytes(rows, K) / per / 1e9, 1),
+            "roofline": roofline(launch_bytes / per / 1e9, HBM_PEAK_GBPS, "GB/s", "hbm",
+                                 kernel="q1 multi-column kernels", bytes_per_launch=launch_bytes),
+            "parity_mismatches": mism,
+            "cpu_baseline": {"value": _r(M * q1_gemv_bytes(rows, K) / t_cpu / 1e9, 4),
+                             "unit": "GB/s (GEMV-equivalent)", "cores": threads, "kind": "oracle",
+                             "sample": f"all {rows} rows x {M} columns, {t_cpu:.2f} s"},
         }
     return out
 
 
-# ------------------------------------------------- secondary workloads
-
-MFMA_F16_PEAK_TFLOPS = 2500.0    # MI355X dense fp16 matrix peak
-
-
-def _events(torch):
-    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-
-
-MIN_SPIN_S = 0.1   # sustained load before each short-kernel timing
-
-
-def spin_up(torch, run, n_min, min_s):
-    """Runs run(n_min), then run(n_min) again until at least min_s seconds of
-    GPU work have passed; returns the number of run() units done (untimed)."""
-    done = 0
-    t = time.perf_counter()
-    while True:
-        run(n_min)
-        torch.cuda.synchronize()
-        done += n_min
-        if time.perf_counter() - t >= min_s:
-            return done
-
-
-def _time_launches(torch, launch, n, warmup):
-    """Mean time (s) per launch of n launches captured in one HIP graph and
-    replayed between two HIP events on the launch stream: the launches run
-    back to back whatever the host's launch rate (a kernel shorter than a
-    Python launch would otherwise leave the GPU idle between launches).
-    The graph is replayed untimed for MIN_SPIN_S first, so the clocks have
-    left idle."""
-    for w in range(warmup):
-        launch(w)
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=torch.cuda.Stream()):
-        for k in range(n):
-            launch(warmup + k)
-    spin_up(torch, lambda _n: g.replay(), 1, MIN_SPIN_S)
-    t0, t1 = _events(torch)
-    t0.record()
-    g.replay()
-    t1.record()
-    torch.cuda.synchronize()
-    total = t0.elapsed_time(t1) / 1e3
-    return total / n, total
-
+# ------------------------------------------------- sign-bit GEMM (prefill)
 
 def bench_sign(args, gd, torch):
     """Sign-bit prefill GEMM y = x @ w^T, M=512 tokens, N=4096, K=4096: MFMA
@@ -588,77 +619,73 @@ def bench_sign(args, gd, torch):
     def launch(k):
         a, b, s_, y = sets[k % ring]
         gd.q1_sign_gemm(a, b, s_, y, M, N, K)
-    per, _ = _time_launches(torch, launch, args.aux_steps, 3)
+    per, st = _time_launches(torch, launch, ring, 3, args.batches)
     flops = 2.0 * M * N * K
     tflops = flops / per / 1e12
     sg_traffic = measured_traffic("sign")
-    # parity on a sample of columns
-    y = sets[(3 + args.aux_steps - 1) % ring][3].cpu().numpy().reshape(M, N)
-    cols = np.arange(0, N, 64)
-    want = oracle.sign_gemm_f64(x, bits[cols], scales[cols], nthreads=cpu_cores())
-    rel = float(np.max(np.abs(y[:, cols] - want)) / np.max(np.abs(want)))
-    # oracle on the host: whole rows of y (all N columns) until the budget
+    # parity: every output of the last launched set against the f64 oracle
+    y = sets[(3 + ring - 1) % ring][3].cpu().numpy().reshape(M, N)
     threads = cpu_cores()
-    t_used, rows_done = 0.0, 0
-    while t_used < args.aux_cpu_seconds and rows_done < M:
-        t = time.perf_counter()
-        oracle.sign_gemm_f64(x[rows_done:rows_done + 4], bits, scales, nthreads=threads)
-        t_used += time.perf_counter() - t
-        rows_done += 4
-    cpu_gflops = 2.0 * rows_done * N * K / t_used / 1e9
+    t = time.perf_counter()
+    want = oracle.sign_gemm_f64(x, bits, scales, nthreads=threads)
+    t_full = time.perf_counter() - t
+    rel = float(np.max(np.abs(y - want)) / np.max(np.abs(want)))
 
     # the same GEMM on weights packed once (q1_sign_pack), and the LUT4
     # comparator on those packed weights
     packed = []
-    for a, b, s_, y in sets:
+    for a, b, s_, yy in sets:
         wp = torch.empty(gd.q1_sign_packed_bytes(N, K), dtype=torch.uint8, device="cuda")
         gd.q1_sign_pack(b, s_, N, K, wp)
-        packed.append((a, wp, y))
+        packed.append((a, wp, yy))
 
     def launch_packed(k):
-        a, wp, y = packed[k % ring]
-        gd.q1_sign_gemm_packed(a, wp, y, M, N, K)
-    per_p, _ = _time_launches(torch, launch_packed, args.aux_steps, 3)
+        a, wp, yy = packed[k % ring]
+        gd.q1_sign_gemm_packed(a, wp, yy, M, N, K)
+    per_p, st_p = _time_launches(torch, launch_packed, ring, 3, args.batches)
+    y_p = packed[(3 + ring - 1) % ring][2].cpu().numpy().reshape(M, N)
+    rel_p = float(np.max(np.abs(y_p - want)) / np.max(np.abs(want)))
 
     def launch_lut(k):
-        a, wp, y = packed[k % ring]
-        gd.q1_sign_gemm_lut4(a, wp, y, M, N, K)
-    per_l, _ = _time_launches(torch, launch_lut, max(4, args.aux_steps // 4), 1)
-    y_l = packed[(1 + max(4, args.aux_steps // 4) - 1) % ring][2].cpu().numpy().reshape(M, N)
-    rel_l = float(np.max(np.abs(y_l[:, cols] - want)) / np.max(np.abs(want)))
+        a, wp, yy = packed[k % ring]
+        gd.q1_sign_gemm_lut4(a, wp, yy, M, N, K)
+    per_l, st_l = _time_launches(torch, launch_lut, ring, 1, args.batches)
+    y_l = packed[(1 + ring - 1) % ring][2].cpu().numpy().reshape(M, N)
+    rel_l = float(np.max(np.abs(y_l - want)) / np.max(np.abs(want)))
     decode = bench_sign_gemv(args, gd, torch)
+    busy = measured_mfma_busy("sign_gemm_kernel")
     return {
         "workload": "sign-bit prefill GEMM y=x@w^T, M=512, N=4096, K=4096, x f32 (fp16 hi+lo on MFMA)",
-        "metric": "useful TFLOP/s (2MNK)", "value": round(tflops, 2), "unit": "TFLOP/s",
-        "us_per_gemm": round(per * 1e6, 2), "prefill_tok_s": round(M / per, 1),
-        "issued_mfma_TFLOPs": round(2 * tflops, 2),
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
-                     "traffic": None if sg_traffic is None else sum(sg_traffic.values()),
-                     "traffic_per_kernel": sg_traffic,
-                     "kernel": "q1_sign_gemm call (sign_prep: split + weight regroup in one launch; sign_gemm)",
-                     "flops_per_launch": flops,
-                     "mfma_busy_hw": measured_mfma_busy("sign_gemm_kernel")},
-        "parity_rel_err_sampled": rel,
-        "cpu_baseline": {"value": round(cpu_gflops / 1e3, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-                         "sample": f"{rows_done} of 512 rows x all 4096 columns (f64 oracle), {t_used:.2f} s"},
-        "packed_weights": {"note": "weights packed once by q1_sign_pack; per call: split + GEMM kernels",
-                           "us_per_gemm": round(per_p * 1e6, 2), "value": round(flops / per_p / 1e12, 2),
-                           "unit": "TFLOP/s", "frac": round(flops / per_p / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)},
+        "metric": "useful TFLOP/s (2MNK)", "value": _r(tflops, 2), "unit": "TFLOP/s",
+        "us": _r(per * 1e6, 2), "timing": st, "prefill_tok_s": _r(M / per, 1),
+        "roofline": roofline(tflops, MFMA_F16_PEAK_TFLOPS, "TFLOP/s", "mfma",
+                             None if sg_traffic is None else sum(sg_traffic.values()),
+                             traffic_per_kernel=sg_traffic,
+                             kernel="q1_sign_gemm call (all its kernels)",
+                             flops_per_launch=flops, mfma_busy_hw=busy),
+        "parity_rel_err": rel,
+        "cpu_baseline": {"value": _r(flops / t_full / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
+                         "kind": "oracle", "sample": f"all 512 x 4096 outputs (f64 oracle), {t_full:.2f} s"},
+        "extra": {"packed_us": _r(per_p * 1e6, 2), "packed_frac": _r(flops / per_p / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+                  "lut4_us": _r(per_l * 1e6, 2)},
+        "packed_weights": {"note": "weights packed once by q1_sign_pack; per call: the remaining kernels",
+                           "us_per_gemm": _r(per_p * 1e6, 2), "value": _r(flops / per_p / 1e12, 2),
+                           "unit": "TFLOP/s", "frac": _r(flops / per_p / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+                           "timing": st_p, "parity_rel_err": rel_p},
         "lut4_comparator": {"note": "the page's LUT4 prefill (table lookup, VALU + LDS), packed weights",
-                            "us_per_gemm": round(per_l * 1e6, 2), "value": round(flops / per_l / 1e12, 2),
-                            "unit": "TFLOP/s", "vs_mfma_packed": round(per_l / per_p, 2),
+                            "us_per_gemm": _r(per_l * 1e6, 2), "value": _r(flops / per_l / 1e12, 2),
+                            "unit": "TFLOP/s", "vs_mfma_packed": _r(per_l / per_p, 2), "timing": st_l,
                             "traffic": (None if measured_traffic("sign_lut") is None
                                         else measured_traffic("sign_lut")["lut4"]),
-                            "parity_rel_err_sampled": rel_l},
+                            "parity_rel_err": rel_l},
         "decode_gemv": decode,
     }
 
 
 def bench_sign_gemv(args, gd, torch):
     """Sign-bit decode GEMV (M=1) on packed weights at the 8B-class decode
-    shapes, one launch per GEMV over a ring of weight copies > 1 GiB; HBM
-    roofline on the packed weight bytes + x + y."""
+    shapes, one launch per GEMV over a ring of weight copies > 1 GiB (one
+    graph covers the ring); HBM roofline on the packed weight bytes + x + y."""
     import oracle
     out = {}
     lt = measured_traffic("sign_lut")
@@ -676,22 +703,22 @@ def bench_sign_gemv(args, gd, torch):
 
         def launch(k):
             gd.q1_sign_gemv(xd, copies[k % ring], y, 1, N, K)
-        per, _ = _time_launches(torch, launch, 64, 4)
+        per, st = _time_launches(torch, launch, ring, 4, args.batches)
         bytes_ = wbytes + K * 4 + N * 4
         got = y.cpu().numpy()
         want = oracle.sign_gemm_f64(x, bits, scales, nthreads=cpu_cores())[0]
         out[f"{N}x{K}"] = {
-            "us_per_gemv": round(per * 1e6, 2), "value": round(bytes_ / per / 1e9, 1), "unit": "GB/s",
-            "roofline": {"bound": "hbm", "achieved": round(bytes_ / per / 1e9, 1), "peak": HBM_PEAK_GBPS,
-                         "unit": "GB/s", "frac": round(bytes_ / per / 1e9 / HBM_PEAK_GBPS, 4),
-                         "traffic": None if lt is None else lt[f"{N}x{K}"],
-                         "kernel": "sign_gemv_kernel", "bytes_per_launch": bytes_,
-                         "timing": "one HIP graph of 64 launches over distinct weight copies"},
+            "us": _r(per * 1e6, 2), "value": _r(bytes_ / per / 1e9, 1), "unit": "GB/s", "timing": st,
+            "roofline": roofline(bytes_ / per / 1e9, HBM_PEAK_GBPS, "GB/s", "hbm",
+                                 None if lt is None else lt[f"{N}x{K}"], kernel="sign_gemv_kernel",
+                                 bytes_per_launch=bytes_),
             "parity_rel_err": float(np.max(np.abs(got - want)) / np.max(np.abs(want))),
         }
         del copies
     return out
 
+
+# ------------------------------------------------------ block-Q8 matmul_nt
 
 def bench_blockq8(args, gd, torch):
     """Block-Q8 matmul_nt k=960, n=49152 at m=1 and m=16: HBM roofline on the
@@ -707,6 +734,7 @@ def bench_blockq8(args, gd, torch):
     sd = torch.from_numpy(scales).cuda()
     copies = [(qd.clone(), sd.clone()) for _ in range(ring)]
     bq_traffic = measured_traffic("blockq8")
+    threads = cpu_cores()
     for m in c["ms"]:
         x = np.ascontiguousarray(x_all[:m])
         xd = torch.from_numpy(x).cuda()
@@ -715,39 +743,31 @@ def bench_blockq8(args, gd, torch):
         def launch(kk):
             q_, s_ = copies[kk % ring]
             gd.blockq8_matmul_nt(xd, q_, s_, y, m, k, n)
-        per, _ = _time_launches(torch, launch, args.aux_steps, 3)
+        per, st = _time_launches(torch, launch, ring, 3, args.batches)
         bytes_ = w_bytes + x.nbytes + m * n * 4
         gbps = bytes_ / per / 1e9
-        cols = np.arange(0, n, 97)
-        got = y.cpu().numpy().reshape(m, n)[:, cols]
-        want = oracle.blockq8_f32(x, quants[cols], scales[cols], nthreads=cpu_cores())
+        got = y.cpu().numpy().reshape(m, n)
+        t = time.perf_counter()
+        want = oracle.blockq8_f32(x, quants, scales, nthreads=threads)   # every output
+        t_cpu = time.perf_counter() - t
         rel = float(np.max(np.abs(got - want)) / np.max(np.abs(want)))
-        threads = cpu_cores()
-        t_used, cols_done, step = 0.0, 0, 4096
-        while t_used < args.aux_cpu_seconds / 2 and cols_done < n:
-            t = time.perf_counter()
-            oracle.blockq8_f32(x, quants[cols_done:cols_done + step], scales[cols_done:cols_done + step],
-                               nthreads=threads)
-            t_used += time.perf_counter() - t
-            cols_done += step
-        cpu_bytes = cols_done * (k + k // 32 * 4) + x.nbytes + m * cols_done * 4
         out[f"m{m}"] = {
             "workload": f"block-Q8 matmul_nt k=960 n=49152 m={m}",
-            "metric": "effective HBM GB/s", "value": round(gbps, 1), "unit": "GB/s",
-            "us_per_launch": round(per * 1e6, 2), "pct_of_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
-            "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": round(gbps / HBM_PEAK_GBPS, 4),
-                         "traffic": None if bq_traffic is None else bq_traffic[f"m{m}"],
-                         "kernel": "blockq8_gemv_kernel" if m == 1 else "blockq8_mfma_kernel<32>",
-                         "bytes_per_launch": bytes_,
-                         "mfma_busy_hw": None if m == 1 else measured_mfma_busy("blockq8_mfma_kernel")},
-            "parity_rel_err_sampled": rel,
-            "cpu_baseline": {"value": round(cpu_bytes / t_used / 1e9, 4), "unit": "GB/s", "cores": threads,
-                             "kind": "oracle",
-                             "sample": f"{cols_done} of 49152 output features, m={m}, {t_used:.2f} s"},
+            "metric": "effective HBM GB/s", "value": _r(gbps, 1), "unit": "GB/s",
+            "us": _r(per * 1e6, 2), "timing": st,
+            "roofline": roofline(gbps, HBM_PEAK_GBPS, "GB/s", "hbm",
+                                 None if bq_traffic is None else bq_traffic[f"m{m}"],
+                                 kernel="blockq8_gemv_kernel" if m == 1 else "blockq8_mfma_kernel<32>",
+                                 bytes_per_launch=bytes_,
+                                 mfma_busy_hw=None if m == 1 else measured_mfma_busy("blockq8_mfma_kernel")),
+            "parity_rel_err": rel,
+            "cpu_baseline": {"value": _r(bytes_ / t_cpu / 1e9, 4), "unit": "GB/s", "cores": threads,
+                             "kind": "oracle", "sample": f"all 49152 output features, m={m}, {t_cpu:.2f} s"},
         }
     return out
 
+
+# ------------------------------------------------- activation quantization
 
 def bench_quant(args, gd, torch):
     """On-device activation quantization (the step before each GEMV): q8_0
@@ -756,7 +776,6 @@ def bench_quant(args, gd, torch):
     roofline on 4 B read per element plus what is written)."""
     import oracle
     out = {}
-    threads = cpu_cores()
 
     def measure(name, kind, shapes, copies_n):
         """shapes: list of (count, K) launched back to back as one step."""
@@ -780,10 +799,11 @@ def bench_quant(args, gd, torch):
                     gd.q8_0_quantize(x, o[0], cnt, K)
                 else:
                     gd.ternary_quantize_act(x, cnt, K, o[0], o[1])
-        per, _ = _time_launches(torch, launch, args.aux_steps, 2)
+        per, st = _time_launches(torch, launch, max(args.aux_steps, copies_n), 2, args.batches)
         bytes_ = sum(cnt * K * 4 + (cnt * (K // 32) * 34 if kind == "q8" else cnt * (K + 4)) for cnt, K in shapes)
         gbps = bytes_ / per / 1e9
-        # parity on the first rows of the first set, and an oracle sample for the CPU baseline
+        # parity on the first rows of the first set (an oracle sample, also
+        # timed as the CPU baseline)
         mism = 0
         t_used, done_bytes = 0.0, 0
         for (cnt, K), (x, o) in zip(shapes, sets[0]):
@@ -808,15 +828,13 @@ def bench_quant(args, gd, torch):
         out[name] = {
             "workload": " + ".join(f"{cnt}x{K}" for cnt, K in shapes) + (" f32 -> q8_0" if kind == "q8"
                                                                            else " f32 -> int8 planes"),
-            "metric": "effective HBM GB/s", "value": round(gbps, 1), "unit": "GB/s",
-            "us_per_step": round(per * 1e6, 2), "launches_per_step": len(shapes),
-            "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": round(gbps / HBM_PEAK_GBPS, 4),
-                         "traffic": None if qt is None else qt[name],
-                         "kernel": "q8_0_quantize_kernel" if kind == "q8" else "act_quant_kernel",
-                         "bytes_per_step": bytes_},
-            "parity_mismatches_sampled": mism,
-            "cpu_baseline": {"value": round(done_bytes / max(t_used, 1e-9) / 1e9, 4), "unit": "GB/s",
+            "metric": "effective HBM GB/s", "value": _r(gbps, 1), "unit": "GB/s",
+            "us": _r(per * 1e6, 2), "timing": st, "launches_per_step": len(shapes),
+            "roofline": roofline(gbps, HBM_PEAK_GBPS, "GB/s", "hbm", None if qt is None else qt[name],
+                                 kernel="q8_0_quantize_kernel" if kind == "q8" else "act_quant_kernel",
+                                 bytes_per_step=bytes_),
+            "parity_mismatches": mism,
+            "cpu_baseline": {"value": _r(done_bytes / max(t_used, 1e-9) / 1e9, 4), "unit": "GB/s",
                              "cores": 1, "kind": "oracle",
                              "sample": "first <= 64 rows of each shape, single-threaded oracle"},
         }
@@ -828,6 +846,8 @@ def bench_quant(args, gd, torch):
     measure("int8_planes_batch_256MiB", "act", [(16384, 4096)], 2)
     return out
 
+
+# ------------------------------------------------------ decode attention
 
 def bench_attention(args, gd, torch):
     """Split-K decode attention for one token at the 8B-class shape (32 query
@@ -855,7 +875,7 @@ def bench_attention(args, gd, torch):
         def launch(kk):
             kc, vc = caches[kk % ring]
             gd.attn_decode_splitk(qd, kc, vc, o, Hq, Hkv, D, L, L, scale, 0, ws)
-        per, _ = _time_launches(torch, launch, args.aux_steps, 2)
+        per, st = _time_launches(torch, launch, max(args.aux_steps, ring), 2, args.batches)
         bytes_ = set_bytes + 2 * Hq * D * 4
         got = o.cpu().numpy().reshape(Hq, D)
         t = time.perf_counter()
@@ -863,19 +883,20 @@ def bench_attention(args, gd, torch):
         t_cpu = time.perf_counter() - t
         out[f"kv{L}"] = {
             "workload": f"decode attention, 1 token, {Hq} query / {Hkv} KV heads, d={D}, kv_len={L}, f32 KV",
-            "metric": "effective HBM GB/s", "value": round(bytes_ / per / 1e9, 1), "unit": "GB/s",
-            "us_per_call": round(per * 1e6, 2),
-            "roofline": {"bound": "hbm", "achieved": round(bytes_ / per / 1e9, 1), "peak": HBM_PEAK_GBPS,
-                         "unit": "GB/s", "frac": round(bytes_ / per / 1e9 / HBM_PEAK_GBPS, 4),
-                         "traffic": None if at is None else at[f"kv{L}"],
-                         "kernel": "attn_split_kernel<4> + attn_merge_kernel", "bytes_per_call": bytes_},
+            "metric": "effective HBM GB/s", "value": _r(bytes_ / per / 1e9, 1), "unit": "GB/s",
+            "us": _r(per * 1e6, 2), "timing": st,
+            "roofline": roofline(bytes_ / per / 1e9, HBM_PEAK_GBPS, "GB/s", "hbm",
+                                 None if at is None else at[f"kv{L}"],
+                                 kernel="attn_split_kernel<4> + attn_merge_kernel", bytes_per_call=bytes_),
             "parity_rel_err": float(np.max(np.abs(got - want)) / np.max(np.abs(want))),
-            "cpu_baseline": {"value": round(bytes_ / t_cpu / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "cpu_baseline": {"value": _r(bytes_ / t_cpu / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
                              "sample": "one whole call (f64 numpy, per head)"},
         }
         del caches
     return out
 
+
+# ----------------------------------------------------------------- ternary
 
 def bench_ternary(args, gd, torch):
     """BitNet-2B-like ternary decode step: 210 GEMVs (per layer 4 x 2560x2560,
@@ -924,41 +945,36 @@ def bench_ternary(args, gd, torch):
         slots.append(per)
     torch.cuda.synchronize()
     step_bytes = step_w_bytes + sum(shapes[j][1] + shapes[j][0] * 4 + 8 for j in range(len(shapes)))
+    pos_ = [0]
 
-    def step(kk):
-        sset = slots[kk % n_sets]
+    def step():
+        sset = slots[pos_[0] % n_sets]
+        pos_[0] += 1
         for K, xd in x_by_K.items():
             gd.ternary_act_bitplanes(xd, xd.shape[0], K, planes_by_K[K])
         for sh, idx in groups.items():
             gd.ternary_gemv_grouped(sset[sh], len(idx), sh[0], sh[1])
 
-    spin_up(torch, lambda n: [step(w) for w in range(n)], 3, args.min_warmup_s)
-    # timed steps: launches queued back to back, events only at the ends
-    t0, t1 = _events(torch)
-    t0.record()
-    for kk in range(args.aux_steps):
-        step(3 + kk)
-    t1.record()
-    torch.cuda.synchronize()
-    total = t0.elapsed_time(t1) / 1e3 / args.aux_steps
-    # GEMV kernels alone: each shape's grouped launch, reps back to back over
-    # the weight sets, between two events
+    spin_up(torch, lambda n: [step() for _ in range(n)], 3, args.min_warmup_s)
+    # R batches of steps queued back to back, events only at a batch's ends
+    med, lo, hi, _ = time_batches(torch, lambda: [step() for _ in range(args.aux_steps)], args.aux_steps,
+                                  args.batches)
+    # GEMV kernels alone: each shape's grouped launch, `reps` back to back
+    # over the weight sets between two events, median of the batches
     reps = 8
     gemv_s = 0.0
     for sh, idx in groups.items():
         for kk in range(2):
             gd.ternary_gemv_grouped(slots[kk % n_sets][sh], len(idx), sh[0], sh[1])
-        a0, a1 = _events(torch)
-        a0.record()
-        for kk in range(reps):
-            gd.ternary_gemv_grouped(slots[kk % n_sets][sh], len(idx), sh[0], sh[1])
-        a1.record()
-        torch.cuda.synchronize()
-        gemv_s += a0.elapsed_time(a1) / 1e3 / reps
+
+        def gb(sh=sh, idx=idx):
+            for kk in range(reps):
+                gd.ternary_gemv_grouped(slots[kk % n_sets][sh], len(idx), sh[0], sh[1])
+        gemv_s += time_batches(torch, gb, reps, args.batches)[0]
     # GEMV bytes of a step: both weight planes, the activation planes, y
     gemv_bytes = step_w_bytes + sum(shapes[j][0] * 4 + 8 * (shapes[j][1] // 32) * 4 for j in range(len(shapes)))
     tern_traffic = measured_traffic("ternary")
-    gbps = step_bytes / total / 1e9
+    gbps = step_bytes / med / 1e9
     # parity: three GEMVs (one per shape), every row, against the oracle
     mism = 0
     for sh, idx in groups.items():
@@ -979,19 +995,18 @@ def bench_ternary(args, gd, torch):
     return {
         "workload": "ternary bitplane decode step: 30 layers x {4x 2560x2560, 2x 6912x2560, 1x 2560x6912} = 210 "
                     "GEMVs, int8 activations as bit planes, P/N weight planes",
-        "metric": "effective HBM GB/s (step)", "value": round(gbps, 1), "unit": "GB/s",
-        "us_per_step": round(total * 1e6, 2), "equiv_tok_s": round(1.0 / total, 1),
-        "context_tok_s_at_0.69GB": round(gbps / 0.69, 1),
-        "pct_of_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
-        "roofline": {"bound": "hbm", "achieved": round(gemv_bytes / gemv_s / 1e9, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(gemv_bytes / gemv_s / 1e9 / HBM_PEAK_GBPS, 4),
-                     "traffic": None if tern_traffic is None else sum(tern_traffic.values()),
-                     "traffic_per_launch": tern_traffic,
-                     "kernel": "ternary_held_grouped_kernel (3 launches per step, one per shape)",
-                     "bytes_per_step_gemv": gemv_bytes},
+        "metric": "effective HBM GB/s (step)", "value": _r(gbps, 1), "unit": "GB/s",
+        "us": _r(med * 1e6, 2), "spread_us": [_r(lo * 1e6, 2), _r(hi * 1e6, 2)],
+        "equiv_tok_s": _r(1.0 / med, 1), "context_tok_s_at_0.69GB": _r(gbps / 0.69, 1),
+        "extra": {"equiv_tok_s": _r(1.0 / med, 1), "gemv_us": _r(gemv_s * 1e6, 2)},
+        "roofline": roofline(gemv_bytes / gemv_s / 1e9, HBM_PEAK_GBPS, "GB/s", "hbm",
+                             None if tern_traffic is None else sum(tern_traffic.values()),
+                             traffic_per_launch=tern_traffic,
+                             kernel="ternary_held_grouped_kernel (3 launches per step, one per shape)",
+                             bytes_per_step_gemv=gemv_bytes),
         "step_bytes": step_bytes, "ring_sets": n_sets,
-        "parity_mismatches_3_gemvs": mism,
-        "cpu_baseline": {"value": round(done_bytes / t_used / 1e9, 4), "unit": "GB/s", "cores": threads,
+        "parity_mismatches": mism,
+        "cpu_baseline": {"value": _r(done_bytes / t_used / 1e9, 4), "unit": "GB/s", "cores": threads,
                          "kind": "oracle",
                          "sample": f"{n_g} GEMVs of the step (first 512 rows each), {t_used:.2f} s"},
     }
@@ -1002,14 +1017,15 @@ def bench_ternary(args, gd, torch):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=50, help="steps per timed batch")
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--batches", type=int, default=15, help="timed batches (median reported), at least 10")
     ap.add_argument("--min-warmup-s", type=float, default=0.2,
                     help="untimed warmup continues until this much sustained load has run")
     ap.add_argument("--workload", default="all",
                     choices=["all", "q1", "q1small", "q1mm", "sign", "blockq8", "ternary", "quant", "attention"],
                     help="all (default): the Q1 metric line plus the other paths under 'workloads'")
-    ap.add_argument("--aux-steps", type=int, default=20, help="timed launches for the other paths")
+    ap.add_argument("--aux-steps", type=int, default=20, help="launches per graph for the other paths (minimum)")
     ap.add_argument("--aux-cpu-seconds", type=float, default=4.0)
     ap.add_argument("--ring-gib", type=float, default=1.25)
     ap.add_argument("--serial-steps", type=int, default=3)
@@ -1023,11 +1039,15 @@ def main():
     ap.add_argument("--ceiling-reps", type=int, default=5)
     ap.add_argument("--no-parity", dest="parity", action="store_false",
                     help="skip the untimed oracle comparison (profiling runs)")
+    ap.add_argument("--detail-out", default=None, help="also write the full record (JSON) to this file")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library runs each product on one MI355X, and sharding "
               "across GPUs is described, not implemented -- run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if args.batches < 10 or args.steps < 1:
+        print("bench.py: --batches must be at least 10 and --steps at least 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -1041,31 +1061,42 @@ def main():
         out = bench_q1(args, gd, torch)
     else:
         out = {"metric": METRIC, "note": "Q1 workload skipped (--workload)"}
+    full = dict(out)
     if args.workload != "q1":
         extra = {}
-        if args.workload in ("all", "sign"):
-            log("[bench] sign-bit prefill GEMM")
-            extra["sign_gemm"] = bench_sign(args, gd, torch)
-        if args.workload in ("all", "blockq8"):
-            log("[bench] block-Q8 matmul_nt")
-            extra["blockq8"] = bench_blockq8(args, gd, torch)
-        if args.workload in ("all", "q1small"):
-            log("[bench] Q1 256x1024 GEMV")
-            extra["q1_256x1024"] = bench_q1_small(args, gd, torch)
-        if args.workload in ("all", "q1mm"):
-            log("[bench] Q1 small-M (several columns)")
-            extra["q1_small_m"] = bench_q1_mm(args, gd, torch)
-        if args.workload in ("all", "ternary"):
-            log("[bench] ternary decode step")
-            extra["ternary_step"] = bench_ternary(args, gd, torch)
-        if args.workload in ("all", "quant"):
-            log("[bench] activation quantization")
-            extra["act_quant"] = bench_quant(args, gd, torch)
-        if args.workload in ("all", "attention"):
-            log("[bench] split-K decode attention")
-            extra["decode_attention"] = bench_attention(args, gd, torch)
-        out["workloads"] = extra
-    print(json.dumps(out), flush=True)
+        steps = [("cfg0_q1_256x1024", "q1small", bench_q1_small),
+                 ("cfg2_sign_gemm", "sign", bench_sign),
+                 ("cfg3_blockq8", "blockq8", bench_blockq8),
+                 ("cfg4_ternary_step", "ternary", bench_ternary),
+                 ("next1_q1_small_m", "q1mm", bench_q1_mm),
+                 ("next2_act_quant", "quant", bench_quant),
+                 ("next4_decode_attention", "attention", bench_attention)]
+        for key, name, fn in steps:
+            if args.workload in ("all", name):
+                log(f"[bench] {key}")
+                extra[key] = fn(args, gd, torch)
+        full["workloads"] = extra
+        short = {}
+        for key, rec in extra.items():
+            if key == "cfg3_blockq8":
+                for m, r in rec.items():
+                    short[f"cfg3_blockq8_{m}"] = compact(r)
+            elif key in ("next1_q1_small_m", "next2_act_quant", "next4_decode_attention"):
+                short[key] = {sub: compact(r) for sub, r in rec.items()}
+            elif key == "cfg2_sign_gemm":
+                short[key] = compact(rec)
+                short["next3_sign_gemv"] = {sub: compact(r) for sub, r in rec["decode_gemv"].items()}
+            else:
+                short[key] = compact(rec)
+        out["workloads"] = short
+    if out.get("cpu_baseline"):
+        cb = out["cpu_baseline"]
+        out["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
+    log("[bench] detail " + json.dumps(full))
+    if args.detail_out:
+        with open(args.detail_out, "w") as f:
+            json.dump(full, f, indent=1)
+    print(json.dumps(out, separators=(",", ":")), flush=True)
 
 
 if __name__ == "__main__":
