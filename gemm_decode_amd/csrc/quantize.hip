@@ -86,7 +86,11 @@ __device__ __forceinline__ uint32_t or8(uint32_t v) {   // OR over the 8 lanes o
     return v;
 }
 
-__device__ __forceinline__ int32_t code_of(float x, float inv32, double inv) {
+// f64_only: the token's reciprocal 127/absmax does not fit in f32 (absmax
+// below about 3.7e-37), so the f32 product could not stand in for the f64
+// one; every code is then decided in f64.
+__device__ __forceinline__ int32_t code_of(float x, float inv32, double inv, bool f64_only) {
+    if (f64_only) return round_code(static_cast<double>(x) * inv);
     const float v = x * inv32;
     const float fl = floorf(v);
     const float fr = v - fl;
@@ -125,6 +129,7 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(const float *__rest
     const double amax = static_cast<double>(token_absmax(m, red, wave, lane));
     const double inv = amax > 0.0 ? 127.0 / amax : 0.0;
     const float inv32 = static_cast<float>(inv);
+    const bool f64_only = !(inv32 <= 3.40282347e38f);   // uniform: the reciprocal overflowed f32
     if (threadIdx.x == 0) scale[c] = amax > 0.0 ? static_cast<float>(amax / 127.0) : 0.0f;
     const int64_t W = K / 32;
     const int k8 = lane % 8, g = lane / 8;
@@ -134,7 +139,7 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(const float *__rest
             const float e[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
             uint32_t u = 0;
 #pragma unroll
-            for (int j = 0; j < 4; j++) u |= (static_cast<uint32_t>(code_of(e[j], inv32, inv)) & 0xffu) << (8 * j);
+            for (int j = 0; j < 4; j++) u |= (static_cast<uint32_t>(code_of(e[j], inv32, inv, f64_only)) & 0xffu) << (8 * j);
             uint32_t mine = 0;
 #pragma unroll
             for (int b = 0; b < 8; b++) {

@@ -125,6 +125,24 @@ def test_token_codes_at_ties(gd, K):
     assert np.array_equal(q[0, 1:], np.floor(base[0, 1:] + 0.5).astype(np.int8))   # ties went up
 
 
+@pytest.mark.parametrize("K", [256, 2560, 8192, 8224])
+def test_token_tiny_absmax(gd, K):
+    """Tokens whose absmax lies in the f32 subnormal range or near 1e-37,
+    where 127/absmax no longer fits in f32: codes and scales still follow the
+    f64 rule bit for bit (x = absmax/2 must give 64, not a clamped 127)."""
+    rng = np.random.default_rng(K + 1)
+    mags = [1e-40, 3e-39, 1e-37, 3.6e-37, 1e-36]
+    x = np.stack([rng.uniform(-1, 1, size=K) * m for m in mags]).astype(np.float32)
+    for r in range(len(mags)):
+        x[r, 0] = np.float32(mags[r])                  # the token's absmax
+        x[r, 1] = np.float32(mags[r]) / np.float32(2)  # half of it
+    planes, scale = run_act(gd, x)
+    q, s = oracle.quantize_absmax_int8(x)
+    assert np.array_equal(planes.cpu().numpy().view(np.uint32).reshape(len(mags), 8, K // 32), planes_of(q))
+    assert np.array_equal(scale.cpu().numpy().view(np.uint32), s.view(np.uint32))
+    assert all(q[r, 1] == 64 for r in range(len(mags)))
+
+
 def test_zero_input(gd):
     x = np.zeros((2, 128), dtype=np.float32)
     assert not run_q8(gd, x).any()
