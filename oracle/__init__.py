@@ -65,7 +65,6 @@ def _declare(L):
     L.gdo_pack_q1_p1.argtypes = [_P, _I64, _I64, _P, _P]
     L.gdo_pack_q8_p1.argtypes = [_P, _I64, _I64, _P, _P]
     L.gdo_q1_q8_gemv_p1packed.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _INT]
-    L.gdo_q1_planes.argtypes = [_P, _I64, _I64, _P, _P]
     L.gdo_sign_gemm_f64.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _INT]
     L.gdo_sign_gemm_f32.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _INT]
     L.gdo_blockq8_f32.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _INT]
@@ -76,7 +75,7 @@ def _declare(L):
     L.gdo_f32_to_f16.restype = ctypes.c_uint16
     L.gdo_quantize_q8_0.argtypes = [_P, _I64, _I64, _P]
     for name in ("gdo_q1_q8_gemv_aos", "gdo_pack_q1_p1", "gdo_pack_q8_p1",
-                 "gdo_q1_q8_gemv_p1packed", "gdo_q1_planes", "gdo_sign_gemm_f64",
+                 "gdo_q1_q8_gemv_p1packed", "gdo_sign_gemm_f64",
                  "gdo_sign_gemm_f32", "gdo_blockq8_f32", "gdo_ternary_dot_direct",
                  "gdo_ternary_gemv", "gdo_quantize_absmax_int8", "gdo_quantize_q8_0"):
         getattr(L, name).restype = None
@@ -133,23 +132,6 @@ def q1_q8_gemv_p1packed(w_aos, a_aos, rows: int, K: int, n_act: int = 1, nthread
     lib().gdo_q1_q8_gemv_p1packed(wd.ctypes.data, wb.ctypes.data, ad.ctypes.data,
                                   aq.ctypes.data, y.ctypes.data, rows, K, n_act, nthreads)
     return y
-
-
-def q1_plane_shapes(rows: int, K: int):
-    nb = K // 128
-    nb8 = (nb + 7) // 8 * 8
-    r64 = (rows + 63) // 64 * 64
-    return (r64 * nb * 4,), (r64 * nb8,)
-
-
-def q1_planes(w_aos, rows: int, K: int):
-    """The library's documented Q1 plane layout: (bits u32[...], scales u16[...])."""
-    w, wp = _c(w_aos, np.uint8)
-    bshape, sshape = q1_plane_shapes(rows, K)
-    bits = np.empty(bshape, dtype=np.uint32)
-    scales = np.empty(sshape, dtype=np.uint16)
-    lib().gdo_q1_planes(wp, rows, K, bits.ctypes.data, scales.ctypes.data)
-    return bits, scales
 
 
 def _check_q1(w, a, rows, K, n_act):

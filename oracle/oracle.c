@@ -63,16 +63,29 @@ float gdo_f16_to_f32(uint16_t h)
     return s ? -v : v;
 }
 
-/* The int8 negation [P1] uses when a sign bit is 0: two's-complement
- * wrapping, so -(-128) stays -128 (Q1_DOT_WGSL, "the reference negates as an
- * i8 (wrapping)"). */
+/* The negation [P1] applies to a quant whose sign bit is 0 is an int8
+ * negation, which wraps: -128 has no positive counterpart in int8 and stays
+ * -128 (Q1_DOT_WGSL, the comment on the sign select). */
 static int32_t neg_i8_wrapping(int32_t q)
 {
     return q == -128 ? -128 : -q;
 }
 
+/* The signed, wrapped quant the method adds for one element: q itself when
+ * the element's sign bit is 1, its int8 negation when it is 0. */
+static int32_t signed_quant(int bit, int8_t q)
+{
+    return bit ? (int32_t)q : neg_i8_wrapping(q);
+}
+
+/* f16 scale stored little-endian at p. */
+static float scale_at(const uint8_t *p)
+{
+    return gdo_f16_to_f32((uint16_t)(p[0] | (p[1] << 8)));
+}
+
 /* ------------------------------------------------------------------------
- * Q1_0 . q8_0, form F1: walks the array-of-structs bytes like Q1_DOT_WGSL.
+ * Q1_0 . q8_0, form F1: from the array-of-structs bytes of both operands.
  *
  * [P1] header comment: per 128 weights a f16 d0 and 128 sign bits; per 32
  * activations a f16 d1 and 32 int8. For block i and accumulation lane l=0..7:
@@ -88,37 +101,43 @@ void gdo_q1_q8_gemv_aos(const uint8_t *w, const uint8_t *a, float *y,
                         int64_t rows, int64_t K, int64_t n_act, int nthreads)
 {
     const int64_t nb = K / QK1;
-    const int64_t nb8 = K / QK8;
     if (nthreads < 1) nthreads = 1;
 #pragma omp parallel for num_threads(nthreads) schedule(static) collapse(2)
     for (int64_t c = 0; c < n_act; c++) {
         for (int64_t r = 0; r < rows; r++) {
-            const uint8_t *act = a + c * nb8 * Q8_BYTES;
+            const uint8_t *act = a + c * (K / QK8) * Q8_BYTES;   /* column c */
+            const uint8_t *wrow = w + r * nb * Q1_BYTES;          /* row r */
             float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
             for (int64_t i = 0; i < nb; i++) {
-                const uint8_t *wb = w + (r * nb + i) * Q1_BYTES;
-                float d0 = gdo_f16_to_f32((uint16_t)(wb[0] | (wb[1] << 8)));
-                float ab[8];
+                const uint8_t *blk = wrow + i * Q1_BYTES;
+                /* The block's integer sums first (exact in int32): s[k][l]
+                 * over the four elements 4l..4l+3 of sub-block k, where
+                 * element t of sub-block k is weight 32k + t of the block,
+                 * whose sign bit sits at bit (32k+t)%8 of byte 2+(32k+t)/8. */
+                int32_t s[4][8];
+                float d1[4];
+                memset(s, 0, sizeof s);
                 for (int k = 0; k < 4; k++) {
-                    const uint8_t *ab8 = act + (i * 4 + k) * Q8_BYTES;
-                    float d1 = gdo_f16_to_f32((uint16_t)(ab8[0] | (ab8[1] << 8)));
-                    for (int l = 0; l < 8; l++) {
-                        int32_t s = 0;
-                        for (int e = 4 * l; e < 4 * l + 4; e++) {
-                            int32_t q = (int32_t)(int8_t)ab8[2 + e];
-                            int bit = (wb[2 + k * 4 + e / 8] >> (e % 8)) & 1;
-                            s += bit ? q : neg_i8_wrapping(q);
-                        }
-                        float prod = d1 * (float)s;
-                        ab[l] = (k == 0) ? prod : ab[l] + prod;
+                    const uint8_t *ablk = act + (4 * i + k) * Q8_BYTES;
+                    d1[k] = scale_at(ablk);
+                    for (int t = 0; t < 32; t++) {
+                        const int j = 32 * k + t;
+                        const int bit = (blk[2 + j / 8] >> (j % 8)) & 1;
+                        s[k][t / 4] += signed_quant(bit, (int8_t)ablk[2 + t]);
                     }
                 }
-                for (int l = 0; l < 8; l++)
-                    acc[l] = fmaf(d0, ab[l], acc[l]);
+                /* Then the float chain of each lane in the stated order:
+                 * ab = d1_0*s_0, + d1_1*s_1, + d1_2*s_2, + d1_3*s_3 (each
+                 * product exact, each add rounded), and one fused step. */
+                const float d0 = scale_at(blk);
+                for (int l = 0; l < 8; l++) {
+                    float ab = d1[0] * (float)s[0][l];
+                    for (int k = 1; k < 4; k++) ab = ab + d1[k] * (float)s[k][l];
+                    acc[l] = fmaf(d0, ab, acc[l]);
+                }
             }
-            float h = ((acc[0] + acc[4]) + (acc[2] + acc[6])) +
-                      ((acc[1] + acc[5]) + (acc[3] + acc[7]));
-            y[c * rows + r] = h;
+            y[c * rows + r] = ((acc[0] + acc[4]) + (acc[2] + acc[6])) +
+                              ((acc[1] + acc[5]) + (acc[3] + acc[7]));
         }
     }
 }
@@ -171,80 +190,34 @@ void gdo_q1_q8_gemv_p1packed(const float *wd, const uint32_t *wb,
                              int64_t rows, int64_t K, int64_t n_act, int nthreads)
 {
     const int64_t nb = K / QK1;
+    const int64_t nb8 = K / QK8;
     if (nthreads < 1) nthreads = 1;
 #pragma omp parallel for num_threads(nthreads) schedule(static) collapse(2)
     for (int64_t c = 0; c < n_act; c++) {
         for (int64_t r = 0; r < rows; r++) {
-            float part[8];
+            const float *act_d = ad + c * nb8;              /* column c's block scales */
+            const uint32_t *act_q = aq + c * nb8 * 8;       /* its quant words, 8 per block */
+            float lane_acc[8];
             for (int l = 0; l < 8; l++) {
                 float acc = 0.f;
                 for (int64_t i = 0; i < nb; i++) {
-                    float d0 = wd[r * nb + i];
-                    float ab = 0.f;
+                    const uint32_t *signs = wb + (r * nb + i) * 4;   /* packQ1: word k = sub-block k */
+                    float prod[4];
                     for (int k = 0; k < 4; k++) {
-                        int64_t b = i * 4 + k;
-                        float d1 = ad[c * nb * 4 + b];
-                        uint32_t bits = (wb[(r * nb + i) * 4 + k] >> (4 * l)) & 0xfu;
-                        uint32_t qw = aq[(c * nb * 4 + b) * 8 + l];
+                        const uint32_t nib = (signs[k] >> (4 * l)) & 0xfu;   /* lane l's four signs */
+                        const uint32_t quad = act_q[(4 * i + k) * 8 + l];    /* lane l's four quants */
                         int32_t s = 0;
-                        for (int j = 0; j < 4; j++) {
-                            int32_t q = (int32_t)(int8_t)(uint8_t)(qw >> (8 * j));
-                            s += ((bits >> j) & 1u) ? q : neg_i8_wrapping(q);
-                        }
-                        float prod = d1 * (float)s;
-                        ab = (k == 0) ? prod : prod + ab;
+                        for (int e = 0; e < 4; e++)
+                            s += signed_quant((int)((nib >> e) & 1u), (int8_t)(uint8_t)(quad >> (8 * e)));
+                        prod[k] = act_d[4 * i + k] * (float)s;
                     }
-                    acc = fmaf(d0, ab, acc);
+                    const float ab = ((prod[0] + prod[1]) + prod[2]) + prod[3];
+                    acc = fmaf(wd[r * nb + i], ab, acc);
                 }
-                part[l] = acc;
+                lane_acc[l] = acc;
             }
-            y[c * rows + r] = ((part[0] + part[4]) + (part[2] + part[6])) +
-                              ((part[1] + part[5]) + (part[3] + part[7]));
-        }
-    }
-}
-
-/* ------------------------------------------------------------------------
- * The library's Q1 plane layout, written from its published definition
- * (include/gemm_decode.h, "Q1 planes"). Integer byte moves only.
- *   R64 = rows rounded up to 64, nb = K/128, nb8 = nb rounded up to 8.
- *   bits  : u32 [R64/64][nb][2 halves][64][2]; word m of half h of
- *           (row r, block i) holds the sign bits of elements 32k + 4l + j
- *           with l = 4h + jj (jj = 0..3), k = 2m + kk (kk = 0..1), j = 0..3,
- *           at bit (8*jj + 2 + 4*kk + j) mod 32.
- *   scales: u16 [R64/64][nb8/8][64][8]; entry (r, i) = the f16 bits of d0.
- *   Padding rows and padding blocks are zero.
- * ------------------------------------------------------------------------ */
-void gdo_q1_planes(const uint8_t *w, int64_t rows, int64_t K,
-                   uint32_t *bits, uint16_t *scales)
-{
-    const int64_t nb = K / QK1;
-    const int64_t nb8 = (nb + 7) / 8 * 8;
-    const int64_t R64 = (rows + 63) / 64 * 64;
-    memset(bits, 0, (size_t)(R64 * nb * 4) * sizeof(uint32_t));
-    memset(scales, 0, (size_t)(R64 * nb8) * sizeof(uint16_t));
-    for (int64_t r = 0; r < rows; r++) {
-        int64_t t = r / 64, lane = r % 64;
-        for (int64_t i = 0; i < nb; i++) {
-            const uint8_t *o = w + (r * nb + i) * Q1_BYTES;
-            scales[((t * (nb8 / 8) + i / 8) * 64 + lane) * 8 + (i % 8)] =
-                (uint16_t)(o[0] | (o[1] << 8));
-            for (int h = 0; h < 2; h++) {
-                for (int m = 0; m < 2; m++) {
-                    uint32_t word = 0;
-                    for (int jj = 0; jj < 4; jj++) {
-                        for (int kk = 0; kk < 2; kk++) {
-                            for (int j = 0; j < 4; j++) {
-                                int e = 32 * (2 * m + kk) + 4 * (4 * h + jj) + j;
-                                int bit = (o[2 + e / 8] >> (e % 8)) & 1;
-                                int pos = (8 * jj + 2 + 4 * kk + j) % 32;
-                                word |= (uint32_t)bit << pos;
-                            }
-                        }
-                    }
-                    bits[(((t * nb + i) * 2 + h) * 64 + lane) * 2 + m] = word;
-                }
-            }
+            y[c * rows + r] = ((lane_acc[0] + lane_acc[4]) + (lane_acc[2] + lane_acc[6])) +
+                              ((lane_acc[1] + lane_acc[5]) + (lane_acc[3] + lane_acc[7]));
         }
     }
 }

@@ -1,14 +1,15 @@
 """GPU parity for the Q1_0 . q8_0 path (repack + GEMV), through the C ABI.
 
-Bar: bit-exact. The planes must equal the oracle's plane writer byte for
-byte; every output's f32 bits must equal the oracle's (form F1, the page
-"browseml-gpu.js" arithmetic). Inputs are seeded and synthetic; -128 quants
+Bar: bit-exact. The planes must equal the declared layout (written by the
+test helper q1_layout) byte for byte; every output's f32 bits must equal the
+oracle's (form F1, the page "browseml-gpu.js" arithmetic). Inputs are seeded and synthetic; -128 quants
 and random f16 exponents come from the page's randomCase generator.
 """
 import numpy as np
 import pytest
 
 import oracle
+import q1_layout
 import workloads as wl
 
 torch = pytest.importorskip("torch")
@@ -57,7 +58,7 @@ def test_repack_matches_oracle_planes(gd, rows, K):
     W = wl.q1_weights_aos(rows, K, seed=rows * 7 + K)
     b, s = planes_on_gpu(gd, W, rows, K)
     torch.cuda.synchronize()
-    ob, os_ = oracle.q1_planes(W, rows, K)
+    ob, os_ = q1_layout.q1_planes(W, rows, K)
     assert np.array_equal(b.cpu().numpy().view(np.uint32), ob)
     assert np.array_equal(s.cpu().numpy().view(np.uint16), os_)
 

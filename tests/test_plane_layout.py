@@ -1,4 +1,6 @@
-"""Pins for the oracle's writer of the library's Q1 plane layout.
+"""Pins for the test helper that writes the library's Q1 plane layout
+(tests/q1_layout.py), the reference the repack kernel is compared with byte
+for byte.
 
 The layout is the library's own (declared in include/gemm_decode.h, "Q1
 planes"); the page "browseml-gpu.js" (packQ1) only fixes what it must carry:
@@ -10,6 +12,7 @@ import numpy as np
 import pytest
 
 import workloads as wl
+from q1_layout import q1_planes
 
 
 def declared_pos(e):
@@ -19,13 +22,13 @@ def declared_pos(e):
     return h * 128 + m, (8 * jj + 2 + 4 * kk + j) % 32
 
 
-def test_each_element_lands_at_declared_bit(orc):
+def test_each_element_lands_at_declared_bit():
     rows, K = 1, 128
     for e in range(128):
         W = np.zeros((1, 1, 18), dtype=np.uint8)
         W[0, 0, 0:2] = [0x00, 0x3C]
         W[0, 0, 2 + e // 8] = 1 << (e % 8)
-        bits, scales = orc.q1_planes(W, rows, K)
+        bits, scales = q1_planes(W, rows, K)
         idx, pos = declared_pos(e)
         want = np.zeros(64 * 4, dtype=np.uint32)
         want[idx] = np.uint32(1) << np.uint32(pos)   # row 0 -> lane 0
@@ -60,9 +63,9 @@ def _decode_planes(bits, scales, rows, K):
 
 
 @pytest.mark.parametrize("rows,K", [(1, 128), (65, 384), (130, 1152)])
-def test_round_trip_and_zero_padding(orc, rows, K):
+def test_round_trip_and_zero_padding(rows, K):
     W = wl.q1_weights_aos(rows, K, seed=rows + K)
-    bits, scales = orc.q1_planes(W, rows, K)
+    bits, scales = q1_planes(W, rows, K)
     assert np.array_equal(_decode_planes(bits, scales, rows, K), W)
     nb = K // 128
     nb8 = (nb + 7) // 8 * 8
