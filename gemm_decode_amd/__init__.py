@@ -73,6 +73,7 @@ def _declare():
         "q8_0_quantize": [_P, _P, _I64, _I64, _P],
         "attn_decode_workspace_bytes": [_I64, _I64, _I64, _I64, _I64, ctypes.POINTER(ctypes.c_size_t)],
         "attn_decode_splitk": [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F32, _I64, _P, ctypes.c_size_t, _P],
+        "attn_decode_splitk_noalloc": [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F32, _I64, _P],
         "ternary_quantize_act": [_P, _I64, _I64, _P, _P, _P],
         "gemm_decode_fill": [_P, ctypes.c_size_t, ctypes.c_uint32, _P],
         "gemm_decode_stream_read": [_P, ctypes.c_size_t, ctypes.c_int32, _P, _I64, _P],
@@ -351,6 +352,21 @@ def attn_decode_splitk(q, k_cache, v_cache, out, n_heads: int, n_kv_heads: int, 
                                    _dev(out, torch.float32, n_heads * head_dim, "out"),
                                    n_heads, n_kv_heads, head_dim, kv_len, kv_stride, float(scale), num_splits,
                                    _dev(workspace, torch.uint8, None, "workspace"), workspace.numel(), _stream()))
+
+
+def attn_decode_splitk_noalloc(q, k_cache, v_cache, out, n_heads: int, n_kv_heads: int, head_dim: int,
+                               kv_len: int, kv_stride: int, scale: float, num_splits: int = 0):
+    """attn_decode_splitk with the split partials in the library's own
+    scratch (no workspace, nothing allocated; calls that overlap on one
+    device race)."""
+    import torch
+    cache_n = n_kv_heads * kv_stride * head_dim
+    _check(_lib.attn_decode_splitk_noalloc(_dev(q, torch.float32, n_heads * head_dim, "q"),
+                                           _dev(k_cache, torch.float32, cache_n, "k_cache"),
+                                           _dev(v_cache, torch.float32, cache_n, "v_cache"),
+                                           _dev(out, torch.float32, n_heads * head_dim, "out"),
+                                           n_heads, n_kv_heads, head_dim, kv_len, kv_stride, float(scale),
+                                           num_splits, _stream()))
 
 
 # ------------------------------------------------------------ measurement

@@ -26,6 +26,8 @@
 // 64 splits at a time under a running maximum.
 // A split with no keys writes max -inf, denominator 0 and output 0, and
 // contributes nothing.
+#include <mutex>
+
 #include "gd_device.h"
 #include "gd_internal.h"
 
@@ -289,26 +291,17 @@ extern "C" int attn_decode_workspace_bytes(int64_t n_heads, int64_t n_kv_heads, 
     return GD_OK;
 }
 
-extern "C" int attn_decode_splitk(const float *q, const float *k_cache, const float *v_cache, float *out,
-                                  int64_t n_heads, int64_t n_kv_heads, int64_t head_dim, int64_t kv_len,
-                                  int64_t kv_stride, float scale, int64_t num_splits, void *workspace,
-                                  size_t workspace_bytes, void *stream) {
-    GD_REQUIRE(q && k_cache && v_cache && out && workspace, GD_EINVAL, "attn_decode_splitk: null pointer");
-    int64_t s, kps;
-    int st = plan(n_heads, n_kv_heads, head_dim, kv_len, num_splits, &s, &kps);
-    if (st) return st;
-    GD_REQUIRE(kv_stride >= kv_len, GD_EINVAL, "attn_decode_splitk: kv_stride (%lld) below kv_len (%lld)",
-               (long long)kv_stride, (long long)kv_len);
-    GD_REQUIRE(aligned(q, 16) && aligned(k_cache, 16) && aligned(v_cache, 16) && aligned(workspace, 16) &&
-                   aligned(out, 4),
-               GD_EALIGN, "attn_decode_splitk: q, caches and workspace must be 16-byte aligned, out 4-byte");
-    const size_t need = static_cast<size_t>(s * n_heads * (kD + 2) * 4);
-    GD_REQUIRE(workspace_bytes >= need, GD_ERANGE, "attn_decode_splitk: workspace of %zu bytes, %zu needed",
-               workspace_bytes, need);
+namespace {
+
+// Enqueues the split and merge launches on a validated call; `workspace`
+// holds the partials of `s` splits (caller-owned, or the file-scope scratch
+// below).
+int launch_attention(const float *q, const float *k_cache, const float *v_cache, float *out, int64_t n_heads,
+                     int64_t n_kv_heads, int64_t kv_len, int64_t kv_stride, float scale, int64_t s, int64_t kps,
+                     void *workspace, hipStream_t hs) {
     float *part_o = static_cast<float *>(workspace);
     float *part_ml = part_o + s * n_heads * kD;
     const int64_t G = n_heads / n_kv_heads;
-    hipStream_t hs = as_stream(stream);
     const dim3 grid(static_cast<uint32_t>(n_kv_heads), static_cast<uint32_t>(s));
 #define GD_ATTN(GG)                                                                                              \
     hipLaunchKernelGGL(attn_split_kernel<GG>, grid, dim3(kThreads), 0, hs, q, k_cache, v_cache, part_o, part_ml, \
@@ -324,5 +317,96 @@ extern "C" int attn_decode_splitk(const float *q, const float *k_cache, const fl
 #undef GD_ATTN
     hipLaunchKernelGGL(attn_merge_kernel, dim3(static_cast<uint32_t>(n_heads)), dim3(kMergeThreads), 0, hs, part_o,
                        part_ml, out, n_heads, s);
+    return GD_OK;
+}
+
+// The checks every attention entry point makes before its launches.
+int validate(const float *q, const float *k_cache, const float *v_cache, float *out, int64_t n_heads,
+             int64_t n_kv_heads, int64_t head_dim, int64_t kv_len, int64_t kv_stride, int64_t num_splits,
+             int64_t *s, int64_t *kps, const char *name) {
+    GD_REQUIRE(q && k_cache && v_cache && out, GD_EINVAL, "%s: null pointer", name);
+    int st = plan(n_heads, n_kv_heads, head_dim, kv_len, num_splits, s, kps);
+    if (st) return st;
+    GD_REQUIRE(kv_stride >= kv_len, GD_EINVAL, "%s: kv_stride (%lld) below kv_len (%lld)", name,
+               (long long)kv_stride, (long long)kv_len);
+    GD_REQUIRE(aligned(q, 16) && aligned(k_cache, 16) && aligned(v_cache, 16) && aligned(out, 4), GD_EALIGN,
+               "%s: q and caches must be 16-byte aligned, out 4-byte", name);
+    return GD_OK;
+}
+
+}  // namespace
+
+extern "C" int attn_decode_splitk(const float *q, const float *k_cache, const float *v_cache, float *out,
+                                  int64_t n_heads, int64_t n_kv_heads, int64_t head_dim, int64_t kv_len,
+                                  int64_t kv_stride, float scale, int64_t num_splits, void *workspace,
+                                  size_t workspace_bytes, void *stream) {
+    int64_t s, kps;
+    int st = validate(q, k_cache, v_cache, out, n_heads, n_kv_heads, head_dim, kv_len, kv_stride, num_splits, &s,
+                      &kps, "attn_decode_splitk");
+    if (st) return st;
+    GD_REQUIRE(workspace, GD_EINVAL, "attn_decode_splitk: null workspace");
+    GD_REQUIRE(aligned(workspace, 16), GD_EALIGN, "attn_decode_splitk: workspace must be 16-byte aligned");
+    const size_t need = static_cast<size_t>(s * n_heads * (kD + 2) * 4);
+    GD_REQUIRE(workspace_bytes >= need, GD_ERANGE, "attn_decode_splitk: workspace of %zu bytes, %zu needed",
+               workspace_bytes, need);
+    launch_attention(q, k_cache, v_cache, out, n_heads, n_kv_heads, kv_len, kv_stride, scale, s, kps, workspace,
+                     as_stream(stream));
     return check_launch("attn_decode_splitk");
+}
+
+// ---------------------------------------------------- no-allocation variant
+// For callers that cannot allocate device memory (code under graph capture,
+// serving loops that forbid it): the split partials live in this file-scope
+// array instead of a caller workspace. Each device the library runs on holds
+// its own copy until the process ends. Host code never uses the array's name
+// as an address: its device address is resolved once per device with
+// hipGetSymbolAddress (with that device current) and kept per device.
+// Nothing in it needs to start at zero: the split launch writes every
+// partial the merge launch reads. Calls that overlap on one device share the
+// array and race.
+static __device__ __align__(256) unsigned char scratch[GD_ATTN_NOALLOC_MAX_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void *g_scratch_addr[kMaxDevices];   // device address of `scratch` per device; null until resolved
+
+int scratch_address(void **addr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(GD_EHIP, "attn_decode_splitk_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+    GD_REQUIRE(dev >= 0 && dev < kMaxDevices, GD_ERANGE, "attn_decode_splitk_noalloc: device %d", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(GD_EHIP, "attn_decode_splitk_noalloc: hipGetSymbolAddress on device %d: %s", dev,
+                        hipGetErrorString(e));
+        g_scratch_addr[dev] = p;
+    }
+    *addr = g_scratch_addr[dev];
+    return GD_OK;
+}
+
+}  // namespace
+
+extern "C" int attn_decode_splitk_noalloc(const float *q, const float *k_cache, const float *v_cache, float *out,
+                                          int64_t n_heads, int64_t n_kv_heads, int64_t head_dim, int64_t kv_len,
+                                          int64_t kv_stride, float scale, int64_t num_splits, void *stream) {
+    int64_t s, kps;
+    int st = validate(q, k_cache, v_cache, out, n_heads, n_kv_heads, head_dim, kv_len, kv_stride, num_splits, &s,
+                      &kps, "attn_decode_splitk_noalloc");
+    if (st) return st;
+    const size_t need = static_cast<size_t>(s * n_heads * (kD + 2) * 4);
+    GD_REQUIRE(need <= GD_ATTN_NOALLOC_MAX_BYTES, GD_ERANGE,
+               "attn_decode_splitk_noalloc: %zu bytes of split partials needed, above the %d-byte scratch; "
+               "use attn_decode_splitk with a workspace", need, GD_ATTN_NOALLOC_MAX_BYTES);
+    void *ws = nullptr;
+    st = scratch_address(&ws);
+    if (st) return st;
+    launch_attention(q, k_cache, v_cache, out, n_heads, n_kv_heads, kv_len, kv_stride, scale, s, kps, ws,
+                     as_stream(stream));
+    return check_launch("attn_decode_splitk_noalloc");
 }

@@ -383,6 +383,22 @@ int attn_decode_splitk(const float *q, const float *k_cache, const float *v_cach
                        int64_t kv_stride, float scale, int64_t num_splits,
                        void *workspace, size_t workspace_bytes, void *stream);
 
+/* attn_decode_splitk without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops or harnesses
+ * that forbid hipMalloc). Same arguments, validation, kernels and results
+ * as attn_decode_splitk; the split partials go to a scratch array inside the
+ * library (GD_ATTN_NOALLOC_MAX_BYTES per device, held from the first call on
+ * that device until the process ends). The call allocates nothing. Requires
+ * num_splits * n_heads * (head_dim + 2) * 4 <= GD_ATTN_NOALLOC_MAX_BYTES
+ * (num_splits = 0: the split count the call picks), else GD_ERANGE before
+ * any launch. Calls on one device share its scratch: calls that overlap on
+ * one device (several streams, several host threads) race; order them.
+ * Errors: GD_EINVAL, GD_ESHAPE, GD_EALIGN, GD_ERANGE, GD_EHIP. */
+#define GD_ATTN_NOALLOC_MAX_BYTES (4 * 1024 * 1024)
+int attn_decode_splitk_noalloc(const float *q, const float *k_cache, const float *v_cache, float *out,
+                               int64_t n_heads, int64_t n_kv_heads, int64_t head_dim, int64_t kv_len,
+                               int64_t kv_stride, float scale, int64_t num_splits, void *stream);
+
 /* ====================================================================
  * Measurement kernels  ("roofline.html": the FILL kernel writes a non-zero,
  * incompressible pattern so reads reach real DRAM; the read kernel streams

@@ -30,7 +30,7 @@ def test_header_declares_the_entry_points():
               "blockq8_matmul_nt", "ternary_act_bitplanes", "ternary_gemv", "ternary_gemv_grouped",
               "q8_0_quantize", "ternary_quantize_act", "q1_sign_packed_bytes", "q1_sign_pack",
               "q1_sign_gemm_packed", "q1_sign_gemv", "q1_sign_gemm_lut4",
-              "attn_decode_workspace_bytes", "attn_decode_splitk",
+              "attn_decode_workspace_bytes", "attn_decode_splitk", "attn_decode_splitk_noalloc",
               "gemm_decode_status_string", "gemm_decode_last_error", "gemm_decode_abi_version",
               "gemm_decode_fill", "gemm_decode_stream_read"]:
         assert n in names, n
@@ -165,3 +165,18 @@ def test_validation_without_gpu(gd):
     # measurement
     assert L.gemm_decode_fill(FAKE, 100, 1, None) == E["shape"]
     assert L.gemm_decode_stream_read(FAKE, 160, 0, FAKE, 1, None) == E["inval"]
+
+
+def test_attention_noalloc_validation_before_any_hip_call(gd):
+    """The no-allocation attention entry point rejects, without touching the
+    device: null pointers, and shapes whose split partials would not fit its
+    fixed scratch (GD_ATTN_NOALLOC_MAX_BYTES = 4 MiB)."""
+    L = gd.lib()
+    buf = ctypes.create_string_buffer(64)
+    p = ctypes.addressof(buf)
+    p16 = p + (-p) % 16
+    assert L.attn_decode_splitk_noalloc(None, p16, p16, p16, 32, 8, 128, 4096, 4096, 0.1, 0, None) == gd.GD_EINVAL
+    # 64 heads x 1024 splits x 130 floats = 34 MB of partials > 4 MiB
+    assert L.attn_decode_splitk_noalloc(p16, p16, p16, p16, 64, 8, 128, 1 << 20, 1 << 20, 0.1, 1024,
+                                        None) == gd.GD_ERANGE
+    assert "scratch" in L.gemm_decode_last_error().decode()
