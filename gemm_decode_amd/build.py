@@ -29,28 +29,43 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+# Host-side AddressSanitizer and UndefinedBehaviorSanitizer for the CPU-only
+# check of the entry points' validation (the device code is built as usual;
+# each -fsanitize= applies to the host compilation only).
+SANITIZE_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def _compile(src: str, build_dir: str = BUILD, extra=()) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [HIPCC, *FLAGS, *lang, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *extra, *lang, "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{res.stdout}{res.stderr}")
     return obj
 
 
-def build(jobs: int = 8) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(jobs: int = 8, sanitize: bool = False, out: str = LIB) -> str:
+    """Compiles csrc/ into `out` (the in-tree library by default). With
+    sanitize, the host code is built with ASan and UBSan into a separate
+    build folder; load such a library only in a process that preloads the
+    clang ASan runtime (see oracle/sanitize_check.py)."""
+    build_dir = os.path.join(HERE, "_build_san" if sanitize else "_build")
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
+    extra = SANITIZE_HOST if sanitize else ()
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+        objs = list(ex.map(lambda s: _compile(s, build_dir, extra), srcs))
+    tmp = out + ".tmp"
+    link_extra = (["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                   "-Xarch_host", "-shared-libsan"] if sanitize else [])
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *link_extra, *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}{res.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -25,17 +25,24 @@ CFLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC",
           "-shared", "-std=c11", "-Wall", "-Wextra"]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile oracle.c into liboracle.so (gcc; CPU only)."""
-    tmp = _LIB + ".tmp"
-    cmd = ["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"]
+SANITIZE_CFLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
+_LIB_SAN = os.path.join(_HERE, "liboracle_san.so")
+
+
+def build(verbose: bool = False, sanitize: bool = False) -> str:
+    """Compile oracle.c into liboracle.so (gcc; CPU only). With sanitize, an
+    ASan + UBSan build into liboracle_san.so, which lib() loads when
+    GD_ORACLE_SANITIZED=1 (in a process that preloads gcc's libasan)."""
+    out = _LIB_SAN if sanitize else _LIB
+    tmp = out + ".tmp"
+    cmd = ["gcc", *CFLAGS, *(SANITIZE_CFLAGS if sanitize else []), _SRC, "-o", tmp, "-lm"]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("oracle build failed:\n" + res.stdout + res.stderr)
     if verbose and res.stderr:
         print(res.stderr)
-    os.replace(tmp, _LIB)
-    return _LIB
+    os.replace(tmp, out)
+    return out
 
 
 _lib = None
@@ -44,9 +51,14 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
-            build()
-        _lib = ctypes.CDLL(_LIB)
+        if os.environ.get("GD_ORACLE_SANITIZED") == "1":
+            if not os.path.exists(_LIB_SAN):
+                build(sanitize=True)
+            _lib = ctypes.CDLL(_LIB_SAN)
+        else:
+            if not os.path.exists(_LIB):
+                build()
+            _lib = ctypes.CDLL(_LIB)
         _declare(_lib)
     return _lib
 
