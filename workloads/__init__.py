@@ -23,7 +23,6 @@ Wire formats produced here (as the pages define them):
 """
 from __future__ import annotations
 
-import math
 from dataclasses import dataclass
 
 import numpy as np
@@ -35,63 +34,73 @@ QK8_0 = 32
 
 
 # ---------------------------------------------------------------------------
-# The page's reproducible generator ("browseml-gpu.js", ``rng``: mulberry32),
-# ``f16bits`` and ``randomCase``, restated from their published definitions.
+# The page's reproducible test case ("browseml-gpu.js": its small generator,
+# a finite-f16 helper and randomCase), regenerated draw for draw so that the
+# page's own shapes and seeds give the page's bytes.
 # ---------------------------------------------------------------------------
 
-def _imul(a: int, b: int) -> int:
-    """32-bit wrapping multiply, as JavaScript's Math.imul (result unsigned)."""
-    return (a * b) & 0xFFFFFFFF
+_M32 = 0xFFFFFFFF
 
 
 class Mulberry32:
-    """mulberry32: a 32-bit counter-based generator returning floats in [0, 1)."""
+    """Tommy Ettinger's mulberry32: a 32-bit state advanced by the Weyl
+    constant 0x6D2B79F5 at every draw; the output is the new state put
+    through two rounds of xor-shift-and-multiply (shift 15 with multiplier
+    state|1, then shift 7 with multiplier |61, added back) and a final
+    xor-shift by 14, read as a fraction of 2^32 in [0, 1)."""
+
+    WEYL = 0x6D2B79F5
 
     def __init__(self, seed: int):
-        self.a = seed & 0xFFFFFFFF
+        self.state = seed & _M32
+
+    def next_u32(self) -> int:
+        self.state = (self.state + self.WEYL) & _M32
+        z = self.state
+        z = ((z ^ (z >> 15)) * (z | 1)) & _M32
+        z = (z ^ ((z + ((z ^ (z >> 7)) * (z | 61))) & _M32)) & _M32
+        return z ^ (z >> 14)
 
     def __call__(self) -> float:
-        self.a = (self.a + 0x6D2B79F5) & 0xFFFFFFFF
-        t = self.a
-        t = _imul(t ^ (t >> 15), t | 1)
-        t ^= (t + _imul(t ^ (t >> 7), t | 61)) & 0xFFFFFFFF
-        return ((t ^ (t >> 14)) & 0xFFFFFFFF) / 4294967296.0
+        return self.next_u32() / 4294967296.0
 
 
 def f16bits(r: Mulberry32, lo: int = 3, hi: int = 17) -> int:
-    """A finite f16 bit pattern: random sign, exponent field in [lo, hi),
-    random mantissa (draw order: sign, exponent, mantissa)."""
-    sign = 0x8000 if r() < 0.5 else 0
-    exp = lo + math.floor(r() * (hi - lo))
-    man = math.floor(r() * 1024)
-    return (sign | (exp << 10) | man) & 0xFFFF
+    """A finite f16 bit pattern with a random sign, an exponent field drawn
+    in [lo, hi) and a random 10-bit mantissa, drawn in that order."""
+    negative = r() < 0.5
+    exponent = lo + int(r() * (hi - lo))
+    mantissa = int(r() * 1024)
+    return (0x8000 if negative else 0) | (exponent << 10) | mantissa
+
+
+def _q1_block(r: Mulberry32) -> bytes:
+    """An 18-byte Q1_0 block: a random f16 scale, then 16 random bytes of
+    sign bits."""
+    scale = f16bits(r)
+    return scale.to_bytes(2, "little") + bytes(int(r() * 256) for _ in range(16))
+
+
+def _q8_block(r: Mulberry32) -> bytes:
+    """A 34-byte q8_0 block: a random f16 scale, then 32 quant bytes, each
+    0x80 (int8 -128) with probability 0.02 and otherwise a random byte (one
+    draw decides, a second draw gives the byte)."""
+    scale = f16bits(r)
+    quants = bytes(0x80 if r() < 0.02 else int(r() * 256) for _ in range(32))
+    return scale.to_bytes(2, "little") + quants
 
 
 def random_case(rows: int, n: int, seed: int = 1):
-    """P1's ``randomCase``: Q1_0 rows x n weights and one q8_0 vector of n,
-    f16 scales from ``f16bits`` and about 2% of quant bytes equal to 0x80
-    (int8 -128). Returns (W bytes [rows*nb*18], A bytes [n/32*34])."""
+    """P1's ``randomCase``: Q1_0 weights of rows x n and one q8_0 vector of
+    n, drawn from one generator seeded with `seed`: every weight block in
+    row-major order, then every activation block. About 2% of the quant
+    bytes are -128. Returns (W bytes [rows*nb*18], A bytes [n/32*34])."""
     if n % QK1_0:
         raise ValueError("n must be a multiple of 128")
     r = Mulberry32(seed)
-    nb = n // QK1_0
-    W = np.zeros(rows * nb * Q1_0_BYTES, dtype=np.uint8)
-    A = np.zeros((n // QK8_0) * Q8_0_BYTES, dtype=np.uint8)
-    for b in range(rows * nb):
-        o = b * Q1_0_BYTES
-        h = f16bits(r)
-        W[o] = h & 255
-        W[o + 1] = h >> 8
-        for j in range(2, Q1_0_BYTES):
-            W[o + j] = math.floor(r() * 256)
-    for b in range(n // QK8_0):
-        o = b * Q8_0_BYTES
-        h = f16bits(r)
-        A[o] = h & 255
-        A[o + 1] = h >> 8
-        for j in range(2, Q8_0_BYTES):
-            A[o + j] = 128 if r() < 0.02 else math.floor(r() * 256)
-    return W, A
+    W = b"".join(_q1_block(r) for _ in range(rows * (n // QK1_0)))
+    A = b"".join(_q8_block(r) for _ in range(n // QK8_0))
+    return np.frombuffer(W, dtype=np.uint8).copy(), np.frombuffer(A, dtype=np.uint8).copy()
 
 
 # ---------------------------------------------------------------------------
