@@ -1040,7 +1040,13 @@ def main():
     ap.add_argument("--no-parity", dest="parity", action="store_false",
                     help="skip the untimed oracle comparison (profiling runs)")
     ap.add_argument("--detail-out", default=None, help="also write the full record (JSON) to this file")
+    ap.add_argument("--min-spin-s", type=float, default=MIN_SPIN_S,
+                    help="sustained load before each short-kernel timing (counter runs set 0)")
+    ap.add_argument("--min-batch-s", type=float, default=MIN_BATCH_S,
+                    help="GPU time per timed batch of the other paths (counter runs set 0)")
     args = ap.parse_args()
+    globals()["MIN_SPIN_S"] = args.min_spin_s
+    globals()["MIN_BATCH_S"] = args.min_batch_s
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library runs each product on one MI355X, and sharding "

@@ -296,6 +296,44 @@ def test_grouped_mixed_rows(gd, K):
         assert np.all(np.isnan(got[rows:])), f"rows {rows}: wrote past its rows"
 
 
+@pytest.mark.parametrize("count", [72, 300])
+def test_grouped_k4096_mixed_problems(gd, count):
+    """A grouped launch at K = 4096 (one 32-block chunk per row) over many
+    problems of mixed row counts (1 to the launch's rows, ragged tails,
+    rows = 0 meaning the launch's rows), consecutive problems sharing one
+    activation buffer in pairs, several problems reading prefixes of the
+    same planes; 72 problems (more than one 64-wide pass over the problem
+    list) and 300 problems of few rows each. Every output bit-exact with the
+    oracle for its own rows, nothing written past them."""
+    K, rows_max = 4096, 5000
+    Ws = [wl.q1_weights_aos(5000, K, 71), wl.q1_weights_aos(4999, K, 72)]
+    nacts = 8
+    A = np.concatenate([wl.q8_acts_aos(K, 7100 + c) for c in range(nacts)])
+    planes = [planes_on_gpu(gd, W, W.shape[0], K) for W in Ws]
+    a_dev = [dev(A[c]) for c in range(nacts)]
+    want_full = [oracle.q1_q8_gemv_aos(W, A, W.shape[0], K, n_act=nacts, nthreads=oracle.max_threads())
+                 .reshape(nacts, W.shape[0]) for W in Ws]
+    if count == 72:
+        cycle = [(0, 5000, 5000), (1, 4999, 4999), (0, 1, 1), (1, 65, 65), (0, 300, 300), (1, 1000, 1000),
+                 (0, 4096, 4096), (0, 5000, 0)]   # (weights, rows, rows field)
+    else:
+        cycle = [(0, 65, 65), (1, 1, 1), (0, 64, 64), (1, 129, 129), (0, 7, 7)]
+    entries, checks = [], []
+    for i in range(count):
+        wi, rows, field = cycle[i % len(cycle)]
+        act = (i // 2) % nacts   # pairs of consecutive problems share an activation buffer
+        y = torch.full((rows + 64,), float("nan"), device="cuda")   # 64 guard elements
+        entries.append((planes[wi][0], planes[wi][1], a_dev[act], y, field))
+        checks.append((y, want_full[wi][act][:rows], rows, i))
+    probs = gd.make_q1_problems(entries)
+    gd.q1_q8_gemv_grouped(probs, count, rows_max, K)
+    torch.cuda.synchronize()
+    for y, want, rows, i in checks:
+        got = y.cpu().numpy()
+        assert_bits_equal(got[:rows], want, f"problem {i} rows {rows}")
+        assert np.all(np.isnan(got[rows:])), f"problem {i} rows {rows}: wrote past its rows"
+
+
 def test_grouped_graph_replay(gd):
     """The grouped launch captured in a HIP graph (as the benchmark replays
     it): four replays, with eager launches and host synchronisation between
