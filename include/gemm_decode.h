@@ -154,20 +154,28 @@ int q1_q8_gemv_grouped(const gd_q1_problem *problems, int64_t count,
  * ====================================================================
  *   y[m][n] = sum_g scales[n][g] * sum_{j<32} x[m][32g+j] * (bit_j ? +1 : -1)
  *   x       device f32 [M][K] row-major, 16-byte aligned, finite. The
- *           product runs on fp16 matrix cores: each row is scaled by a
- *           power of two that brings its largest |x| into [2^14, 2^15) and
- *           split into a high and a low fp16 part (the scaling is undone
- *           exactly on y); relative error ~1e-7 of ||y||_inf.
+ *           product runs on fp16 matrix cores: each row of x is scaled, in
+ *           each eighth of K (ceil(K/256) groups), by the power of two that
+ *           brings its largest |x| there into [2^14, 2^15), each output's
+ *           scales by the power of two that does the same for its largest
+ *           |scale|, and both are split into a high and a low
+ *           fp16 part (x = xh + xl, s = sh + sl, each within 2^-22 of its
+ *           value while normal in fp16); a 32-weight group contributes
+ *           xh*sh + xl*sh + xh*sl of its signed products, accumulated in
+ *           f32 on the matrix cores per eighth of K; each eighth's sum is
+ *           unscaled exactly and the eight are added in a fixed order.
+ *           Error within 1e-5 of ||y||_inf (about 5e-7 on N(0,1)
+ *           activations and |N(0,0.02)| scales at K = 4096).
  *   w_bits  device u32 [N][K/32], bit j of word g = weight 32g+j (LSB
  *           first), 4-byte aligned.
  *   w_scales device f32 [N][K/32], 4-byte aligned.
  *   y       device f32 [M][N], 4-byte aligned.
  *   workspace  device scratch of at least q1_sign_gemm_workspace_bytes(M,
  *           N, K) bytes, 16-byte aligned, owned by the caller. A first
- *           kernel writes the split activations and the weights regrouped
- *           by pairs of groups into it for the second; calls that share it
- *           must be ordered on one stream. Its contents on entry do not
- *           matter and on return are unspecified.
+ *           kernel writes the split activations and the weights in the
+ *           matrix-core layout (see q1_sign_pack) into it for the second;
+ *           calls that share it must be ordered on one stream. Its contents
+ *           on entry do not matter and on return are unspecified.
  * Requires K % 32 == 0. Errors: GD_EINVAL, GD_ESHAPE, GD_EALIGN, GD_ERANGE
  * (M, N or K above 2^31 - 1, workspace too small), GD_EHIP. */
 int q1_sign_gemm(const float *x, const uint32_t *w_bits, const float *w_scales,
@@ -175,21 +183,32 @@ int q1_sign_gemm(const float *x, const uint32_t *w_bits, const float *w_scales,
                  void *workspace, size_t workspace_bytes, void *stream);
 
 /* Workspace bytes q1_sign_gemm needs: 4*K per token (tokens padded to a
- * multiple of 16) plus 4 per padded token, plus 16 per output and pair of
- * 32-weight groups (ceil(K/64) pairs). Host only. Errors: GD_EINVAL,
- * GD_ESHAPE (K % 32 != 0), GD_ERANGE. */
+ * multiple of 16) plus 32 per padded token (an exponent per eighth of K),
+ * plus 16 per output and pair of 32-weight groups (ceil(K/64) pairs), plus
+ * 4 per output. Host only.
+ * Errors: GD_EINVAL, GD_ESHAPE (K % 32 != 0), GD_ERANGE. */
 int q1_sign_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t *bytes);
 
 /* Bytes of the packed sign-bit weights written by q1_sign_pack:
- * 16 * N * ceil(K/64). Host only. Errors: GD_EINVAL, GD_ESHAPE, GD_ERANGE. */
+ * 32 * N * ceil(K/64) + 4 * N. Host only. Errors: GD_EINVAL, GD_ESHAPE,
+ * GD_ERANGE. */
 int q1_sign_packed_bytes(int64_t N, int64_t K, size_t *bytes);
 
 /* One-time repack of the page's sign words and scales (the layouts
- * q1_sign_gemm takes) for the calls below: for each output n and pair of
- * 32-weight groups (g, g+1), g even, the u32x4 {bits[n][g], bits[n][g+1],
- * scale[n][g], scale[n][g+1]} (scales as f32 bit patterns) at index
- * (g/2)*N + n, a missing group g+1 = K/32 having bits 0 and scale 0, so the
- * words of one group pair for consecutive outputs are contiguous.
+ * q1_sign_gemm takes) for the calls below, in three sections (P = 16 * N *
+ * ceil(K/64) bytes each for the first two):
+ *   [0, P)      for the table kernels (q1_sign_gemv, q1_sign_gemm_lut4):
+ *               for each output n and pair of 32-weight groups (g, g+1),
+ *               g even, the u32x4 {bits[n][g], bits[n][g+1], scale[n][g],
+ *               scale[n][g+1]} (scales as f32 bit patterns) at index
+ *               (g/2)*N + n, a missing group g+1 = K/32 having bits 0 and
+ *               scale 0, so the words of one group pair for consecutive
+ *               outputs are contiguous;
+ *   [P, 2P)     for the matrix-core GEMM: for each group g and output n the
+ *               u32x2 {bits[n][g], sh | sl << 16} at index g*N + n, sh and
+ *               sl the fp16 high and low parts of scale[n][g] * 2^c_n;
+ *   [2P, 2P+4N) the int32 c_n per output: the exponent that puts the
+ *               output's largest |scale| in [2^14, 2^15) (0 if all are 0).
  *   w_bits, w_scales  as for q1_sign_gemm, 4-byte aligned.
  *   w_packed          device, q1_sign_packed_bytes(N, K) bytes, 16-byte
  *                     aligned; written whole.
@@ -200,7 +219,7 @@ int q1_sign_pack(const uint32_t *w_bits, const float *w_scales, int64_t N, int64
 /* q1_sign_gemm on weights packed once by q1_sign_pack (no per-call
  * regrouping launch); same numerics and bits as q1_sign_gemm. The workspace
  * holds only the split activations and row exponents: at least
- * 4*K*M16 + 4*M16 bytes (M16 = M rounded up to 16), so any size
+ * 4*K*M16 + 32*M16 bytes (M16 = M rounded up to 16), so any size
  * q1_sign_gemm_workspace_bytes(M, N, K) returns is enough. x, w_packed and
  * workspace 16-byte aligned, y 4-byte. Errors: GD_EINVAL, GD_ESHAPE,
  * GD_EALIGN, GD_ERANGE, GD_EHIP. */

@@ -93,17 +93,18 @@ def test_validation_without_gpu(gd):
     assert L.q1_sign_gemm(FAKE + 4, FAKE, FAKE, FAKE, 4, 4, 128, FAKE, WS, None) == E["align"]
     assert L.q1_sign_gemm(FAKE, FAKE, FAKE, FAKE, 4, 4, 128, FAKE + 8, WS, None) == E["align"]
     assert L.q1_sign_gemm(FAKE, FAKE, FAKE, FAKE, 0, 4, 128, FAKE, WS, None) == E["inval"]
-    # workspace: 4*K bytes per token (padded to 16), 4 per padded token, 16 per output and group pair
+    # workspace: 4*K bytes per token (padded to 16), 32 per padded token, 16 per output and group
+    # pair, 4 per output
     ws = ctypes.c_size_t()
     assert L.q1_sign_gemm_workspace_bytes(17, 5, 128, ctypes.byref(ws)) == 0
-    assert ws.value == 32 * 128 * 4 + 32 * 4 + 5 * 2 * 16
+    assert ws.value == 32 * 128 * 4 + 32 * 32 + 5 * 2 * 16 + 5 * 4
     assert L.q1_sign_gemm_workspace_bytes(17, 5, 96, ctypes.byref(ws)) == 0
-    assert ws.value == 32 * 96 * 4 + 32 * 4 + 5 * 2 * 16
+    assert ws.value == 32 * 96 * 4 + 32 * 32 + 5 * 2 * 16 + 5 * 4
     assert L.q1_sign_gemm_workspace_bytes(17, 5, 100, ctypes.byref(ws)) == E["shape"]
     assert L.q1_sign_gemm(FAKE, FAKE, FAKE, FAKE, 17, 5, 128, FAKE, 32 * 128 * 4, None) == E["range"]
-    # packed sign-bit weights: 16 bytes per output and group pair
-    assert L.q1_sign_packed_bytes(5, 128, ctypes.byref(ws)) == 0 and ws.value == 5 * 2 * 16
-    assert L.q1_sign_packed_bytes(5, 96, ctypes.byref(ws)) == 0 and ws.value == 5 * 2 * 16
+    # packed sign-bit weights: two sections of 16 bytes per output and group pair, 4 per output
+    assert L.q1_sign_packed_bytes(5, 128, ctypes.byref(ws)) == 0 and ws.value == 2 * 5 * 2 * 16 + 5 * 4
+    assert L.q1_sign_packed_bytes(5, 96, ctypes.byref(ws)) == 0 and ws.value == 2 * 5 * 2 * 16 + 5 * 4
     assert L.q1_sign_packed_bytes(5, 100, ctypes.byref(ws)) == E["shape"]
     assert L.q1_sign_pack(FAKE, FAKE, 4, 128, FAKE + 4, None) == E["align"]
     assert L.q1_sign_pack(FAKE, None, 4, 128, FAKE, None) == E["inval"]

@@ -50,7 +50,8 @@ def test_integer_exact_pins_tiling(gd):
     assert np.array_equal(y, oracle.sign_gemm_f64(x, bits, scales))
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 1, 32), (16, 16, 32), (17, 33, 96), (130, 129, 512), (64, 256, 4096)])
+@pytest.mark.parametrize("M,N,K", [(1, 1, 32), (16, 16, 32), (17, 33, 96), (130, 129, 512), (64, 256, 4096),
+                                   (33, 70, 8224)])
 def test_ragged_shapes(gd, M, N, K):
     x, bits, scales = wl.sign_gemm_inputs(M, N, K, seed=M + N + K)
     y = run(gd, x, bits, scales)
@@ -104,13 +105,43 @@ def test_row_magnitudes(gd):
             assert rel_err(y[r:r + 1], want[r:r + 1]) <= TOL, r
 
 
+@pytest.mark.parametrize("packed", [False, True])
+def test_output_scale_magnitudes(gd, packed):
+    """Outputs whose scales sit 40 decades apart, an all-zero output, and an
+    output whose own scales span 23 decades: each output column meets the
+    bar against its own largest value and the zero output is 0 (each output
+    has its own power-of-two normalisation)."""
+    M, N, K = 40, 8, 1024
+    x, bits, scales = wl.sign_gemm_inputs(M, N, K, seed=11)
+    mags = np.array([1e-20, 1e-4, 1.0, 1e4, 1e20, 0.0, 1.0, 1.0])
+    sc = scales.astype(np.float64) * mags[:, None]
+    sc[6] = np.geomspace(1e-20, 1e3, K // 32)
+    sc[7, ::3] *= -1.0
+    sc = sc.astype(np.float32)
+    want = oracle.sign_gemm_f64(x, bits, sc)
+    if packed:
+        wp = torch.empty(gd.q1_sign_packed_bytes(N, K), dtype=torch.uint8, device="cuda")
+        gd.q1_sign_pack(dev(bits.view(np.int32)), dev(sc), N, K, wp)
+        yt = torch.full((M * N,), float("nan"), device="cuda")
+        gd.q1_sign_gemm_packed(dev(x), wp, yt, M, N, K)
+        torch.cuda.synchronize()
+        y = yt.cpu().numpy().reshape(M, N)
+    else:
+        y = run(gd, x, bits, sc)
+    for n in range(N):
+        if mags[n] == 0.0:
+            assert np.all(y[:, n] == 0.0)
+        else:
+            assert rel_err(y[:, n:n + 1], want[:, n:n + 1]) <= TOL, n
+
+
 def test_explicit_workspace_and_reuse(gd):
     """A caller-owned workspace of exactly the reported size gives the same
     bits as the cached one, and reusing it for a second, smaller call on the
     same stream leaves no trace of the first."""
     M, N, K = 100, 200, 640
     need = gd.q1_sign_gemm_workspace_bytes(M, N, K)
-    assert need == 112 * K * 4 + 112 * 4 + N * (K // 64) * 16
+    assert need == 112 * K * 4 + 112 * 32 + N * (K // 64) * 16 + N * 4
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     x, bits, scales = wl.sign_gemm_inputs(M, N, K, seed=3)
     y1 = torch.empty(M * N, device="cuda")

@@ -44,7 +44,9 @@ def pack(gd, bits, scales):
 
 
 def packed_ref(bits, scales):
-    """The packed layout written from the header's definition."""
+    """The packed layout written from the header's definition: the table
+    kernels' section, the matrix-core section (only its first 8*N*G bytes
+    are defined) and the per-output exponents, as uint32 arrays."""
     N, G = bits.shape
     G2 = (G + 1) // 2
     out = np.zeros((G2, N, 4), dtype=np.uint32)
@@ -55,7 +57,27 @@ def packed_ref(bits, scales):
         if 2 * p + 1 < G:
             out[p, :, 1] = bits[:, 2 * p + 1]
             out[p, :, 3] = sb[:, 2 * p + 1]
-    return out.reshape(-1)
+    smax = np.max(np.abs(scales), axis=1)
+    c = np.where(smax > 0, 15 - np.frexp(smax)[1], 0).astype(np.int32)
+    v = np.ldexp(scales, c[:, None]).astype(np.float32)            # exact: a power-of-two scaling
+    sh = v.astype(np.float16)
+    sl = (v - sh.astype(np.float32)).astype(np.float16)           # v - sh is exact in f32
+    hl = sh.view(np.uint16).astype(np.uint32) | (sl.view(np.uint16).astype(np.uint32) << 16)
+    mc = np.zeros((G, N, 2), dtype=np.uint32)
+    mc[:, :, 0] = bits.T
+    mc[:, :, 1] = hl.T
+    return out.reshape(-1), mc.reshape(-1), c.view(np.uint32)
+
+
+def check_packed(wp, bits, scales):
+    N, G = bits.shape
+    words = wp.cpu().numpy().view(np.uint32)
+    tab, mc, cexp = packed_ref(bits, scales)
+    sec = tab.size                                   # 4 words per output and group pair
+    assert words.size == 2 * sec + N
+    assert np.array_equal(words[:sec], tab), "table kernels' section"
+    assert np.array_equal(words[sec:sec + mc.size], mc), "matrix-core section"
+    assert np.array_equal(words[2 * sec:], cexp), "output exponents"
 
 
 def run(gd, fn, x, wp, N):
@@ -71,7 +93,26 @@ def test_pack_layout(gd, N, K):
     _, bits, scales = wl.sign_gemm_inputs(1, N, K, seed=N + K)
     wp = pack(gd, bits, scales)
     torch.cuda.synchronize()
-    assert np.array_equal(wp.cpu().numpy().view(np.uint32), packed_ref(bits, scales))
+    check_packed(wp, bits, scales)
+
+
+def test_pack_layout_extreme_scales(gd):
+    """Outputs whose scales span many decades, an all-zero output, negative
+    and subnormal scales: the matrix-core section's exponents and fp16
+    pairs follow the definition exactly."""
+    N, K = 6, 256
+    _, bits, scales = wl.sign_gemm_inputs(1, N, K, seed=77)
+    scales = scales.astype(np.float64)
+    scales[0] *= 1e-30
+    scales[1] *= 1e30
+    scales[2] = 0.0
+    scales[3] *= -1.0
+    scales[4, ::2] = 1e-41                    # f32 subnormals beside normal values
+    scales[5] = np.geomspace(1e-20, 1e3, K // 32)
+    scales = scales.astype(np.float32)
+    wp = pack(gd, bits, scales)
+    torch.cuda.synchronize()
+    check_packed(wp, bits, scales)
 
 
 @pytest.mark.parametrize("M,N,K", [(17, 33, 96), (130, 129, 512), (512, 4096, 4096)])
