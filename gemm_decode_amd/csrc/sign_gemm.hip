@@ -64,7 +64,7 @@ typedef const u32x2 __attribute__((address_space(1))) *g_u2;
 typedef const f32x2 __attribute__((address_space(1))) *g_f2;
 typedef const float __attribute__((address_space(1))) *g_f1;
 
-constexpr int kPrepThreads = 256;
+constexpr int kPrepThreads = 512;
 constexpr int kThreads = 512;             // 8 waves: the K eighths of one 64 x 128 tile
 constexpr int kTM = 64, kTN = 128;
 constexpr int kKParts = kThreads / 64;    // K parts of the GEMM (one per wave), each with its own row exponents
@@ -128,9 +128,11 @@ __global__ __launch_bounds__(kPrepThreads) void sign_wpack_kernel(const uint32_t
 // gets the exponent c_n that puts its largest |scale| in [2^14, 2^15), and
 // each group's scale s becomes v = s * 2^c_n split as h = fp16(v), l =
 // fp16(v - h) (v - h is exact in f32). Group g of output n is the u32x2
-// {bits, h | l << 16} at g*N + n. Sixteen threads per output: they find its
-// largest |scale| together, then write its groups.
-constexpr int kBpCols = kPrepThreads / 16;   // outputs per workgroup
+// {bits, h | l << 16} at g*N + n. A workgroup packs 16 outputs: its waves
+// read the outputs' scale and sign rows 64 groups at a time (256-byte
+// reads), and each 64-group chunk turns around in LDS so that the 16
+// outputs' words of one group go out as one 128-byte write.
+constexpr int kBpCols = 16;   // outputs per workgroup
 
 __device__ __forceinline__ uint32_t split_scale(float s, int e) {
     const float v = __builtin_ldexpf(s, e);
@@ -142,44 +144,47 @@ __device__ __forceinline__ uint32_t split_scale(float s, int e) {
 
 __device__ __forceinline__ void bpack_cols(const uint32_t *bits_g, const float *scales_g, int64_t N, int64_t G,
                                            u32x2 *__restrict__ wb, int32_t *__restrict__ cexp, int64_t blk) {
-    const int tid = threadIdx.x;
-    const int64_t n = blk * kBpCols + tid / 16;
-    const int c = tid % 16;
-    const bool live = n < N;
-    const int64_t nl = live ? n : N - 1;
-    const float *srow = scales_g + nl * G;
-    const uint32_t *brow = bits_g + nl * G;
-    // groups c, c + 16, ... in chunks of 128, each chunk's loads issued together
-    float smax = 0.0f;
-    for (int64_t g0 = 0; g0 < G; g0 += 128) {
-        float v[8];
+    constexpr int kWaves = kPrepThreads / 64, kRows = kBpCols / kWaves;   // outputs per wave
+    __shared__ u32x2 tile[kBpCols][65];
+    __shared__ int ex[kBpCols];
+    const int tid = threadIdx.x, w = tid / 64, l = tid % 64;
+    const int64_t n0 = blk * kBpCols;
+    // 1. each output's largest |scale| and exponent
 #pragma unroll
-        for (int k = 0; k < 8; k++) {
-            const int64_t g = g0 + c + 16 * k;
-            v[k] = g < G ? srow[g] : 0.0f;
+    for (int k = 0; k < kRows; k++) {
+        const int r = w + kWaves * k;
+        const int64_t n = n0 + r;
+        float m = 0.0f;
+        if (n < N)
+            for (int64_t g = l; g < G; g += 64) m = fmaxf(m, fabsf(scales_g[n * G + g]));
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+        if (l == 0) {
+            const int e = m > 0.0f ? 15 - __builtin_amdgcn_frexp_expf(m) : 0;
+            ex[r] = e;
+            if (n < N) cexp[n] = e;
         }
-#pragma unroll
-        for (int k = 0; k < 8; k++) smax = fmaxf(smax, fabsf(v[k]));
     }
+    __syncthreads();
+    // 2. 64 groups at a time: rows in, turned around, groups out
+    for (int64_t g0 = 0; g0 < G; g0 += 64) {
 #pragma unroll
-    for (int o = 8; o > 0; o >>= 1) smax = fmaxf(smax, __shfl_xor(smax, o));   // within the output's 16 lanes
-    const int e = smax > 0.0f ? 15 - __builtin_amdgcn_frexp_expf(smax) : 0;
-    if (live && c == 0) cexp[n] = e;
-    if (!live) return;
-    for (int64_t g0 = 0; g0 < G; g0 += 128) {
-        float v[8];
-        uint32_t b[8];
-#pragma unroll
-        for (int k = 0; k < 8; k++) {
-            const int64_t g = g0 + c + 16 * k;
-            v[k] = g < G ? srow[g] : 0.0f;
-            b[k] = g < G ? brow[g] : 0u;
+        for (int k = 0; k < kRows; k++) {
+            const int r = w + kWaves * k;
+            const int64_t n = n0 + r, g = g0 + l;
+            u32x2 v = {0u, 0u};
+            if (n < N && g < G) v = u32x2{bits_g[n * G + g], split_scale(scales_g[n * G + g], ex[r])};
+            tile[r][l] = v;
         }
+        __syncthreads();
 #pragma unroll
-        for (int k = 0; k < 8; k++) {
-            const int64_t g = g0 + c + 16 * k;
-            if (g < G) wb[g * N + n] = u32x2{b[k], split_scale(v[k], e)};
+        for (int k = 0; k < 64 * kBpCols / kPrepThreads; k++) {
+            const int i = tid + kPrepThreads * k;
+            const int gl = i / kBpCols, r = i % kBpCols;
+            const int64_t g = g0 + gl, n = n0 + r;
+            if (g < G && n < N) wb[g * N + n] = tile[r][gl];
         }
+        __syncthreads();
     }
 }
 
@@ -194,12 +199,12 @@ __global__ __launch_bounds__(kPrepThreads) void sign_bpack_kernel(const uint32_t
 // runs), finds each row's largest |x| in that part, so that (row, part) has
 // its own exponent e (x * 2^e in [2^14, 2^15)), and writes the part's
 // 2 KiB blocks whole. Lane 16q + r of wave w handles row 16t + r, quarter q
-// of groups w, w + 4, ... of the part: the lane layout of the blocks.
+// of groups w, w + 8, ... of the part: the lane layout of the blocks.
 constexpr int kParts = kKParts;
 
 __device__ __forceinline__ void split_tile(const float *x_g, int64_t M, int64_t K, uint32_t *__restrict__ xs,
                                            int32_t *__restrict__ rexp, int64_t t, int p) {
-    static_assert(kPrepThreads == 256, "four waves per split workgroup");
+    constexpr int kW = kPrepThreads / 64;   // waves; wave w takes groups w, w + kW, ... of the part
     const int64_t G = K / 32, Gp = (G + kParts - 1) / kParts;
     const int64_t g0 = p * Gp;
     int64_t gn = G - g0;
@@ -208,18 +213,18 @@ __device__ __forceinline__ void split_tile(const float *x_g, int64_t M, int64_t 
     const int64_t m = t * 16 + r;
     const bool live = m < M;
     const g_f4 row = (g_f4)(x_g + (live ? m : 0) * K);
-    __shared__ float red[4][16];
+    __shared__ float red[kW][16];
     // Up to kHeld groups per lane stay in registers between the two passes
-    // (K <= 4096 * kHeld / 4); longer parts are read again for the second.
-    constexpr int kHeld = 4;
-    const bool held = gn <= 4 * kHeld;
+    // (K <= 256 * kW * kHeld); longer parts are read again for the second.
+    constexpr int kHeld = 2;
+    const bool held = gn <= kW * kHeld;
     const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
     f32x4 ha[kHeld], hb[kHeld];
     float amax = 0.0f;
     if (held) {
 #pragma unroll
         for (int k = 0; k < kHeld; k++) {
-            const int64_t i = w + 4 * k;
+            const int64_t i = w + kW * k;
             const bool in = live && i < gn;
             ha[k] = in ? row[8 * (g0 + i) + q] : zero;
             hb[k] = in ? row[8 * (g0 + i) + 4 + q] : zero;
@@ -227,7 +232,7 @@ __device__ __forceinline__ void split_tile(const float *x_g, int64_t M, int64_t 
             for (int e = 0; e < 4; e++) amax = fmaxf(amax, fmaxf(fabsf(ha[k][e]), fabsf(hb[k][e])));
         }
     } else if (live) {
-        for (int64_t i = w; i < gn; i += 4) {
+        for (int64_t i = w; i < gn; i += kW) {
             const int64_t g = g0 + i;
             const f32x4 a = row[8 * g + q], b = row[8 * g + 4 + q];
 #pragma unroll
@@ -238,7 +243,9 @@ __device__ __forceinline__ void split_tile(const float *x_g, int64_t M, int64_t 
     amax = fmaxf(amax, __shfl_xor(amax, 32));
     if (q == 0) red[w][r] = amax;
     __syncthreads();
-    const float rm = fmaxf(fmaxf(red[0][r], red[1][r]), fmaxf(red[2][r], red[3][r]));
+    float rm = red[0][r];
+#pragma unroll
+    for (int k = 1; k < kW; k++) rm = fmaxf(rm, red[k][r]);
     const int e = rm > 0.0f ? 15 - __builtin_amdgcn_frexp_expf(rm) : 0;
     if (w == 0 && q == 0) rexp[m * kParts + p] = e;   // padded rows included (e = 0)
 
@@ -262,9 +269,9 @@ __device__ __forceinline__ void split_tile(const float *x_g, int64_t M, int64_t 
     if (held) {
 #pragma unroll
         for (int k = 0; k < kHeld; k++)
-            if (w + 4 * k < gn) emit(g0 + w + 4 * k, ha[k], hb[k]);
+            if (w + kW * k < gn) emit(g0 + w + kW * k, ha[k], hb[k]);
     } else {
-        for (int64_t i = w; i < gn; i += 4) {
+        for (int64_t i = w; i < gn; i += kW) {
             const int64_t g = g0 + i;
             emit(g, live ? row[8 * g + q] : zero, live ? row[8 * g + 4 + q] : zero);
         }
