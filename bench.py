@@ -59,26 +59,27 @@ _TRAFFIC = {
     "q1_small": ("q1.hip", "d26001046218be80", {"7646 x 256x1024": (139143.5, 7646.0)}),
     "ternary": ("ternary.hip", "8f60006b03cd5750",
                 {"2560x2560": (101998.1, 1200.0), "6912x2560": (137366.5, 1620.1), "2560x6912": (65806.6, 300.0)}),
-    "blockq8": ("blockq8.hip", "123bb6b095593ab2", {"m1": (26534.5, 192.4), "m16": (27477.1, 3072.0)}),
-    "sign": ("sign_gemm.hip", "8079002f8fe77553",
-             {"prep": (6201.5, 12304.0), "gemm": (21352.5, 9728.0)}),
+    "blockq8": ("blockq8.hip", "f40db311846149b4", {"m1": (26820.7, 192.6), "m16": (27505.7, 3072.0)}),
+    # per call on the caller's words: prep (split + weight pack) + gemm
+    "sign": ("sign_gemm.hip", "9a7f346a8abf876e",
+             {"prep": (6187.0, 12432.0), "gemm": (20670.0, 8192.0)}),
     "sign_lut": ("sign_lut.hip", "c9273fa6aeb445b1",
                  {"4096x4096": (2170.0, 16.0), "14336x4096": (7290.0, 56.0), "lut4": (35127.5, 8192.0)}),
-    "quant": ("quantize.hip", "aa440e939b0b9a5a",
-              {"q8_0_decode": (266.5, 136.0), "q8_0_batch_256MiB": (131082.5, 69632.0),
-               "int8_planes_decode_step": (522.6 + 536.5, 227.8 + 203.4),
-               "int8_planes_batch_256MiB": (131147.4, 66074.8)}),
+    "quant": ("quantize.hip", "22fc8bec22001fef",
+              {"q8_0_decode": (266.5, 136.0), "q8_0_batch_256MiB": (131082.9, 69632.0),
+               "int8_planes_decode_step": (540.5 + 572.6, 227.8 + 203.4),
+               "int8_planes_batch_256MiB": (131166.1, 66080.5)}),
     # per call: split kernel + merge kernel
-    "attention": ("attention.hip", "90a47144e8c51bc0",
-                  {"kv4096": (16453.5 + 605.0, 1040.0 + 16.0),
-                   "kv32768": (131141.5 + 605.0, 1040.0 + 16.0)}),
+    "attention": ("attention.hip", "849b98fd33aa133e",
+                  {"kv4096": (16453.1 + 605.0, 1040.0 + 16.0),
+                   "kv32768": (131141.2 + 605.0, 1040.0 + 16.0)}),
 }
 
 # Hardware MFMA busy fraction (rocprofv3 SQ_VALU_MFMA_BUSY_CYCLES over the
 # dispatch's duration x 1024 SIMDs at 2.4 GHz), for the kernel source measured.
 _MFMA_BUSY = {
-    "sign_gemm_kernel": ("sign_gemm.hip", "8079002f8fe77553", 0.286),
-    "blockq8_mfma_kernel": ("blockq8.hip", "123bb6b095593ab2", 0.086),
+    "sign_gemm_kernel": ("sign_gemm.hip", "9a7f346a8abf876e", 0.456),
+    "blockq8_mfma_kernel": ("blockq8.hip", "f40db311846149b4", 0.078),
 }
 
 
@@ -142,6 +143,13 @@ def compact(full: dict) -> dict:
         if k in full:
             out[k] = full[k]
     return out
+
+
+def with_floor(rec: dict, floor_us: float) -> dict:
+    """A decode-size entry with its time as a multiple of the launch floor."""
+    if rec.get("us") is not None and floor_us > 0:
+        rec["x_launch_floor"] = _r(rec["us"] / floor_us, 2)
+    return rec
 
 
 # ----------------------------------------------------------------- timing
@@ -211,6 +219,15 @@ def _time_launches(torch, launch, n, warmup, batches):
     del g
     return med, {"min_us": _r(lo * 1e6, 3), "max_us": _r(hi * 1e6, 3), "batches": batches,
                  "launches_per_batch": reps * n}
+
+
+def measured_launch_floor(gd, torch, batches: int):
+    """Per-launch time of a trivial kernel (a 4 KiB fill) replayed 64 times in
+    a HIP graph: the floor under any one launch on this machine, against which the
+    latency-bound decode-size launches are read. Returns (us, timing)."""
+    buf = torch.empty(4096, dtype=torch.uint8, device="cuda")
+    per, st = _time_launches(torch, lambda k: gd.gemm_decode_fill(buf, k + 1), 64, 3, batches)
+    return per * 1e6, st
 
 
 def measured_read_ceiling(gd, torch, gib: float = 2.0, passes: int = 8, reps: int = 5):
@@ -662,7 +679,8 @@ def bench_sign(args, gd, torch):
                              None if sg_traffic is None else sum(sg_traffic.values()),
                              traffic_per_kernel=sg_traffic,
                              kernel="q1_sign_gemm call (all its kernels)",
-                             flops_per_launch=flops, mfma_busy_hw=busy),
+                             flops_per_launch=flops, mfma_busy_hw=busy,
+                             mfma_issued_per_useful=3),
         "parity_rel_err": rel,
         "cpu_baseline": {"value": _r(flops / t_full / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
                          "kind": "oracle", "sample": f"all 512 x 4096 outputs (f64 oracle), {t_full:.2f} s"},
@@ -1067,7 +1085,11 @@ def main():
         out = bench_q1(args, gd, torch)
     else:
         out = {"metric": METRIC, "note": "Q1 workload skipped (--workload)"}
+    floor_us, floor_st = measured_launch_floor(gd, torch, args.batches)
+    out["launch_floor_us"] = _r(floor_us, 3)
     full = dict(out)
+    full["launch_floor"] = {"us": _r(floor_us, 3), "timing": floor_st,
+                            "kernel": "4 KiB fill, 64 launches per HIP graph"}
     if args.workload != "q1":
         extra = {}
         steps = [("cfg0_q1_256x1024", "q1small", bench_q1_small),
@@ -1088,10 +1110,11 @@ def main():
                 for m, r in rec.items():
                     short[f"cfg3_blockq8_{m}"] = compact(r)
             elif key in ("next1_q1_small_m", "next2_act_quant", "next4_decode_attention"):
-                short[key] = {sub: compact(r) for sub, r in rec.items()}
+                short[key] = {sub: with_floor(compact(r), floor_us) for sub, r in rec.items()}
             elif key == "cfg2_sign_gemm":
                 short[key] = compact(rec)
-                short["next3_sign_gemv"] = {sub: compact(r) for sub, r in rec["decode_gemv"].items()}
+                short["next3_sign_gemv"] = {sub: with_floor(compact(r), floor_us)
+                                            for sub, r in rec["decode_gemv"].items()}
             else:
                 short[key] = compact(rec)
         out["workloads"] = short

@@ -90,7 +90,7 @@ _declare()
 
 # The problem structs below mirror the header of this ABI version; a library
 # built from other sources would read them with another layout.
-ABI_VERSION = 3
+ABI_VERSION = 4
 if _lib.gemm_decode_abi_version() != ABI_VERSION:
     raise ImportError(f"{LIB_PATH} has ABI version {_lib.gemm_decode_abi_version()}, this binding needs "
                       f"{ABI_VERSION}: rebuild it")

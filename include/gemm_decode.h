@@ -53,7 +53,7 @@ const char *gemm_decode_status_string(int status);
 const char *gemm_decode_last_error(void);
 /* ABI version of this header (incremented on incompatible changes). */
 int gemm_decode_abi_version(void);
-#define GEMM_DECODE_ABI_VERSION 3
+#define GEMM_DECODE_ABI_VERSION 4
 
 /* ====================================================================
  * Q1_0 . q8_0  ("browseml-gpu.js": header comment "The arithmetic, as the

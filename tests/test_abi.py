@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol(gd):
     lib = ctypes.CDLL(gd.LIB_PATH)
     missing = [n for n in declared_functions() if not hasattr(lib, n)]
     assert not missing, missing
-    assert lib.gemm_decode_abi_version() == gd.ABI_VERSION == 3
+    assert lib.gemm_decode_abi_version() == gd.ABI_VERSION == 4
 
 
 def test_status_strings(gd):
