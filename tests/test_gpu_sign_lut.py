@@ -129,13 +129,14 @@ def test_packed_gemm_matches_unpacked(gd, M, N, K):
 
 
 GEMV_SHAPES = [(1, 1, 32), (1, 63, 96), (1, 4096, 4096), (1, 14336, 4096), (1, 4096, 14336), (3, 130, 8224),
-               (2, 200, 4096 + 64)]
+               (2, 200, 4096 + 64), (1, 8192, 2080), (2, 8193, 2080)]
 
 
 @pytest.mark.parametrize("M,N,K", GEMV_SHAPES)
 def test_gemv_parity(gd, M, N, K):
     """Decode shapes (4096x4096, 14336x4096, and 4096x14336 over several
-    table chunks), an odd group count, and K past a chunk by one pair."""
+    table chunks), an odd group count, K past a chunk by one pair, and N on
+    both sides of the switch from 16 to 64 outputs per workgroup."""
     x, bits, scales = wl.sign_gemm_inputs(M, N, K, seed=M * 7 + N + K)
     y = run(gd, "q1_sign_gemv", x, pack(gd, bits, scales), N)
     assert rel_err(y, oracle.sign_gemm_f64(x, bits, scales, nthreads=oracle.max_threads())) <= TOL
