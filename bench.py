@@ -571,9 +571,8 @@ def bench_q1_small(args, gd, torch):
 
 def bench_q1_mm(args, gd, torch):
     """Q1_0.q8_0 with several activation columns (P1's multi-column Q1_MM,
-    the prompt side of the same method) on the 14336x4096 decode weight: the
-    columns share one read of the weights and keep the bits of their own
-    batch-1 GEMVs. Weight copies rotate over a ring > 1 GiB (one graph of
+    the prompt side of the same method) on the 14336x4096 decode weight: one
+    launch, each column its own GEMV with the bits of its batch-1 result. Weight copies rotate over a ring > 1 GiB (one graph of
     launches covers the whole ring, so no copy is read again from cache)."""
     import oracle
     cfg = wl.Q1_DECODE[1]
@@ -604,11 +603,11 @@ def bench_q1_mm(args, gd, torch):
         launch_bytes = w_bytes + M * ((K // 32) * 34 + rows * 4)
         out[f"m{M}"] = {
             "workload": f"Q1_0.q8_0 small-M: {M} activation columns x 14336x4096 weight",
-            "metric": "HBM GB/s (weights read once)", "value": _r(launch_bytes / per / 1e9, 1), "unit": "GB/s",
+            "metric": "HBM GB/s (weight bytes counted once)", "value": _r(launch_bytes / per / 1e9, 1), "unit": "GB/s",
             "us": _r(per * 1e6, 2), "timing": st,
             "gemv_equivalent_GBps": _r(M * q1_gemv_bytes(rows, K) / per / 1e9, 1),
             "roofline": roofline(launch_bytes / per / 1e9, HBM_PEAK_GBPS, "GB/s", "hbm",
-                                 kernel="q1 multi-column kernels", bytes_per_launch=launch_bytes),
+                                 kernel="q1_gemv_kernel (one grid row per column)", bytes_per_launch=launch_bytes),
             "parity_mismatches": mism,
             "cpu_baseline": {"value": _r(M * q1_gemv_bytes(rows, K) / t_cpu / 1e9, 4),
                              "unit": "GB/s (GEMV-equivalent)", "cores": threads, "kind": "oracle",

@@ -32,16 +32,15 @@ constexpr int kThreads = 512;             // 8 waves: 4 tiles x 2 halves
 constexpr int kRowsPerWG = 256;
 constexpr int kChunkBlocks = 32;          // blocks whose tables fit in LDS
 constexpr int kTableFloats = kChunkBlocks * 32 * 16;   // 64 KiB
-constexpr int kGroupsPerThread = kChunkBlocks * 32 / kThreads;   // 2
 // A single GEMV of up to this many 256-row blocks takes the one-chain-per-
 // thread kernel (latency); larger ones fill the chip with 256-row blocks.
 constexpr int64_t kLatMaxRowBlocks = 64;
 constexpr int64_t kLatWideRows = 8192;
-// While n_act * rows stays within this (about four waves per SIMD in all), a
+// While n_act * rows stays within this (about two waves per SIMD in all), a
 // few-row product runs as independent one-chain-per-thread GEMVs, one per
-// column (each re-reads the weights, mostly from cache), rather than the
-// kernel that shares one read of them across columns.
-constexpr int64_t kLatMaxColumnRows = 32768;
+// column; above it each column runs the 256-row kernel (both re-read the
+// weights per column, mostly from cache).
+constexpr int64_t kLatMaxColumnRows = 16384;
 // Threads per workgroup of the grouped launch (two per row of a 64-row tile).
 constexpr int kGroupedThreads = 512;
 
@@ -506,194 +505,6 @@ __global__ __launch_bounds__(NT) void q1_gemv_grouped_small_kernel(const gd_q1_p
     }
 }
 
-// ------------------------------------------------------- several columns
-// Small-M product (P1's multi-column Q1_MM): MC activation columns against
-// the same weights in one workgroup, every column's chains in the stated
-// order, so each column has the bits of its own batch-1 GEMV. LDS holds the
-// tables of all MC columns for a chunk of CB = 32/MC blocks (64 KiB); a
-// block's 16 table offsets are extracted once and serve every column, and
-// the weights are read once per group of MC columns. Chunks are handled in
-// pairs so a block's place in its 8-block scale group is a constant.
-template <int MC>
-struct McShape {
-    static constexpr int CB = 32 / MC;                 // blocks per chunk
-    static constexpr int NS = (CB + 7) / 8;            // scale groups per chunk
-};
-
-// Table groups g = ((c*CB + u)*4 + k)*8 + l of a chunk (1024 of them, two
-// per thread), for chunk blocks i0 .. i0+CB-1 of columns c0 .. c0+MC-1.
-// Columns past ncols and blocks past nb read clamped positions; their
-// entries are never used.
-template <int MC, int NT>
-__device__ __forceinline__ void mc_table_loads(TableRawN<NT> &raw, const uint16_t *a_generic, int64_t col_halves,
-                                               int ncols, int64_t i0, int cb) {
-    constexpr int CB = McShape<MC>::CB;
-    const auto a = (const uint16_t __attribute__((address_space(1))) *)a_generic;
-#pragma unroll
-    for (int j = 0; j < TableRawN<NT>::NG; j++) {
-        const int g = threadIdx.x + NT * j;
-        const int c = g / (CB * 32), rem = g % (CB * 32);
-        int u = rem >> 5;
-        const int k = (rem >> 3) & 3, l = rem & 7;
-        u = u < cb ? u : cb - 1;
-        const int cc = c < ncols ? c : ncols - 1;
-        const auto blk = a + cc * col_halves + ((i0 + u) * 4 + k) * 17;   // 34 bytes = 17 halves
-        raw.d[j] = blk[0];
-        raw.q01[j] = blk[1 + 2 * l];
-        raw.q23[j] = blk[2 + 2 * l];
-    }
-}
-
-// The 16 table reads of half H of one block against one column's tables at t.
-template <int H>
-__device__ __forceinline__ void half_reads_at(const char *t, const u32x2 &wb, float (&v)[16]) {
-    const uint32_t wm[2] = {wb.x, wb.y};
-#pragma unroll
-    for (int m = 0; m < 2; m++) {
-        const uint32_t w = wm[m];
-        const uint32_t wr = __builtin_amdgcn_alignbit(w, w, 4);
-        const char *t0 = t + (2 * m) * 512 + (4 * H) * 64;
-        const char *t1 = t0 + 512;
-        v[8 * m + 0] = *reinterpret_cast<const float *>(t0 + 0 * 64 + grp<0>(w));
-        v[8 * m + 1] = *reinterpret_cast<const float *>(t0 + 1 * 64 + grp<1>(w));
-        v[8 * m + 2] = *reinterpret_cast<const float *>(t0 + 2 * 64 + grp<2>(w));
-        v[8 * m + 3] = *reinterpret_cast<const float *>(t0 + 3 * 64 + grp<3>(w));
-        v[8 * m + 4] = *reinterpret_cast<const float *>(t1 + 0 * 64 + grp<0>(wr));
-        v[8 * m + 5] = *reinterpret_cast<const float *>(t1 + 1 * 64 + grp<1>(wr));
-        v[8 * m + 6] = *reinterpret_cast<const float *>(t1 + 2 * 64 + grp<2>(wr));
-        v[8 * m + 7] = *reinterpret_cast<const float *>(t1 + 3 * 64 + grp<3>(wr));
-    }
-}
-
-template <int MC>
-struct McChunk {
-    u32x2 w[McShape<MC>::CB];
-    u32x4 s8[McShape<MC>::NS];
-};
-
-// Weights of chunk j (blocks past nb and scale groups past the last read
-// clamped positions; never used).
-template <int MC>
-__device__ __forceinline__ void mc_load(const RowPtrs &rp, int64_t j, int64_t nb, McChunk<MC> &b) {
-    constexpr int CB = McShape<MC>::CB, NS = McShape<MC>::NS;
-#pragma unroll
-    for (int u = 0; u < CB; u++) {
-        int64_t i = j * CB + u;
-        i = i < nb ? i : nb - 1;
-        b.w[u] = rp.bits[i * 128];   // plain: other column groups re-read these weights
-    }
-    const int64_t ng = (nb + 7) / 8;
-#pragma unroll
-    for (int n = 0; n < NS; n++) {
-        int64_t gi = (j * CB) / 8 + n;
-        gi = gi < ng ? gi : ng - 1;
-        b.s8[n] = rp.sc[gi * 64];
-    }
-}
-
-// Compute one chunk: block u of it is block P*CB + u of its 8-block scale
-// pair position P (0 or 1 for CB = 4, else 0). Reads of column c+1 are issued
-// before the arithmetic of column c.
-template <int H, int MC, int P>
-__device__ __forceinline__ void mc_compute(const char *tab, const McChunk<MC> &b, int cb, float (&acc)[MC][4]) {
-    constexpr int CB = McShape<MC>::CB;
-#pragma unroll
-    for (int u = 0; u < CB; u++) {
-        if (u < cb) {                                    // uniform: a short last chunk
-        const int pos = P * CB + u;                      // position in the chunk's scale words
-        const u32x4 &s8 = b.s8[pos / 8];
-        const int e = pos % 8;
-        const uint32_t word = (e < 2) ? s8.x : (e < 4) ? s8.y : (e < 6) ? s8.z : s8.w;
-        const float d0 = f16_to_f32(static_cast<uint16_t>((e & 1) ? (word >> 16) : (word & 0xffffu)));
-        float v[2][16];
-        half_reads_at<H>(tab + u * 2048, b.w[u], v[0]);
-#pragma unroll
-        for (int c = 0; c < MC; c++) {
-            if (c + 1 < MC) half_reads_at<H>(tab + ((c + 1) * CB + u) * 2048, b.w[u], v[(c + 1) & 1]);
-            half_math(v[c & 1], d0, acc[c]);
-        }
-        }
-    }
-}
-
-template <int H, int MC, int NT>
-__device__ __forceinline__ void mc_half_row(float *tab, const uint16_t *a, int64_t col_halves, int ncols,
-                                            const RowPtrs &rp, int64_t nb, float (&acc)[MC][4]) {
-    constexpr int CB = McShape<MC>::CB;
-    const char *tabc = reinterpret_cast<const char *>(tab);
-    const int64_t nch = (nb + CB - 1) / CB;
-    McChunk<MC> ba, bb;
-    mc_load<MC>(rp, 0, nb, ba);
-    for (int64_t j = 0; j < nch; j += 2) {
-        {   // chunk j (even), weights in ba
-            const int cb = static_cast<int>((nb - j * CB) < CB ? (nb - j * CB) : CB);
-            TableRawN<NT> raw;
-            mc_table_loads<MC, NT>(raw, a, col_halves, ncols, j * CB, cb);
-            asm volatile("" ::: "memory");   // table loads ahead of the next chunk's weights
-            mc_load<MC>(rp, j + 1, nb, bb);
-            if (j > 0) __syncthreads();
-            table_store<NT>(tab, raw, kChunkBlocks);
-            __syncthreads();
-            mc_compute<H, MC, 0>(tabc, ba, cb, acc);
-        }
-        if (j + 1 < nch) {   // chunk j+1 (odd), weights in bb
-            const int cb = static_cast<int>((nb - (j + 1) * CB) < CB ? (nb - (j + 1) * CB) : CB);
-            TableRawN<NT> raw;
-            mc_table_loads<MC, NT>(raw, a, col_halves, ncols, (j + 1) * CB, cb);
-            asm volatile("" ::: "memory");
-            mc_load<MC>(rp, j + 2, nb, ba);
-            __syncthreads();
-            table_store<NT>(tab, raw, kChunkBlocks);
-            __syncthreads();
-            mc_compute<H, MC, (CB < 8 ? 1 : 0)>(tabc, bb, cb, acc);
-        }
-    }
-}
-
-// NT threads: NT/128 tiles of 64 rows, two waves (halves) each.
-template <int MC, int NT>
-__global__ __launch_bounds__(NT) void q1_gemv_mc_kernel(const uint32_t *bits, const uint4 *scales, const uint16_t *a,
-                                                        float *y, int64_t rows, int64_t nb, int64_t nb8,
-                                                        int64_t n_act) {
-    __shared__ float tab[kTableFloats];
-    const int64_t c0 = static_cast<int64_t>(blockIdx.y) * MC;     // first column of this group
-    const int ncols = static_cast<int>((n_act - c0) < MC ? (n_act - c0) : MC);
-    const int64_t col_halves = nb * 4 * 17;
-    const uint16_t *ag = a + c0 * col_halves;
-    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
-    const int tl = wave >> 1, h = wave & 1;
-    const int64_t r = static_cast<int64_t>(blockIdx.x) * (NT / 2) + tl * 64 + lane;
-    const int64_t r64 = (rows + 63) / 64 * 64;
-    const int64_t rl = r < r64 ? r : r64 - 1;
-    const int64_t t = rl / 64, ln = rl % 64;
-    RowPtrs rp{(gptr_u2)bits + ((t * nb) * 2 + h) * 64 + ln, (gptr_u4)scales + t * (nb8 / 8) * 64 + ln};
-    float acc[MC][4];
-#pragma unroll
-    for (int c = 0; c < MC; c++)
-#pragma unroll
-        for (int q = 0; q < 4; q++) acc[c][q] = 0.0f;
-    if (h == 0)
-        mc_half_row<0, MC, NT>(tab, ag, col_halves, ncols, rp, nb, acc);
-    else
-        mc_half_row<1, MC, NT>(tab, ag, col_halves, ncols, rp, nb, acc);
-    // The high half hands lanes 4..7 of every column to the low half through LDS.
-    __syncthreads();
-    float4 *xch = reinterpret_cast<float4 *>(tab) + (tl * 64 + lane) * MC;
-    if (h == 1) {
-#pragma unroll
-        for (int c = 0; c < MC; c++) xch[c] = make_float4(acc[c][0], acc[c][1], acc[c][2], acc[c][3]);
-    }
-    __syncthreads();
-    if (h == 0 && r < rows) {
-#pragma unroll
-        for (int c = 0; c < MC; c++) {
-            if (c >= ncols) break;
-            const float4 hi = xch[c];
-            y[(c0 + c) * rows + r] = ((acc[c][0] + hi.x) + (acc[c][2] + hi.z)) + ((acc[c][1] + hi.y) + (acc[c][3] + hi.w));
-        }
-    }
-}
-
 // -------------------------------------------------- one GEMV, few rows
 // A lone GEMV with few row tiles (a decode step's projection) leaves most
 // CUs idle under the 256-row mapping, and each of its threads walks four
@@ -951,40 +762,11 @@ extern "C" int q1_q8_gemv(const void *bits_plane, const void *scale_plane, const
         }
         return check_launch("q1_q8_gemv");
     }
-    if (n_act >= 2) {   // columns in groups that share one read of the weights
-        // The largest group (8, 4, 2 columns) that still gives about three
-        // quarters of the 256 CUs a workgroup; fewer workgroups leave CUs
-        // idle, while more groups only re-read the weights (mostly from L2).
-        // When 2-column groups of 256 rows would occupy at most half of the
-        // CUs, they take 128 rows instead: twice as many table builds per
-        // row, twice as many CUs at work. Measured at 14336 x 4096: 3 and 4
-        // columns 16.7 -> 13.3 us; at 5 to 8 columns (168 to 224 workgroups of
-        // 256 rows) 128-row workgroups were slower (18 - 20 us against 16.7).
-        int mc = 2;
-        for (int cand : {8, 4}) {
-            if (n_act >= cand / 2 + 1 && gx * ((n_act + cand - 1) / cand) >= 192) {
-                mc = cand;
-                break;
-            }
-        }
-        const bool narrow = mc == 2 && gx * ((n_act + 1) / 2) <= 128;
-        const int64_t tiles = narrow ? (rows + kRowsPerWG / 2 - 1) / (kRowsPerWG / 2) : gx;
-        const dim3 grid(static_cast<uint32_t>(tiles), static_cast<uint32_t>((n_act + mc - 1) / mc));
-        if (narrow)
-            hipLaunchKernelGGL((q1_gemv_mc_kernel<2, kThreads / 2>), grid, dim3(kThreads / 2), 0, hs, bp, sp, ap, y,
-                               rows, nb, nb8, n_act);
-        else if (mc == 2)
-            hipLaunchKernelGGL((q1_gemv_mc_kernel<2, kThreads>), grid, dim3(kThreads), 0, hs, bp, sp, ap, y, rows,
-                               nb, nb8, n_act);
-        else if (mc == 4)
-            hipLaunchKernelGGL((q1_gemv_mc_kernel<4, kThreads>), grid, dim3(kThreads), 0, hs, bp, sp, ap, y, rows,
-                               nb, nb8, n_act);
-        else
-            hipLaunchKernelGGL((q1_gemv_mc_kernel<8, kThreads>), grid, dim3(kThreads), 0, hs, bp, sp, ap, y, rows,
-                               nb, nb8, n_act);
-        return check_launch("q1_q8_gemv");
-    }
-
+    // Each column its own 256-row GEMV (blockIdx.y). Groups of columns that
+    // share one read of the weights through LDS tables of several columns
+    // (P1's Q1_MM4) measured slower at every n_act from 2 to 32: they halve
+    // the independent chains per column group, and these launches are bound
+    // by VALU latency, not by the weight stream (the re-reads hit L2 / MALL).
     hipLaunchKernelGGL(q1_gemv_kernel, dim3(static_cast<uint32_t>(gx), static_cast<uint32_t>(n_act)),
                        dim3(kThreads), 0, as_stream(stream), static_cast<const uint32_t *>(bits_plane),
                        static_cast<const uint4 *>(scale_plane), static_cast<const uint16_t *>(a_q8), y, rows, nb,

@@ -115,8 +115,8 @@ int q1_repack(const void *w_aos, int64_t rows, int64_t K,
  *   y      device f32 [n_act][rows] (column c at y + c*rows, as Q1_MM_WGSL's
  *          O[col*rows + row]), 4-byte aligned.
  * n_act = 1 is the batch-1 decode GEMV; n_act > 1 (the small-M product)
- * keeps every column's bits: columns run in groups of 2, 4 or 8 that share
- * one read of the weights, the group size chosen to occupy the CUs.
+ * keeps every column's bits: one launch runs every column as its own GEMV
+ * (each re-reads the weights, mostly from cache).
  * Limits: rows <= 2^31 - 64, n_act <= 65535. Errors: GD_EINVAL, GD_ESHAPE
  * (K % 128), GD_EALIGN, GD_ERANGE, GD_EHIP. */
 int q1_q8_gemv(const void *bits_plane, const void *scale_plane, const void *a_q8,

@@ -74,8 +74,8 @@ def test_gemv_small_config_bit_exact(gd):
 
 def test_page_exact_protocol(gd):
     """The page's exact() protocol: randomCase(256, 2048, seed 1) row by row,
-    then five activations (one partial tile of four) through the multi-column
-    path, each column against its own oracle result."""
+    then five activations through the several-column entry point, each
+    column against its own oracle result."""
     rows, n = 256, 2048
     W, A = wl.random_case(rows, n, 1)
     As = np.concatenate([A] + [wl.random_case(1, n, 100 + k)[1] for k in range(1, 5)])
@@ -98,10 +98,10 @@ def test_ragged_and_chunked_shapes(gd, rows, K, seed):
 @pytest.mark.parametrize("n_act", [2, 3, 4, 5, 7, 8, 9, 16])
 @pytest.mark.parametrize("rows,K", [(65, 128), (300, 1152), (257, 4608), (64, 8192)])
 def test_multi_column_bit_exact(gd, n_act, rows, K):
-    """Several activation columns against one weight (the small-M product):
-    columns share one read of the weights in groups of 2, 4 or 8; K covers
-    one block, short last chunks and several chunk pairs; every column must
-    carry the bits of its own batch-1 GEMV."""
+    """Several activation columns against one weight (the small-M product),
+    each column its own GEMV in one launch; K covers one block, short last
+    chunks and several chunks; every column must carry the bits of its own
+    batch-1 GEMV."""
     W = wl.q1_weights_aos(rows, K, rows + K)
     A = np.concatenate([wl.q8_acts_aos(K, 7000 + 31 * c + K) for c in range(n_act)])
     got = run_gemv(gd, W, A, rows, K, n_act)
@@ -110,18 +110,18 @@ def test_multi_column_bit_exact(gd, n_act, rows, K):
 
 
 @pytest.mark.parametrize("rows,K,n_act", [
-    (14329, 4096, 16),   # 56 row blocks: groups of 4 columns
-    (14329, 4096, 29),   # groups of 8, the last one partial (5 columns)
-    (12289, 1152, 16),   # 49 row blocks, 9 blocks per row: groups of 4, short chunks
-    (12289, 1152, 40),   # groups of 8, short chunks
-    (14336, 4096, 4),    # 128-row workgroups (256-row ones would fill 112 CUs), groups of 2
-    (10000, 1152, 6),    # 128-row workgroups, three groups of 2, short chunks
-    (12545, 1152, 6),    # 150 workgroups of 256 rows: kept
+    (14329, 4096, 16),   # 56 row blocks x 16 columns: two workgroups per CU
+    (14329, 4096, 29),   # more workgroups than fit on the CUs at once
+    (12289, 1152, 16),   # 49 row blocks, 9 blocks per row (a short last group)
+    (12289, 1152, 40),   # 40 grid rows of columns, short chunks
+    (14336, 4096, 4),    # the decode weight, 224 workgroups
+    (10000, 1152, 6),    # a ragged last row block
+    (12545, 1152, 6),    # one row past a 256-row block
 ])
 def test_multi_column_wide_groups(gd, rows, K, n_act):
-    """Shapes whose row count makes the 4- and 8-column kernels the ones
-    chosen, and shapes on either side of the switch to 128-row workgroups; every column
-    bit-exact with its own batch-1 GEMV."""
+    """Many columns over wide weights (the 256-row kernel, one grid row per
+    column, up to several workgroups per CU); every column bit-exact with
+    its own batch-1 GEMV."""
     W = wl.q1_weights_aos(rows, K, 11 + n_act)
     A = np.concatenate([wl.q8_acts_aos(K, 9000 + c) for c in range(n_act)])
     got = run_gemv(gd, W, A, rows, K, n_act)
@@ -155,15 +155,16 @@ def test_single_gemv_paths(gd, rows, K):
 
 
 @pytest.mark.parametrize("rows,K,n_act", [
-    (4096, 4096, 8),     # n_act * rows = 32768: one one-chain-per-thread GEMV per column
-    (4096, 4096, 9),     # just past it: the shared-weight kernel
-    (2049, 1152, 16),    # past it, short chunks
-    (14336, 4096, 2),    # 64-row workgroups, two columns
-    (300, 4224, 3),      # a column chunk of one block
+    (4096, 4096, 4),     # n_act * rows = 16384: the one-chain-per-thread kernel per column
+    (4096, 4096, 5),     # just past it: the 256-row kernel per column
+    (8192, 8192, 2),     # at it with 64-row workgroups and two full chunks
+    (2049, 1152, 8),     # just past it, short chunks
+    (14336, 4096, 2),    # the decode weight, two columns
+    (300, 4224, 3),      # a chunk of one block
 ])
 def test_columns_across_the_dispatch_boundary(gd, rows, K, n_act):
-    """Several columns on either side of the switch between per-column
-    GEMVs and the shared-weight kernel: every column bit-exact with its own
+    """Several columns on either side of the switch between the
+    one-chain-per-thread and the 256-row kernel: every column bit-exact with its own
     batch-1 GEMV, nothing written past the last column."""
     W = wl.q1_weights_aos(rows, K, rows + 3 * n_act)
     A = np.concatenate([wl.q8_acts_aos(K, 500 + 17 * c + rows) for c in range(n_act)])
