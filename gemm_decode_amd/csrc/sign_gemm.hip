@@ -342,19 +342,20 @@ __global__ __launch_bounds__(kThreads) void sign_gemm_kernel(const uint32_t *xs_
     if (L >= tiles) return;                             // uniform: the whole workgroup leaves
     const int64_t tm = L / tiles_n, tn = L % tiles_n;
     const int64_t m16 = (M + 15) / 16;
+    // The tile's row (per K part) and output exponents, fetched now and
+    // parked in LDS for the epilogue (a barrier before it orders them);
+    // rows past the padded rows take the last padded tile's (never stored).
+    static_assert(kTM * kKParts == kThreads && kTN <= kThreads, "one exponent per thread");
+    int my_er, my_ec = 0;
     {
-        // fetched now so that the epilogue does not wait for them; rows past
-        // the padded rows take the last padded tile's (never stored)
-        static_assert(kTM * kKParts == kThreads && kTN <= kThreads, "one exponent per thread");
         const int lr = static_cast<int>(threadIdx.x) / kKParts, lp = static_cast<int>(threadIdx.x) % kKParts;
         int64_t t = tm * 4 + lr / 16;
         t = t < m16 ? t : m16 - 1;
-        ex_r[lr][lp] = rexp[(t * 16 + lr % 16) * kKParts + lp];
+        my_er = rexp[(t * 16 + lr % 16) * kKParts + lp];
         if (threadIdx.x < kTN) {
             const int64_t n = tn * kTN + threadIdx.x;
-            ex_c[threadIdx.x] = cexp[n < N ? n : N - 1];
+            my_ec = cexp[n < N ? n : N - 1];
         }
-        __syncthreads();
     }
     const int kw = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / 64);   // wave-uniform
     const int l = threadIdx.x % 64;
@@ -478,6 +479,9 @@ __global__ __launch_bounds__(kThreads) void sign_gemm_kernel(const uint32_t *xs_
         __builtin_amdgcn_sched_barrier(0);
     }
     if (i < cnt) compute(r0, v0);
+    ex_r[threadIdx.x / kKParts][threadIdx.x % kKParts] = my_er;
+    if (threadIdx.x < kTN) ex_c[threadIdx.x] = my_ec;
+    __syncthreads();
 
     // Each wave first undoes its part's scalings on its own sums, exactly:
     // element (row, output) times 2^-(row's exponent in this part + the
