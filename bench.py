@@ -55,20 +55,21 @@ MIN_BATCH_S = 0.02     # GPU time per timed batch of the other paths
 # valid for the kernel source they were measured on: reported only while its
 # hash matches, null after any change to it.
 _TRAFFIC = {
-    "q1": ("q1.hip", "d26001046218be80", {"step": (167527.9, 2304.0)}),
-    "q1_small": ("q1.hip", "d26001046218be80", {"7646 x 256x1024": (139143.5, 7646.0)}),
+    "q1": ("q1.hip", "c30a53aa2b735911", {"step": (167514.1, 2304.0)}),
+    "q1_small": ("q1.hip", "c30a53aa2b735911", {"7646 x 256x1024": (139137.4, 7646.0)}),
+    "q1mm": ("q1.hip", "c30a53aa2b735911", {"m2": (4299.5, 112.0), "m4": (4333.5, 224.0), "m8": (4401.5, 448.0)}),
     "ternary": ("ternary.hip", "8f60006b03cd5750",
-                {"2560x2560": (101998.1, 1200.0), "6912x2560": (137366.5, 1620.1), "2560x6912": (65806.6, 300.0)}),
-    "blockq8": ("blockq8.hip", "f40db311846149b4", {"m1": (26820.7, 192.6), "m16": (27505.7, 3072.0)}),
-    # per call on the caller's words: prep (split + weight pack) + gemm
-    "sign": ("sign_gemm.hip", "9a7f346a8abf876e",
-             {"prep": (6187.0, 12432.0), "gemm": (20670.0, 8192.0)}),
-    "sign_lut": ("sign_lut.hip", "c9273fa6aeb445b1",
-                 {"4096x4096": (2170.0, 16.0), "14336x4096": (7290.0, 56.0), "lut4": (35127.5, 8192.0)}),
+                {"2560x2560": (102095.7, 1200.0), "6912x2560": (137522.1, 1620.0), "2560x6912": (65810.5, 300.0)}),
+    "blockq8": ("blockq8.hip", "f40db311846149b4", {"m1": (26826.4, 192.7), "m16": (27510.8, 3072.0)}),
+    # per call on the caller's words: prep (split + weight regroup) + gemm
+    "sign": ("sign_gemm.hip", "da3d176e2baf8a9a",
+             {"prep": (6187.0, 12432.0), "gemm": (20670.5, 8192.0)}),
+    "sign_lut": ("sign_lut.hip", "a89ec91d09f85a4e",
+                 {"4096x4096": (2141.5, 16.0), "14336x4096": (7294.6, 56.0), "lut4": (35127.5, 8192.0)}),
     "quant": ("quantize.hip", "22fc8bec22001fef",
               {"q8_0_decode": (266.5, 136.0), "q8_0_batch_256MiB": (131082.9, 69632.0),
                "int8_planes_decode_step": (540.5 + 572.6, 227.8 + 203.4),
-               "int8_planes_batch_256MiB": (131166.1, 66080.5)}),
+               "int8_planes_batch_256MiB": (131165.8, 66081.1)}),
     # per call: split kernel + merge kernel
     "attention": ("attention.hip", "849b98fd33aa133e",
                   {"kv4096": (16453.1 + 605.0, 1040.0 + 16.0),
@@ -78,7 +79,7 @@ _TRAFFIC = {
 # Hardware MFMA busy fraction (rocprofv3 SQ_VALU_MFMA_BUSY_CYCLES over the
 # dispatch's duration x 1024 SIMDs at 2.4 GHz), for the kernel source measured.
 _MFMA_BUSY = {
-    "sign_gemm_kernel": ("sign_gemm.hip", "9a7f346a8abf876e", 0.456),
+    "sign_gemm_kernel": ("sign_gemm.hip", "da3d176e2baf8a9a", 0.481),
     "blockq8_mfma_kernel": ("blockq8.hip", "f40db311846149b4", 0.078),
 }
 
@@ -572,8 +573,9 @@ def bench_q1_small(args, gd, torch):
 def bench_q1_mm(args, gd, torch):
     """Q1_0.q8_0 with several activation columns (P1's multi-column Q1_MM,
     the prompt side of the same method) on the 14336x4096 decode weight: one
-    launch, each column its own GEMV with the bits of its batch-1 result. Weight copies rotate over a ring > 1 GiB (one graph of
-    launches covers the whole ring, so no copy is read again from cache)."""
+    launch, each column its own GEMV with the bits of its batch-1 result.
+    Weight copies rotate over a ring > 1 GiB (one graph of launches covers
+    the whole ring, so no copy is read again from cache)."""
     import oracle
     cfg = wl.Q1_DECODE[1]
     rows, K = cfg.rows, cfg.K
@@ -585,6 +587,7 @@ def bench_q1_mm(args, gd, torch):
     copies = [(b0.clone(), s0.clone()) for _ in range(ring)]
     w_bytes = rows * (K // 128) * 18
     threads = cpu_cores()
+    mt = measured_traffic("q1mm")
     out = {}
     for M in (2, 4, 8):
         A = np.concatenate([wl.q8_acts_aos(K, sd) for sd in cfg.act_seeds[:M]])
@@ -607,6 +610,7 @@ def bench_q1_mm(args, gd, torch):
             "us": _r(per * 1e6, 2), "timing": st,
             "gemv_equivalent_GBps": _r(M * q1_gemv_bytes(rows, K) / per / 1e9, 1),
             "roofline": roofline(launch_bytes / per / 1e9, HBM_PEAK_GBPS, "GB/s", "hbm",
+                                 None if mt is None else mt[f"m{M}"],
                                  kernel="q1_gemv_kernel (one grid row per column)", bytes_per_launch=launch_bytes),
             "parity_mismatches": mism,
             "cpu_baseline": {"value": _r(M * q1_gemv_bytes(rows, K) / t_cpu / 1e9, 4),
