@@ -731,7 +731,7 @@ def bench_sign_gemv(args, gd, torch):
         out[f"{N}x{K}"] = {
             "us": _r(per * 1e6, 2), "value": _r(bytes_ / per / 1e9, 1), "unit": "GB/s", "timing": st,
             "roofline": roofline(bytes_ / per / 1e9, HBM_PEAK_GBPS, "GB/s", "hbm",
-                                 None if lt is None else lt[f"{N}x{K}"], kernel="sign_gemv_kernel",
+                                 None if lt is None else lt[f"{N}x{K}"], kernel="sign_gemv_narrow_kernel<16>" if N <= 8192 else "sign_gemv_kernel",
                                  bytes_per_launch=bytes_),
             "parity_rel_err": float(np.max(np.abs(got - want)) / np.max(np.abs(want))),
         }
