@@ -31,31 +31,75 @@ __device__ __forceinline__ float absmax4(const float4 &v) {
     return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
 }
 
+// ------------------------------------------------------ f32 decisions
+// Codes are decided in f32 first: with inv32 = f32(127/absmax) and v32 = x *
+// inv32 (two roundings), |v32 - v| <= 127 * 2^-23 ~ 1.5e-5 for the f64
+// product v the rule rounds, so Math.round(v32) = Math.round(v) unless v32
+// lies within kTieGuard of a half-integer; only those elements are decided
+// again in f64 exactly as the rule states.
+constexpr float kTieGuard = 6.4e-5f;   // 4x the f32 error bound above
+
+// f32(127 / a) and f32(a / 127) for a finite f32 a > 0, correctly rounded
+// f32 divisions. They equal the f64 quotients rounded to f32 (the rule's
+// order): an f32 midpoint is never within 2^-49 (relative) of either exact
+// quotient, far beyond f64's rounding, so rounding twice cannot differ.
+__device__ __forceinline__ float recip127(float a) { return 127.0f / a; }
+__device__ __forceinline__ float scale_of(float a) { return a / 127.0f; }
+
+// Four codes, byte j of the result the code of element j. A code is
+// floor(v32 + 0.5) for v32 = x * inv32: outside kTieGuard of a half-integer
+// that is Math.round of the f64 product (v32 + 0.5 rounds by at most 2^-17
+// for |v32| < 128, and |v32| <= 127 + 2^-16 keeps it in [-127, 127] without
+// a clamp). A lane with any of its codes near a tie, or whose reciprocal
+// overflowed f32 (f64_only), decides its four codes again in f64 exactly as
+// the rule states.
+__device__ __forceinline__ uint32_t codes4(const float4 &v, float inv32, float absmax, bool f64_only) {
+    const float e[4] = {v.x, v.y, v.z, v.w};
+    int32_t q[4];
+    bool exact = f64_only;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const float t = e[j] * inv32;
+        q[j] = static_cast<int32_t>(floorf(t + 0.5f));
+        exact |= fabsf(__builtin_amdgcn_fractf(t) - 0.5f) < kTieGuard;
+    }
+    if (exact) {   // rare
+        const double inv = 127.0 / static_cast<double>(absmax);
+#pragma unroll
+        for (int j = 0; j < 4; j++) q[j] = round_code(static_cast<double>(e[j]) * inv);
+    }
+    uint32_t packed = 0;
+#pragma unroll
+    for (int j = 0; j < 4; j++) packed |= (static_cast<uint32_t>(q[j]) & 0xffu) << (8 * j);
+    return packed;
+}
+
 // ----------------------------------------------------------------- q8_0
 // Eight lanes per 32-element block (one float4 each); the block's absmax
-// meets over the eight lanes, each lane writes its four codes as two 16-bit
-// stores (a 34-byte block is only 2-byte aligned) and lane 0 writes d.
+// meets over the eight lanes (three DPP steps), each lane writes its four
+// codes (codes4) as two 16-bit stores (a 34-byte block is only 2-byte
+// aligned) and lane 0 writes d.
+__device__ __forceinline__ float max8(float v) {   // max over the 8 lanes of a half-row
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false)));
+    return v;
+}
+
 __global__ __launch_bounds__(kThreads) void q8_0_quantize_kernel(const float4 *__restrict__ x,
                                                                  uint16_t *__restrict__ out, int64_t nblocks) {
     const int64_t gid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
     const int64_t blk = gid >> 3;
     const int part = static_cast<int>(threadIdx.x & 7);
-    if (blk >= nblocks) return;   // all eight lanes of a block leave together
+    if (blk >= nblocks) return;   // all eight lanes of a block leave together (blocks are 8-lane aligned)
     const float4 v = x[blk * 8 + part];
-    float m = absmax4(v);
-    m = fmaxf(m, __shfl_xor(m, 1, 8));
-    m = fmaxf(m, __shfl_xor(m, 2, 8));
-    m = fmaxf(m, __shfl_xor(m, 4, 8));
-    const double amax = static_cast<double>(m);
+    const float m = max8(absmax4(v));
     uint32_t packed = 0;
     uint16_t d = 0;
-    if (amax > 0.0) {
-        const double inv = 127.0 / amax;
-        const float e[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int j = 0; j < 4; j++)
-            packed |= (static_cast<uint32_t>(round_code(static_cast<double>(e[j]) * inv)) & 0xffu) << (8 * j);
-        d = __builtin_bit_cast(uint16_t, static_cast<_Float16>(static_cast<float>(amax / 127.0)));
+    if (m > 0.0f) {
+        const float inv32 = recip127(m);
+        packed = codes4(v, inv32, m, !(inv32 <= 3.40282347e38f));   // f64 only if the reciprocal overflowed
+        d = __builtin_bit_cast(uint16_t, static_cast<_Float16>(scale_of(m)));
     }
     uint16_t *o = out + blk * 17;   // 34 bytes = 17 halves
     o[1 + 2 * part] = static_cast<uint16_t>(packed & 0xffffu);
@@ -67,37 +111,33 @@ __global__ __launch_bounds__(kThreads) void q8_0_quantize_kernel(const float4 *_
 // One workgroup (four waves) per token. Chunk c holds elements 256c..256c+255,
 // lane l its four elements 256c + 4l .. +3 (one 16-byte load); wave w owns
 // chunks wR .. wR+R-1 (K <= 1024 R), all loaded at once. The token's absmax
-// meets through the waves and LDS. Codes are decided in f32 first: with
-// v32 = x * f32(127/absmax), |v32 - v| <= 1.5e-5 for the f64 product v the
-// rule rounds, so Math.round(v32) = Math.round(v) unless v32 lies within
-// kTieGuard of a half-integer, and only those elements are decided again in
-// f64 exactly as the rule states. Planes: lanes 8g .. 8g+7 of a chunk hold the
-// 32 elements of plane word 8c + g; each lane forms plane b's 4 bits of its
-// codes with one v_dot4_u32_u8 on the code bytes masked to bit b, places them
-// at bits 4(l%8).., the 8 lanes OR them together with three DPP steps, and
-// lane 8g + b keeps plane b's word, so one store per chunk writes all 64
-// words (plane b, word 8c + g at lane 8g + b).
-constexpr float kTieGuard = 6.4e-5f;   // 4x the f32 error bound above
-
-__device__ __forceinline__ uint32_t or8(uint32_t v) {   // OR over the 8 lanes of a half-row
-    v |= static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0xB1, 0xF, 0xF, false));   // quad [1,0,3,2]
-    v |= static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x4E, 0xF, 0xF, false));   // quad [2,3,0,1]
-    v |= static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x141, 0xF, 0xF, false));  // half-row mirror
-    return v;
+// meets through the waves and LDS; codes come from codes4. Planes: lanes
+// 8g .. 8g+7 of a chunk hold the 32 elements of plane word 8c + g, lane 8g + k
+// elements 4k .. 4k+3 of it, i.e. bits 4k .. 4k+3 of every plane's word. A
+// lane first transposes its 4 x 8 code bits in place (four delta swaps), so
+// that nibble b holds bit b of its four codes; the eight lanes then
+// transpose their 8 x 8 nibbles (three exchange steps with the lanes k ^ 1,
+// k ^ 2, k ^ 4), after which lane 8g + b holds plane b's word, and one
+// store per chunk writes all 64 words (plane b, word 8c + g at lane 8g + b).
+__device__ __forceinline__ uint32_t bits_to_nibbles(uint32_t x) {   // bit 8j + b -> bit 4b + j
+    uint32_t t;
+    t = (x ^ (x >> 12)) & 0x0000F0F0u;
+    x ^= t ^ (t << 12);
+    t = (x ^ (x >> 6)) & 0x00CC00CCu;
+    x ^= t ^ (t << 6);
+    t = (x ^ (x >> 3)) & 0x0A0A0A0Au;
+    x ^= t ^ (t << 3);
+    t = (x ^ (x >> 1)) & 0x22222222u;
+    x ^= t ^ (t << 1);
+    return x;
 }
 
-// f64_only: the token's reciprocal 127/absmax does not fit in f32 (absmax
-// below about 3.7e-37), so the f32 product could not stand in for the f64
-// one; every code is then decided in f64.
-__device__ __forceinline__ int32_t code_of(float x, float inv32, double inv, bool f64_only) {
-    if (f64_only) return round_code(static_cast<double>(x) * inv);
-    const float v = x * inv32;
-    const float fl = floorf(v);
-    const float fr = v - fl;
-    if (fabsf(fr - 0.5f) < kTieGuard) return round_code(static_cast<double>(x) * inv);   // near a tie: f64
-    float q = fl + (fr >= 0.5f ? 1.0f : 0.0f);
-    q = q > 127.0f ? 127.0f : (q < -127.0f ? -127.0f : q);
-    return static_cast<int32_t>(q);
+// One exchange step of the 8 x 8 nibble transpose: keep the nibbles whose
+// slot bit t equals this lane's bit t, take the partner's others, moved by
+// 2^t slots (a rotate by sh bits, sh per lane).
+__device__ __forceinline__ uint32_t nibble_step(uint32_t x, uint32_t partner, uint32_t sh, uint32_t keep) {
+    const uint32_t rot = __builtin_amdgcn_alignbit(partner, partner, sh);
+    return (x & keep) | (rot & ~keep);
 }
 
 __device__ __forceinline__ float token_absmax(float m, float *red, int wave, int lane) {
@@ -126,29 +166,33 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(const float *__rest
         v[i] = reinterpret_cast<const float4 *>(xr)[e4 < nq ? e4 : nq - 1];   // clamped: issued, not used
         if (e4 < nq) m = fmaxf(m, absmax4(v[i]));
     }
-    const double amax = static_cast<double>(token_absmax(m, red, wave, lane));
-    const double inv = amax > 0.0 ? 127.0 / amax : 0.0;
-    const float inv32 = static_cast<float>(inv);
+    const float amax = token_absmax(m, red, wave, lane);
+    const float inv32 = amax > 0.0f ? recip127(amax) : 0.0f;
     const bool f64_only = !(inv32 <= 3.40282347e38f);   // uniform: the reciprocal overflowed f32
-    if (threadIdx.x == 0) scale[c] = amax > 0.0 ? static_cast<float>(amax / 127.0) : 0.0f;
+    if (threadIdx.x == 0) scale[c] = amax > 0.0f ? scale_of(amax) : 0.0f;
     const int64_t W = K / 32;
     const int k8 = lane % 8, g = lane / 8;
+    // the exchange steps' per-lane rotates and keep masks (kLow: slot bit t = 0)
+    constexpr uint32_t kLow[3] = {0x0F0F0F0Fu, 0x00FF00FFu, 0x0000FFFFu};
+    uint32_t sh[3], keep[3];
+#pragma unroll
+    for (int t = 0; t < 3; t++) {
+        const bool hi = (k8 >> t) & 1;
+        sh[t] = hi ? (4u << t) : 32u - (4u << t);
+        keep[t] = hi ? ~kLow[t] : kLow[t];
+    }
 #pragma unroll
     for (int i = 0; i < R; i++) {
         if ((c0 + i) * 256 < K) {   // uniform per wave
-            const float e[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-            uint32_t u = 0;
-#pragma unroll
-            for (int j = 0; j < 4; j++) u |= (static_cast<uint32_t>(code_of(e[j], inv32, inv, f64_only)) & 0xffu) << (8 * j);
-            uint32_t mine = 0;
-#pragma unroll
-            for (int b = 0; b < 8; b++) {
-                const uint32_t nib = __builtin_amdgcn_udot4(u & (0x01010101u << b), 0x08040201u, 0u, false) >> b;
-                const uint32_t word = or8(nib << (4 * k8));
-                mine = (k8 == b) ? word : mine;
-            }
+            uint32_t w = bits_to_nibbles(codes4(v[i], inv32, amax, f64_only));
+            int p = __builtin_amdgcn_update_dpp(0, static_cast<int>(w), 0xB1, 0xF, 0xF, false);   // lane k ^ 1
+            w = nibble_step(w, static_cast<uint32_t>(p), sh[0], keep[0]);
+            p = __builtin_amdgcn_update_dpp(0, static_cast<int>(w), 0x4E, 0xF, 0xF, false);       // lane k ^ 2
+            w = nibble_step(w, static_cast<uint32_t>(p), sh[1], keep[1]);
+            p = __builtin_amdgcn_ds_swizzle(static_cast<int>(w), 0x101F);   // lane k ^ 4: xor mask 4, 32-lane groups
+            w = nibble_step(w, static_cast<uint32_t>(p), sh[2], keep[2]);
             const int64_t wi = (c0 + i) * 8 + g;   // plane word index of this lane's group
-            if (wi < W) planes[c * 8 * W + k8 * W + wi] = mine;
+            if (wi < W) planes[c * 8 * W + k8 * W + wi] = w;
         }
     }
 }

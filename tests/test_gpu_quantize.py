@@ -95,6 +95,33 @@ def test_q8_0_scale_extremes(gd):
     assert np.array_equal(got, oracle.quantize_q8_0(x))
 
 
+@pytest.mark.parametrize("K", [256, 4096])
+def test_q8_0_codes_at_ties_and_tiny_blocks(gd, K):
+    """Blocks whose scaled values sit exactly on half-integers and one f32
+    ulp either side (the f32 decision must hand them to the f64 rule, ties
+    toward +infinity), and blocks whose absmax is subnormal or near 1e-37
+    (127/absmax beyond f32, every code in f64): bit for bit with the
+    oracle."""
+    rng = np.random.default_rng(K + 7)
+    base = rng.integers(-126, 126, size=(3, K)).astype(np.float64) + 0.5
+    x = base.astype(np.float32)
+    x[1] = np.nextafter(x[1], np.float32(np.inf))     # just above the ties
+    x[2] = np.nextafter(x[2], np.float32(-np.inf))    # just below
+    x[0, ::32], x[1, ::32], x[2, ::32] = 127.0, 127.0, -127.0   # each block's absmax 127: reciprocal 1
+    mags = np.array([1e-40, 3e-39, 1e-37, 3.6e-37, 1e-36, 1.0], dtype=np.float64)
+    tiny = rng.uniform(-1, 1, size=(1, K)) * np.repeat(np.resize(mags, K // 32), 32)[None, :]
+    tiny = tiny.astype(np.float32)
+    for blk in range(K // 32):
+        m = np.float32(mags[blk % len(mags)])
+        tiny[0, 32 * blk] = m                          # the block's absmax
+        tiny[0, 32 * blk + 1] = m / np.float32(2)      # half of it: code 64, not a clamped 127
+    x = np.concatenate([x, tiny])
+    got = run_q8(gd, x)
+    want = oracle.quantize_q8_0(x)
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, f"{bad.size} bytes differ, first at {bad[:8]}"
+
+
 @pytest.mark.parametrize("count,K", [(1, 32), (1, 96), (1, 2560), (1, 6912), (4, 2560), (3, 160), (2, 2048),
                                      (2, 8192), (1, 8224), (2, 14336)])
 def test_token_planes_and_scales(gd, count, K):
