@@ -10,9 +10,11 @@
 // floor(v) + (v - floor(v) >= 0.5) in f64. The scale is absmax/127 (f64
 // quotient rounded to f32). For q8_0 (page "browseml-gpu.js", packQ8: f16 d,
 // then 32 int8 codes) the same rule is applied per block of 32, with d the
-// f16 rounding (nearest even) of that f32 scale. Every decision is made in
-// f64 exactly as written, so codes and scales are bit-exact with any IEEE
-// evaluation of the same steps. Inputs must be finite.
+// f16 rounding (nearest even) of that f32 scale. Codes are decided in f32
+// where that provably gives the f64 rule's result, and in f64 exactly as
+// written everywhere else (near a tie, or when 127/absmax leaves f32's
+// range), so codes and scales are bit-exact with any IEEE evaluation of the
+// rule's steps. Inputs must be finite.
 #include "gd_internal.h"
 
 namespace {

@@ -18,10 +18,12 @@
 //
 // Mapping. Weights come packed by q1_sign_pack: a u32x4 {bits g, bits g+1,
 // scale g, scale g+1} at (g/2)*N + n, so one load of 64 consecutive outputs'
-// words of a group pair is 1 KiB, one output per lane. All lanes of a wave
-// read the same 16-entry table at once (at most 16 distinct dwords, in
-// distinct banks). A nibble's table offset is a byte of the word shifted by
-// 2 in either direction, taken with one SDWA v_and_b32.
+// words of a group pair is 1 KiB. The decode GEMV serves 64 outputs per
+// workgroup (one per lane, the waves splitting K), or 16 (each output's K
+// split over 32 slices) where 64 would leave the CUs short of workgroups.
+// All lanes that read a table read the same 16 entries at once (at most 16
+// distinct dwords, in distinct banks). A nibble's table offset is a byte of
+// the word shifted by 2 in either direction, taken with one SDWA v_and_b32.
 #include "gd_device.h"
 #include "gd_internal.h"
 
