@@ -128,11 +128,15 @@ __global__ __launch_bounds__(kPrepThreads) void sign_wpack_kernel(const uint32_t
 // gets the exponent c_n that puts its largest |scale| in [2^14, 2^15), and
 // each group's scale s becomes v = s * 2^c_n split as h = fp16(v), l =
 // fp16(v - h) (v - h is exact in f32). Group g of output n is the u32x2
-// {bits, h | l << 16} at g*N + n. A workgroup packs 16 outputs: its waves
-// read the outputs' scale and sign rows 64 groups at a time (256-byte
-// reads), and each 64-group chunk turns around in LDS so that the 16
-// outputs' words of one group go out as one 128-byte write.
+// {bits, h | l << 16} at g*N + n. A workgroup packs 16 outputs. With at most
+// kBpHeld * 128 groups per output (K <= 16384) every word it needs is loaded
+// at once: half a wave per output, lane c holding groups 4c..4c+3 of each
+// 128-group chunk, so the output's exponent comes from registers (a 32-lane
+// reduction) with one memory latency in all; each chunk then turns around in
+// LDS so that the 16 outputs' words of one group go out as one 128-byte
+// write. Longer rows read the scales twice, 64 groups at a time.
 constexpr int kBpCols = 16;   // outputs per workgroup
+constexpr int kBpHeld = 4;    // 128-group chunks held in registers
 
 __device__ __forceinline__ uint32_t split_scale(float s, int e) {
     const float v = __builtin_ldexpf(s, e);
@@ -142,11 +146,64 @@ __device__ __forceinline__ uint32_t split_scale(float s, int e) {
            (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, l)) << 16);
 }
 
+__device__ __forceinline__ int scale_exponent(float m) {
+    return m > 0.0f ? 15 - __builtin_amdgcn_frexp_expf(m) : 0;
+}
+
+__device__ __forceinline__ void bpack_held(const uint32_t *bits_g, const float *scales_g, int64_t N, int64_t G,
+                                           u32x2 *__restrict__ wb, int32_t *__restrict__ cexp, int64_t blk,
+                                           u32x2 (*tile)[129]) {
+    static_assert(kBpCols * 32 == kPrepThreads, "half a wave per output");
+    const int tid = threadIdx.x, r = tid / 32, c = tid % 32;
+    const int64_t n0 = blk * kBpCols, n = n0 + r;
+    const bool live = n < N;
+    const int64_t H = (G + 127) / 128;   // chunks, <= kBpHeld
+    uint32_t bw[kBpHeld][4];
+    float sc[kBpHeld][4];
+#pragma unroll
+    for (int h = 0; h < kBpHeld; h++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const int64_t g = 128 * h + 4 * c + j;
+            const bool in = live && h < H && g < G;
+            bw[h][j] = in ? bits_g[n * G + g] : 0u;
+            sc[h][j] = in ? scales_g[n * G + g] : 0.0f;
+        }
+    float m = 0.0f;
+#pragma unroll
+    for (int h = 0; h < kBpHeld; h++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) m = fmaxf(m, fabsf(sc[h][j]));
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 32));
+    const int e = scale_exponent(m);
+    if (c == 0 && live) cexp[n] = e;
+#pragma unroll
+    for (int h = 0; h < kBpHeld; h++) {
+        if (h >= H) break;   // uniform
+        if (h > 0) __syncthreads();   // the previous chunk's reads of the tile are done
+#pragma unroll
+        for (int j = 0; j < 4; j++) tile[r][4 * c + j] = u32x2{bw[h][j], split_scale(sc[h][j], e)};
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < 128 * kBpCols / kPrepThreads; k++) {
+            const int i = tid + kPrepThreads * k;
+            const int gl = i / kBpCols, rr = i % kBpCols;
+            const int64_t g = 128 * h + gl, nn = n0 + rr;
+            if (g < G && nn < N) wb[g * N + nn] = tile[rr][gl];
+        }
+    }
+}
+
 __device__ __forceinline__ void bpack_cols(const uint32_t *bits_g, const float *scales_g, int64_t N, int64_t G,
                                            u32x2 *__restrict__ wb, int32_t *__restrict__ cexp, int64_t blk) {
     constexpr int kWaves = kPrepThreads / 64, kRows = kBpCols / kWaves;   // outputs per wave
-    __shared__ u32x2 tile[kBpCols][65];
+    __shared__ u32x2 tile[kBpCols][129];
     __shared__ int ex[kBpCols];
+    if (G <= 128 * kBpHeld) {   // uniform
+        bpack_held(bits_g, scales_g, N, G, wb, cexp, blk, tile);
+        return;
+    }
     const int tid = threadIdx.x, w = tid / 64, l = tid % 64;
     const int64_t n0 = blk * kBpCols;
     // 1. each output's largest |scale| and exponent
@@ -160,7 +217,7 @@ __device__ __forceinline__ void bpack_cols(const uint32_t *bits_g, const float *
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
         if (l == 0) {
-            const int e = m > 0.0f ? 15 - __builtin_amdgcn_frexp_expf(m) : 0;
+            const int e = scale_exponent(m);
             ex[r] = e;
             if (n < N) cexp[n] = e;
         }

@@ -88,7 +88,7 @@ def run(gd, fn, x, wp, N):
     return y.cpu().numpy().reshape(M, N)
 
 
-@pytest.mark.parametrize("N,K", [(1, 32), (65, 96), (130, 2048), (64, 4096 + 32)])
+@pytest.mark.parametrize("N,K", [(1, 32), (65, 96), (130, 2048), (64, 4096 + 32), (17, 16384), (20, 16384 + 32)])
 def test_pack_layout(gd, N, K):
     _, bits, scales = wl.sign_gemm_inputs(1, N, K, seed=N + K)
     wp = pack(gd, bits, scales)
