@@ -55,21 +55,21 @@ MIN_BATCH_S = 0.02     # GPU time per timed batch of the other paths
 # valid for the kernel source they were measured on: reported only while its
 # hash matches, null after any change to it.
 _TRAFFIC = {
-    "q1": ("q1.hip", "c30a53aa2b735911", {"step": (167514.1, 2304.0)}),
-    "q1_small": ("q1.hip", "c30a53aa2b735911", {"7646 x 256x1024": (139137.4, 7646.0)}),
+    "q1": ("q1.hip", "c30a53aa2b735911", {"step": (167507.2, 2304.0)}),
+    "q1_small": ("q1.hip", "c30a53aa2b735911", {"7646 x 256x1024": (139137.5, 7646.0)}),
     "q1mm": ("q1.hip", "c30a53aa2b735911", {"m2": (4299.5, 112.0), "m4": (4333.5, 224.0), "m8": (4401.5, 448.0)}),
     "ternary": ("ternary.hip", "8f60006b03cd5750",
-                {"2560x2560": (102095.7, 1200.0), "6912x2560": (137522.1, 1620.0), "2560x6912": (65810.5, 300.0)}),
-    "blockq8": ("blockq8.hip", "f40db311846149b4", {"m1": (26826.4, 192.7), "m16": (27510.8, 3072.0)}),
+                {"2560x2560": (102137.0, 1200.0), "6912x2560": (137551.5, 1620.1), "2560x6912": (65796.1, 300.0)}),
+    "blockq8": ("blockq8.hip", "f40db311846149b4", {"m1": (26807.6, 192.5), "m16": (27508.6, 3072.0)}),
     # per call on the caller's words: prep (split + weight regroup) + gemm
-    "sign": ("sign_gemm.hip", "da3d176e2baf8a9a",
-             {"prep": (6187.0, 12432.0), "gemm": (20670.5, 8192.0)}),
-    "sign_lut": ("sign_lut.hip", "a89ec91d09f85a4e",
+    "sign": ("sign_gemm.hip", "65273486dc365ea0",
+             {"prep": (6189.5, 12432.0), "gemm": (20668.0, 8192.0)}),
+    "sign_lut": ("sign_lut.hip", "e92bac0f6aefae3f",
                  {"4096x4096": (2141.5, 16.0), "14336x4096": (7294.6, 56.0), "lut4": (35127.5, 8192.0)}),
-    "quant": ("quantize.hip", "22fc8bec22001fef",
+    "quant": ("quantize.hip", "43e80662c6c5dcbe",
               {"q8_0_decode": (266.5, 136.0), "q8_0_batch_256MiB": (131082.9, 69632.0),
-               "int8_planes_decode_step": (540.5 + 572.6, 227.8 + 203.4),
-               "int8_planes_batch_256MiB": (131165.8, 66081.1)}),
+               "int8_planes_decode_step": (488.5 + 480.8, 227.8 + 203.4),
+               "int8_planes_batch_256MiB": (131110.9, 66072.5)}),
     # per call: split kernel + merge kernel
     "attention": ("attention.hip", "849b98fd33aa133e",
                   {"kv4096": (16453.1 + 605.0, 1040.0 + 16.0),
@@ -79,7 +79,7 @@ _TRAFFIC = {
 # Hardware MFMA busy fraction (rocprofv3 SQ_VALU_MFMA_BUSY_CYCLES over the
 # dispatch's duration x 1024 SIMDs at 2.4 GHz), for the kernel source measured.
 _MFMA_BUSY = {
-    "sign_gemm_kernel": ("sign_gemm.hip", "da3d176e2baf8a9a", 0.481),
+    "sign_gemm_kernel": ("sign_gemm.hip", "65273486dc365ea0", 0.458),
     "blockq8_mfma_kernel": ("blockq8.hip", "f40db311846149b4", 0.078),
 }
 
