@@ -503,7 +503,8 @@ def bench_q1_small(args, gd, torch):
     """Q1_0.q8_0 GEMV rows=256, K=1024, batch 1 (the correctness-sized
     config; 38,976 algorithmic bytes per GEMV). (G): independent problems in
     grouped launches, each reading its own copy of the planes, the copies
-    rotating over a ring > 1 GiB: the streaming figure. (S): one launch per
+    rotating over a ring > 1 GiB: the streaming figure; the problems share
+    one activation vector, counted once per launch. (S): one launch per
     GEMV, back to back from a HIP graph: the latency figure."""
     import oracle
     cfg = wl.Q1_SMALL
@@ -541,7 +542,11 @@ def bench_q1_small(args, gd, torch):
         gd.q1_q8_gemv(bits[t][i * bb:(i + 1) * bb], scl[t][i * sb:(i + 1) * sb], a, ys1, rows, K, 1)
     per_s, st_s = _time_launches(torch, single, 64, 4, args.batches)
     mism += int((ys1.cpu().numpy().view(np.uint32) != want).sum())
-    g_gbps = count * gemv_bytes / per_g / 1e9
+    # the launch's algorithmic bytes: every problem's weights and output, and
+    # the one activation vector all of them share, once
+    act_bytes = (K // 32) * 34
+    launch_bytes = count * (gemv_bytes - act_bytes) + act_bytes
+    g_gbps = launch_bytes / per_g / 1e9
     small_traffic = measured_traffic("q1_small")
     threads = cpu_cores()
     t_used, n_g = 0.0, 0
@@ -561,7 +566,7 @@ def bench_q1_small(args, gd, torch):
         "roofline": roofline(g_gbps, HBM_PEAK_GBPS, "GB/s", "hbm",
                              (None if small_traffic is None or count != 7646
                               else small_traffic["7646 x 256x1024"]),
-                             kernel="q1_gemv_grouped_small_kernel", bytes_per_launch=count * gemv_bytes),
+                             kernel="q1_gemv_grouped_small_kernel", bytes_per_launch=launch_bytes),
         "parity_mismatches": mism,
         "cpu_baseline": {"value": _r(n_g * gemv_bytes / t_used / 1e9, 4), "unit": "GB/s", "cores": threads,
                          "kind": "oracle", "sample": f"{n_g} GEMVs of 256x1024, {t_used:.2f} s"},
