@@ -33,6 +33,25 @@ constexpr int kRowsPerWG = kRowsPerPass * kPasses;
 // ------------------------------------------------------------ bit planes
 // One thread per (vector, 32-element word): plane b word m = bit b of the
 // bytes x[32m .. 32m+31], element 32m+j at bit j.
+// bit 8j + b of x -> bit 4b + j: nibble b of the result holds bit b of the
+// word's four bytes, in byte order (four delta swaps of the 5-bit bit index).
+__device__ __forceinline__ uint32_t bytes_to_nibbles(uint32_t x) {
+    uint32_t t;
+    t = (x ^ (x >> 12)) & 0x0000F0F0u;
+    x ^= t ^ (t << 12);
+    t = (x ^ (x >> 6)) & 0x00CC00CCu;
+    x ^= t ^ (t << 6);
+    t = (x ^ (x >> 3)) & 0x0A0A0A0Au;
+    x ^= t ^ (t << 3);
+    t = (x ^ (x >> 1)) & 0x22222222u;
+    x ^= t ^ (t << 1);
+    return x;
+}
+
+// One plane word per thread: its 32 codes are 8 words of 4 bytes; each word
+// turns into 8 nibbles (bit b of its four codes in nibble b), then an 8 x 8
+// transpose of those nibbles across the 8 registers (three swap stages)
+// leaves plane b's word, bit j = bit b of code j, in register b.
 __global__ void act_bitplanes_kernel(const int8_t *__restrict__ x, uint32_t *__restrict__ planes, int64_t count,
                                      int64_t W) {
     const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -40,21 +59,23 @@ __global__ void act_bitplanes_kernel(const int8_t *__restrict__ x, uint32_t *__r
     const int64_t v = gid / W, m = gid % W;
     const uint4 *src = reinterpret_cast<const uint4 *>(x + (v * W + m) * 32);
     const uint4 lo = src[0], hi = src[1];
-    const uint32_t bytes[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-    uint32_t out[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    uint32_t r[8] = {bytes_to_nibbles(lo.x), bytes_to_nibbles(lo.y), bytes_to_nibbles(lo.z), bytes_to_nibbles(lo.w),
+                     bytes_to_nibbles(hi.x), bytes_to_nibbles(hi.y), bytes_to_nibbles(hi.z), bytes_to_nibbles(hi.w)};
+    constexpr uint32_t kMask[3] = {0x0F0F0F0Fu, 0x00FF00FFu, 0x0000FFFFu};
 #pragma unroll
-    for (int q = 0; q < 8; q++) {
+    for (int st = 0; st < 3; st++) {
+        const int d = 1 << st, sh = 4 << st;
 #pragma unroll
-        for (int by = 0; by < 4; by++) {
-            const uint32_t val = (bytes[q] >> (8 * by)) & 0xffu;
-            const int j = 4 * q + by;
-#pragma unroll
-            for (int b = 0; b < 8; b++) out[b] |= ((val >> b) & 1u) << j;
+        for (int q = 0; q < 8; q++) {
+            if (q & d) continue;
+            const uint32_t t = ((r[q] >> sh) ^ r[q + d]) & kMask[st];
+            r[q + d] ^= t;
+            r[q] ^= t << sh;
         }
     }
     uint32_t *dst = planes + v * 8 * W + m;
 #pragma unroll
-    for (int b = 0; b < 8; b++) dst[b * W] = out[b];
+    for (int b = 0; b < 8; b++) dst[b * W] = r[b];
 }
 
 // --------------------------------------------------------------- GEMV
