@@ -55,12 +55,12 @@ MIN_BATCH_S = 0.02     # GPU time per timed batch of the other paths
 # valid for the kernel source they were measured on: reported only while its
 # hash matches, null after any change to it.
 _TRAFFIC = {
-    "q1": ("q1.hip", "c30a53aa2b735911", {"step": (167507.2, 2304.0)}),
-    "q1_small": ("q1.hip", "c30a53aa2b735911", {"7646 x 256x1024": (139137.5, 7646.0)}),
+    "q1": ("q1.hip", "c30a53aa2b735911", {"step": (167505.3, 2304.0)}),
+    "q1_small": ("q1.hip", "c30a53aa2b735911", {"7646 x 256x1024": (139137.7, 7646.0)}),
     "q1mm": ("q1.hip", "c30a53aa2b735911", {"m2": (4299.5, 112.0), "m4": (4333.5, 224.0), "m8": (4401.5, 448.0)}),
-    "ternary": ("ternary.hip", "8f60006b03cd5750",
-                {"2560x2560": (102137.0, 1200.0), "6912x2560": (137551.5, 1620.1), "2560x6912": (65796.1, 300.0)}),
-    "blockq8": ("blockq8.hip", "f40db311846149b4", {"m1": (26807.6, 192.5), "m16": (27508.6, 3072.0)}),
+    "ternary": ("ternary.hip", "126a8cf5dd046c1e",
+                {"2560x2560": (102264.8, 1200.0), "6912x2560": (137670.6, 1620.0), "2560x6912": (65860.6, 300.0)}),
+    "blockq8": ("blockq8.hip", "f40db311846149b4", {"m1": (26823.8, 192.5), "m16": (27509.1, 3072.0)}),
     # per call on the caller's words: prep (split + weight regroup) + gemm
     "sign": ("sign_gemm.hip", "65273486dc365ea0",
              {"prep": (6189.5, 12432.0), "gemm": (20668.0, 8192.0)}),
@@ -69,7 +69,7 @@ _TRAFFIC = {
     "quant": ("quantize.hip", "43e80662c6c5dcbe",
               {"q8_0_decode": (266.5, 136.0), "q8_0_batch_256MiB": (131082.9, 69632.0),
                "int8_planes_decode_step": (488.5 + 480.8, 227.8 + 203.4),
-               "int8_planes_batch_256MiB": (131110.9, 66072.5)}),
+               "int8_planes_batch_256MiB": (131110.9, 66071.3)}),
     # per call: split kernel + merge kernel
     "attention": ("attention.hip", "849b98fd33aa133e",
                   {"kv4096": (16453.1 + 605.0, 1040.0 + 16.0),
@@ -80,7 +80,7 @@ _TRAFFIC = {
 # dispatch's duration x 1024 SIMDs at 2.4 GHz), for the kernel source measured.
 _MFMA_BUSY = {
     "sign_gemm_kernel": ("sign_gemm.hip", "65273486dc365ea0", 0.458),
-    "blockq8_mfma_kernel": ("blockq8.hip", "f40db311846149b4", 0.078),
+    "blockq8_mfma_kernel": ("blockq8.hip", "f40db311846149b4", 0.079),
 }
 
 
