@@ -37,11 +37,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kPairBytes = 1024;   // tables of one group pair: 16 nibble groups x 16 floats
 
-// Builds the 16 entries of nibble group q (activation elements e..e+3 of
-// row xr, zero past K) at tab + q*16.
-__device__ __forceinline__ void build_group(float *tab, int q, const float *xr, int64_t e, int64_t K) {
-    f32x4 x = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (e < K) x = *reinterpret_cast<const f32x4 *>(xr + e);   // K % 32 == 0: all four in range
+// Builds the 16 entries of a nibble group from its four activation elements
+// x at tab + q*16.
+__device__ __forceinline__ void build_group_x(float *tab, int q, const f32x4 &x) {
     float v[16];
     v[0] = -(((x[0] + x[1]) + x[2]) + x[3]);
     const float d[4] = {2.0f * x[0], 2.0f * x[1], 2.0f * x[2], 2.0f * x[3]};   // exact
@@ -100,6 +98,22 @@ constexpr int kGvThreads = 512;
 constexpr int kGvWaves = kGvThreads / 64;
 constexpr int kGvChunkPairs = 64;
 constexpr int kGvPairsPerWave = kGvChunkPairs / kGvWaves;   // 8
+constexpr int kGvGroupIters = kGvChunkPairs * 16 / kGvThreads;   // nibble groups each thread builds per chunk
+
+// The activation elements of this thread's nibble groups q = tid + kGvThreads*i
+// of the chunk at pair c0 (zero past the chunk's cp pairs or past K). They are
+// loaded before the chunk's weights: loads complete in order, so the table
+// build then waits for these alone while the weights are still arriving.
+__device__ __forceinline__ void chunk_x(const float *xr, int64_t c0, int64_t cp, int64_t K,
+                                        f32x4 (&xq)[kGvGroupIters]) {
+#pragma unroll
+    for (int i = 0; i < kGvGroupIters; i++) {
+        const int q = threadIdx.x + kGvThreads * i;
+        const int64_t e = c0 * 64 + 4 * q;
+        xq[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        if (q < cp * 16 && e < K) xq[i] = *reinterpret_cast<const f32x4 *>(xr + e);
+    }
+}
 
 __global__ __launch_bounds__(kGvThreads) void sign_gemv_kernel(const float *__restrict__ x,
                                                                const u32x4 *__restrict__ wv_g,
@@ -120,6 +134,9 @@ __global__ __launch_bounds__(kGvThreads) void sign_gemv_kernel(const float *__re
         const int p0 = wave * kGvPairsPerWave;
         int cnt = static_cast<int>(cp) - p0;
         cnt = cnt < 0 ? 0 : (cnt > kGvPairsPerWave ? kGvPairsPerWave : cnt);   // uniform per wave
+        f32x4 xq[kGvGroupIters];
+        chunk_x(xr, c0, cp, K, xq);
+        asm volatile("" ::: "memory");   // the activation loads go first
         u32x4 v[kGvPairsPerWave];
 #pragma unroll
         for (int p = 0; p < kGvPairsPerWave; p++) {
@@ -128,7 +145,11 @@ __global__ __launch_bounds__(kGvThreads) void sign_gemv_kernel(const float *__re
             v[p] = gd::ld_stream(&wv[pg * N + nl]);   // read once (the LUT4 kernel's re-reads stay plain)
         }
         if (c0 > 0) __syncthreads();   // the previous chunk's reads are done
-        for (int q = threadIdx.x; q < cp * 16; q += kGvThreads) build_group(tab, q, xr, c0 * 64 + 4 * q, K);
+#pragma unroll
+        for (int i = 0; i < kGvGroupIters; i++) {
+            const int q = threadIdx.x + kGvThreads * i;
+            if (q < cp * 16) build_group_x(tab, q, xq[i]);
+        }
         __syncthreads();
         if (cnt == kGvPairsPerWave) {
 #pragma unroll
@@ -189,6 +210,9 @@ __global__ __launch_bounds__(kGvThreads) void sign_gemv_narrow_kernel(const floa
         const int64_t cp = (G2 - c0) < kGvChunkPairs ? (G2 - c0) : kGvChunkPairs;   // pairs in this chunk
         // this slice's pairs: sl, sl + kSlices, ... (consecutive slices on
         // consecutive pairs, whose padded tables fall in different banks)
+        f32x4 xq[kGvGroupIters];
+        chunk_x(xr, c0, cp, K, xq);
+        asm volatile("" ::: "memory");   // the activation loads go first
         u32x4 v[kPairsPerSlice];
 #pragma unroll
         for (int p = 0; p < kPairsPerSlice; p++) {
@@ -197,8 +221,11 @@ __global__ __launch_bounds__(kGvThreads) void sign_gemv_narrow_kernel(const floa
             v[p] = gd::ld_stream(&wv[pg * N + nl]);   // read once (the LUT4 kernel's re-reads stay plain)
         }
         if (c0 > 0) __syncthreads();   // the previous chunk's reads are done
-        for (int q = threadIdx.x; q < cp * 16; q += kGvThreads)   // nibble group q % 16 of pair q / 16
-            build_group(reinterpret_cast<float *>(tab + (q / 16) * kGvPairStride), q % 16, xr, c0 * 64 + 4 * q, K);
+#pragma unroll
+        for (int i = 0; i < kGvGroupIters; i++) {   // nibble group q % 16 of pair q / 16
+            const int q = threadIdx.x + kGvThreads * i;
+            if (q < cp * 16) build_group_x(reinterpret_cast<float *>(tab + (q / 16) * kGvPairStride), q % 16, xq[i]);
+        }
         __syncthreads();
 #pragma unroll
         for (int p = 0; p < kPairsPerSlice; p++) {
@@ -229,6 +256,7 @@ constexpr int kL4Threads = 512;
 constexpr int kL4Tokens = 16;
 constexpr int kL4ChunkPairs = 8;
 constexpr int kL4TokenBytes = kL4ChunkPairs * kPairBytes;   // 8 KiB
+constexpr int kL4GroupIters = kL4Tokens * kL4ChunkPairs * 16 / kL4Threads;   // table groups per thread and chunk
 
 __global__ __launch_bounds__(kL4Threads) void sign_lut4_kernel(const float *__restrict__ x,
                                                                const u32x4 *__restrict__ wv_g,
@@ -246,6 +274,20 @@ __global__ __launch_bounds__(kL4Threads) void sign_lut4_kernel(const float *__re
     for (int t = 0; t < kL4Tokens; t++) acc[t] = 0.0f;
     for (int64_t c0 = 0; c0 < G2; c0 += kL4ChunkPairs) {
         const int cp = static_cast<int>((G2 - c0) < kL4ChunkPairs ? (G2 - c0) : kL4ChunkPairs);   // uniform
+        // the activation elements of this thread's table groups first (loads
+        // complete in order: the build then waits for these alone); tokens
+        // past M get zero tables (never stored)
+        f32x4 xg[kL4GroupIters];
+#pragma unroll
+        for (int j = 0; j < kL4GroupIters; j++) {
+            const int i = threadIdx.x + kL4Threads * j;
+            const int t = i / (cp * 16), q = i % (cp * 16);
+            const int64_t m = m0 + t;
+            const int64_t e = c0 * 64 + 4 * q;
+            xg[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            if (i < kL4Tokens * cp * 16 && m < M && e < K) xg[j] = *reinterpret_cast<const f32x4 *>(x + m * K + e);
+        }
+        asm volatile("" ::: "memory");
         u32x4 v[kL4ChunkPairs];
 #pragma unroll
         for (int p = 0; p < kL4ChunkPairs; p++) {
@@ -254,11 +296,10 @@ __global__ __launch_bounds__(kL4Threads) void sign_lut4_kernel(const float *__re
             v[p] = wv[pg * N + nl];
         }
         if (c0 > 0) __syncthreads();
-        for (int i = threadIdx.x; i < kL4Tokens * cp * 16; i += kL4Threads) {
-            const int t = i / (cp * 16), q = i % (cp * 16);
-            const int64_t m = m0 + t;
-            // tokens past M get zero tables (never stored)
-            build_group(tab + t * (kL4TokenBytes / 4), q, x + (m < M ? m : 0) * K, m < M ? c0 * 64 + 4 * q : K, K);
+#pragma unroll
+        for (int j = 0; j < kL4GroupIters; j++) {
+            const int i = threadIdx.x + kL4Threads * j;
+            if (i < kL4Tokens * cp * 16) build_group_x(tab + (i / (cp * 16)) * (kL4TokenBytes / 4), i % (cp * 16), xg[j]);
         }
         __syncthreads();
 #pragma unroll
@@ -300,10 +341,11 @@ extern "C" int q1_sign_gemv(const float *x, const void *w_packed, float *y, int6
     int st = check_args("q1_sign_gemv", x, w_packed, y, M, N, K);
     if (st) return st;
     GD_REQUIRE(M <= 65535, GD_ERANGE, "q1_sign_gemv: M (%lld) above 65535", (long long)M);
-    // Up to N = 8192 the narrow form (16 outputs per workgroup: 5.6 -> 4.5
-    // us at 4096 x 4096); above it 64 outputs per workgroup already give
-    // 224+ workgroups and build fewer tables (16 or 32 outputs per workgroup
-    // measured 9.6 and 7.1 against 6.8 us at 14336 x 4096).
+    // Up to N = 8192 the narrow form (16 outputs per workgroup, four times
+    // the workgroups: about 20 % faster at 4096 x 4096); above it 64 outputs
+    // per workgroup already give 224+ workgroups and build fewer tables (16
+    // or 32 outputs per workgroup measured 41 % and 4 % slower at
+    // 14336 x 4096, and 56 outputs, 256 workgroups, 1 % faster).
     const u32x4 *wp = static_cast<const u32x4 *>(w_packed);
     if (N <= kGvNarrowMaxN)
         hipLaunchKernelGGL(sign_gemv_narrow_kernel<kGvNarrowOutputs>,
