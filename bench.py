@@ -446,7 +446,7 @@ def bench_q1(args, gd, torch):
         "roofline": roofline(gbps, HBM_PEAK_GBPS, "GB/s", "hbm",
                              None if q1_traffic is None else q1_traffic["step"],
                              traffic_source=TRAFFIC_SOURCE if q1_traffic else None,
-                             kernel="q1_gemv_grouped_kernel", us_per_launch=_r(med * 1e6, 2),
+                             kernel="q1_gemv_grouped2_kernel<4, 2>", us_per_launch=_r(med * 1e6, 2),
                              bytes_per_launch=step_bytes,
                              timing=f"HIP events on the launch stream around each batch of {args.steps} "
                                     f"back-to-back launches (one per step); median of {args.batches} batches"),

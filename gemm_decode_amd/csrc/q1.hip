@@ -43,6 +43,11 @@ constexpr int64_t kLatWideRows = 8192;
 constexpr int64_t kLatMaxColumnRows = 16384;
 // Threads per workgroup of the grouped launch (two per row of a 64-row tile).
 constexpr int kGroupedThreads = 512;
+// 256-row units per workgroup of the grouped launch when K is 16, 24 or 32
+// whole blocks (one table chunk): the units share the table build. On the
+// decode step two measured 5 % faster than one; three were slower than two,
+// and four (132 VGPRs, three waves per SIMD) much slower.
+constexpr int kUnitsPerWG = 2;
 
 // Pointers into device global memory (address space 1), so weight loads are
 // global_load (counted by vmcnt only), not flat loads that also hold lgkmcnt.
@@ -425,6 +430,103 @@ __global__ __launch_bounds__(NT) void q1_gemv_grouped_kernel(const gd_q1_problem
     q1_gemv_body<NT>(p, tab, prow, nb, nb8);
 }
 
+// Grouped problems with K = 8*NG blocks (NG = 2..4 full groups, one table
+// chunk): a workgroup runs UN consecutive 256-row units of one problem. They
+// all use the activation's one table, built once; each unit's first two
+// groups are loaded while the previous unit's last two are computed (the
+// refills of the flat group sequence simply run on into the next unit); and
+// the workgroup's start (the problem's descriptor, the first loads, the
+// table build) is paid once per UN units. Each unit's outputs meet through
+// LDS slots of their own, so the table stays intact. Same reads and
+// arithmetic as above, so the same bits.
+template <int H>
+__device__ __forceinline__ void unit_tree(float4 *slot, const float (&acc)[4], float *y, int64_t r, int64_t prow,
+                                          bool first) {
+    // The sums are needed only after the barrier on the low half, which would
+    // let the compiler sink the whole unit's arithmetic past it and hold every
+    // table read until then: pin them here.
+    asm volatile("" ::"v"(acc[0]), "v"(acc[1]), "v"(acc[2]), "v"(acc[3]));
+    if (!first) __syncthreads();   // the previous unit's values have been read
+    if (H == 1) *slot = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    __syncthreads();
+    if (H == 0 && r < prow) {
+        const float4 hi = *slot;
+        y[r] = ((acc[0] + hi.x) + (acc[2] + hi.z)) + ((acc[1] + hi.y) + (acc[3] + hi.w));
+    }
+}
+
+// Group F of the flat sequence (unit F / NG, group F % NG), refilling its
+// register set with group F + 2 of the sequence.
+template <int H, int NG, int UN, int F>
+__device__ __forceinline__ void unit_seq(const char *tabc, u32x2 (&w0)[8], u32x2 (&w1)[8], u32x4 &s0, u32x4 &s1,
+                                         float (&acc)[4], const RowPtrs (&rp)[UN], float4 *slot, float *y,
+                                         const int64_t (&r)[UN], int64_t prow, int live) {
+    if constexpr (F < UN * NG) {
+        constexpr int FT = F + 2;
+        constexpr bool REF = FT < UN * NG;
+        constexpr int TU = REF ? FT / NG : 0, TG = REF ? FT % NG : 0;
+        if constexpr (F % 2 == 0)
+            group8<H, 8 * (F % NG), REF>(tabc, w0, s0, acc, rp[TU], TG);
+        else
+            group8<H, 8 * (F % NG), REF>(tabc, w1, s1, acc, rp[TU], TG);
+        if constexpr (F % NG == NG - 1) {
+            constexpr int U = F / NG;
+            unit_tree<H>(slot, acc, y, r[U], prow, U == 0);
+            if constexpr (U + 1 < UN) {
+                if (live <= U + 1) return;   // uniform: no further unit in this problem
+#pragma unroll
+                for (int i = 0; i < 4; i++) acc[i] = 0.0f;
+            }
+        }
+        unit_seq<H, NG, UN, F + 1>(tabc, w0, w1, s0, s1, acc, rp, slot, y, r, prow, live);
+    }
+}
+
+template <int NG, int UN>
+__global__ __launch_bounds__(kGroupedThreads) void q1_gemv_grouped2_kernel(const gd_q1_problem *probs, int64_t rows) {
+    constexpr int NT = kGroupedThreads;
+    constexpr int64_t nb = 8 * NG, nb8 = nb;
+    __shared__ float tab[kTableFloats];
+    __shared__ float4 xch[NT / 128][64];
+    const gd_q1_problem pr = probs[blockIdx.y];
+    const int64_t prow = (pr.rows >= 1 && pr.rows <= rows) ? pr.rows : rows;
+    const int64_t u0 = static_cast<int64_t>(blockIdx.x) * UN;    // first unit of 256 rows
+    if (u0 * (NT / 2) >= prow) return;                           // uniform: before any barrier
+    const int64_t units_left = (prow + NT / 2 - 1) / (NT / 2) - u0;
+    const int live = static_cast<int>(units_left < UN ? units_left : UN);
+    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+    const int tl = wave >> 1, h = wave & 1;
+    const int64_t r64 = (prow + 63) / 64 * 64;
+    int64_t r[UN];
+    RowPtrs rp[UN];
+#pragma unroll
+    for (int u = 0; u < UN; u++) {
+        r[u] = (u0 + u) * (NT / 2) + tl * 64 + lane;
+        // rows past the padded rows (and missing units) read the last
+        // padded row: never stored
+        const int64_t rl = r[u] < r64 ? r[u] : r64 - 1;
+        const int64_t t = rl / 64, ln = rl % 64;
+        rp[u] = RowPtrs{(gptr_u2)pr.bits_plane + ((t * nb) * 2 + h) * 64 + ln,
+                        (gptr_u4)pr.scale_plane + t * (nb8 / 8) * 64 + ln};
+    }
+    TableRaw raw;
+    table_loads<NT>(raw, static_cast<const uint16_t *>(pr.a_q8), 0, static_cast<int>(nb));
+    asm volatile("" ::: "memory");   // the table's loads go first
+    u32x2 w0[8], w1[8];
+    u32x4 s0, s1;
+    load_group(rp[0], 0, w0, s0, true);
+    load_group(rp[1 / NG], 1 % NG, w1, s1, true);
+    table_store<NT>(tab, raw, static_cast<int>(nb));
+    __syncthreads();
+    const char *tabc = reinterpret_cast<const char *>(tab);
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float4 *slot = &xch[tl][lane];
+    if (h == 0)
+        unit_seq<0, NG, UN, 0>(tabc, w0, w1, s0, s1, acc, rp, slot, pr.y, r, prow, live);
+    else
+        unit_seq<1, NG, UN, 0>(tabc, w0, w1, s0, s1, acc, rp, slot, pr.y, r, prow, live);
+}
+
 // Grouped problems with K <= 1024: one group of at most eight blocks per
 // row, so one table build per workgroup and no chunk loop. Each workgroup
 // (NT threads: NT/2 rows, two waves per 64-row tile as above) stages its
@@ -793,6 +895,18 @@ extern "C" int q1_q8_gemv_grouped(const gd_q1_problem *problems, int64_t count, 
         return check_launch("q1_q8_gemv_grouped");
     }
     constexpr int NT = kGroupedThreads;
+    if (nb == 16 || nb == 24 || nb == 32) {   // full groups, one table chunk: two units per workgroup
+        constexpr int UN = kUnitsPerWG;
+        const dim3 grid(static_cast<uint32_t>((rows + UN * (NT / 2) - 1) / (UN * (NT / 2))),
+                        static_cast<uint32_t>(count));
+        if (nb == 16)
+            hipLaunchKernelGGL((q1_gemv_grouped2_kernel<2, UN>), grid, dim3(NT), 0, as_stream(stream), problems, rows);
+        else if (nb == 24)
+            hipLaunchKernelGGL((q1_gemv_grouped2_kernel<3, UN>), grid, dim3(NT), 0, as_stream(stream), problems, rows);
+        else
+            hipLaunchKernelGGL((q1_gemv_grouped2_kernel<4, UN>), grid, dim3(NT), 0, as_stream(stream), problems, rows);
+        return check_launch("q1_q8_gemv_grouped");
+    }
     const int64_t gx = (rows + NT / 2 - 1) / (NT / 2);
     hipLaunchKernelGGL(q1_gemv_grouped_kernel<NT>, dim3(static_cast<uint32_t>(gx), static_cast<uint32_t>(count)),
                        dim3(NT), 0, as_stream(stream), problems, rows, nb, nb8);

@@ -297,6 +297,37 @@ def test_grouped_mixed_rows(gd, K):
         assert np.all(np.isnan(got[rows:])), f"rows {rows}: wrote past its rows"
 
 
+@pytest.mark.parametrize("K", [2048, 3072, 4096])
+def test_grouped_two_units_per_workgroup(gd, K):
+    """K of 16, 24 or 32 blocks (whole groups of eight, one table chunk)
+    runs two 256-row units of a problem per workgroup, the second unit's
+    first groups loaded during the first unit's last ones. Row counts of one
+    unit, of a second unit that is partial or a single row, of an odd number
+    of units (the last workgroup with one unit) and of many units, plus
+    rows = 0 (the launch's rows): every output bit-exact with the oracle for
+    its own rows, nothing written past them."""
+    rows_max = 1800
+    shapes = [(256, 256), (257, 257), (300, 300), (512, 512), (700, 700), (1, 1), (1800, 0), (1537, 1537),
+              (64, 64), (511, 511)]   # (rows, rows field)
+    entries, keep, wants = [], [], []
+    for i, (rows, field) in enumerate(shapes):
+        W = wl.q1_weights_aos(rows, K, 90 + i + K)
+        A = wl.q8_acts_aos(K, 9000 + i + K)
+        b, s = planes_on_gpu(gd, W, rows, K)
+        a = dev(A.reshape(-1))
+        y = torch.full((rows + 64,), float("nan"), device="cuda")      # 64 guard elements
+        entries.append((b, s, a, y, field))
+        keep.append((b, s, a, y, rows))
+        wants.append(oracle.q1_q8_gemv_aos(W, A, rows, K, nthreads=oracle.max_threads()))
+    probs = gd.make_q1_problems(entries)
+    gd.q1_q8_gemv_grouped(probs, len(entries), rows_max, K)
+    torch.cuda.synchronize()
+    for (b, s, a, y, rows), want in zip(keep, wants):
+        got = y.cpu().numpy()
+        assert_bits_equal(got[:rows], want.reshape(-1), f"K {K} rows {rows}")
+        assert np.all(np.isnan(got[rows:])), f"K {K} rows {rows}: wrote past its rows"
+
+
 @pytest.mark.parametrize("count", [72, 300])
 def test_grouped_k4096_mixed_problems(gd, count):
     """A grouped launch at K = 4096 (one 32-block chunk per row) over many
