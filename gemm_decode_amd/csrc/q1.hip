@@ -45,9 +45,10 @@ constexpr int64_t kLatMaxColumnRows = 16384;
 constexpr int kGroupedThreads = 512;
 // 256-row units per workgroup of the grouped launch when K is 16, 24 or 32
 // whole blocks (one table chunk): the units share the table build. On the
-// decode step two measured 5 % faster than one; three were slower than two,
-// and four (132 VGPRs, three waves per SIMD) much slower.
-constexpr int kUnitsPerWG = 2;
+// decode step (weights streamed from HBM) two units per workgroup measured
+// 3 % faster than one and three another 1.5 %; four need 132 VGPRs (three
+// waves per SIMD) and were much slower.
+constexpr int kUnitsPerWG = 3;
 
 // Pointers into device global memory (address space 1), so weight loads are
 // global_load (counted by vmcnt only), not flat loads that also hold lgkmcnt.
@@ -895,7 +896,7 @@ extern "C" int q1_q8_gemv_grouped(const gd_q1_problem *problems, int64_t count, 
         return check_launch("q1_q8_gemv_grouped");
     }
     constexpr int NT = kGroupedThreads;
-    if (nb == 16 || nb == 24 || nb == 32) {   // full groups, one table chunk: two units per workgroup
+    if (nb == 16 || nb == 24 || nb == 32) {   // full groups, one table chunk: kUnitsPerWG units per workgroup
         constexpr int UN = kUnitsPerWG;
         const dim3 grid(static_cast<uint32_t>((rows + UN * (NT / 2) - 1) / (UN * (NT / 2))),
                         static_cast<uint32_t>(count));

@@ -298,17 +298,18 @@ def test_grouped_mixed_rows(gd, K):
 
 
 @pytest.mark.parametrize("K", [2048, 3072, 4096])
-def test_grouped_two_units_per_workgroup(gd, K):
+def test_grouped_units_per_workgroup(gd, K):
     """K of 16, 24 or 32 blocks (whole groups of eight, one table chunk)
-    runs two 256-row units of a problem per workgroup, the second unit's
-    first groups loaded during the first unit's last ones. Row counts of one
-    unit, of a second unit that is partial or a single row, of an odd number
-    of units (the last workgroup with one unit) and of many units, plus
-    rows = 0 (the launch's rows): every output bit-exact with the oracle for
-    its own rows, nothing written past them."""
+    runs several consecutive 256-row units of a problem per workgroup, each
+    unit's first groups loaded during the previous unit's last ones. Row
+    counts of one unit, of a last unit that is partial or a single row, of
+    unit counts that leave the last workgroup with one, two or all of its
+    units, and of many units, plus rows = 0 (the launch's rows): every
+    output bit-exact with the oracle for its own rows, nothing written past
+    them."""
     rows_max = 1800
     shapes = [(256, 256), (257, 257), (300, 300), (512, 512), (700, 700), (1, 1), (1800, 0), (1537, 1537),
-              (64, 64), (511, 511)]   # (rows, rows field)
+              (64, 64), (511, 511), (768, 768), (1025, 1025)]   # (rows, rows field)
     entries, keep, wants = [], [], []
     for i, (rows, field) in enumerate(shapes):
         W = wl.q1_weights_aos(rows, K, 90 + i + K)
