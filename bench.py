@@ -566,7 +566,7 @@ def bench_q1_small(args, gd, torch):
         "roofline": roofline(g_gbps, HBM_PEAK_GBPS, "GB/s", "hbm",
                              (None if small_traffic is None or count != 7646
                               else small_traffic["7646 x 256x1024"]),
-                             kernel="q1_gemv_grouped_small_kernel", bytes_per_launch=launch_bytes),
+                             kernel="q1_gemv_grouped_small2_kernel<2>", bytes_per_launch=launch_bytes),
         "parity_mismatches": mism,
         "cpu_baseline": {"value": _r(n_g * gemv_bytes / t_used / 1e9, 4), "unit": "GB/s", "cores": threads,
                          "kind": "oracle", "sample": f"{n_g} GEMVs of 256x1024, {t_used:.2f} s"},

@@ -538,6 +538,10 @@ __global__ __launch_bounds__(kGroupedThreads) void q1_gemv_grouped2_kernel(const
 // hides the latency that a workgroup's single short pass otherwise exposes.
 constexpr int kSmallBlocks = 8;
 constexpr int kSmallThreads = 256;   // 128 rows per workgroup
+// 128-row units per workgroup at K = 1024: two measured 1.5 % faster than one
+// on 7,646 problems of 256 rows; three and four slower (the second register
+// set and the row pointers cost occupancy: 94 to 116 VGPRs against 65).
+constexpr int kSmallUnitsPerWG = 2;
 
 template <int NT>
 __global__ __launch_bounds__(NT) void q1_gemv_grouped_small_kernel(const gd_q1_problem *probs, int64_t rows,
@@ -606,6 +610,56 @@ __global__ __launch_bounds__(NT) void q1_gemv_grouped_small_kernel(const gd_q1_p
         const float4 hi = *xch;
         pr.y[r] = ((acc[0] + hi.x) + (acc[2] + hi.z)) + ((acc[1] + hi.y) + (acc[3] + hi.w));
     }
+}
+
+// K = 1024 (one group of eight blocks per row) with UN consecutive 128-row
+// units per workgroup: one 16 KiB table for all of them, each unit's blocks
+// loaded two units ahead (two register sets), the start paid once per UN
+// units. Same reads and arithmetic as above, so the same bits.
+template <int UN>
+__global__ __launch_bounds__(kSmallThreads) void q1_gemv_grouped_small2_kernel(const gd_q1_problem *probs,
+                                                                              int64_t rows) {
+    constexpr int NT = kSmallThreads;
+    constexpr int64_t nb = kSmallBlocks;
+    __shared__ __attribute__((aligned(16))) float tab[kSmallBlocks * 512];
+    __shared__ float4 xch[NT / 128][64];
+    const gd_q1_problem pr = probs[blockIdx.y];
+    const int64_t prow = (pr.rows >= 1 && pr.rows <= rows) ? pr.rows : rows;
+    const int64_t u0 = static_cast<int64_t>(blockIdx.x) * UN;    // first unit of 128 rows
+    if (u0 * (NT / 2) >= prow) return;                           // uniform: before any barrier
+    const int64_t units_left = (prow + NT / 2 - 1) / (NT / 2) - u0;
+    const int live = static_cast<int>(units_left < UN ? units_left : UN);
+    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+    const int tl = wave >> 1, h = wave & 1;
+    const int64_t r64 = (prow + 63) / 64 * 64;
+    int64_t r[UN];
+    RowPtrs rp[UN];
+#pragma unroll
+    for (int u = 0; u < UN; u++) {
+        r[u] = (u0 + u) * (NT / 2) + tl * 64 + lane;
+        const int64_t rl = r[u] < r64 ? r[u] : r64 - 1;
+        const int64_t t = rl / 64, ln = rl % 64;
+        rp[u] = RowPtrs{(gptr_u2)pr.bits_plane + ((t * nb) * 2 + h) * 64 + ln, (gptr_u4)pr.scale_plane + t * 64 + ln};
+    }
+    // the activation's table groups first (one per thread)
+    const auto a = (const uint16_t __attribute__((address_space(1))) *)pr.a_q8;
+    const int g = threadIdx.x;   // 256 groups, 256 threads
+    const auto blk = a + ((g >> 5) * 4 + ((g >> 3) & 3)) * 17;
+    const uint32_t rd = blk[0], rq01 = blk[1 + 2 * (g & 7)], rq23 = blk[2 + 2 * (g & 7)];
+    asm volatile("" ::: "memory");
+    u32x2 w0[8], w1[8];
+    u32x4 s0, s1;
+    load_group(rp[0], 0, w0, s0, true);
+    load_group(rp[UN > 1 ? 1 : 0], 0, w1, s1, true);
+    table_group(tab + threadIdx.x * 16, rd, rq01, rq23);
+    __syncthreads();
+    const char *tabc = reinterpret_cast<const char *>(tab);
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float4 *slot = &xch[tl][lane];
+    if (h == 0)
+        unit_seq<0, 1, UN, 0>(tabc, w0, w1, s0, s1, acc, rp, slot, pr.y, r, prow, live);
+    else
+        unit_seq<1, 1, UN, 0>(tabc, w0, w1, s0, s1, acc, rp, slot, pr.y, r, prow, live);
 }
 
 // -------------------------------------------------- one GEMV, few rows
@@ -887,6 +941,15 @@ extern "C" int q1_q8_gemv_grouped(const gd_q1_problem *problems, int64_t count, 
     GD_REQUIRE(count <= 65535, GD_ERANGE, "q1_q8_gemv_grouped: count (%lld) above 65535", (long long)count);
     GD_REQUIRE(aligned(problems, 8), GD_EALIGN, "q1_q8_gemv_grouped: problems must be 8-byte aligned");
     const int64_t nb = K / 128, nb8 = (nb + 7) / 8 * 8;
+    if (nb == kSmallBlocks) {   // one whole group per row: kSmallUnitsPerWG units per workgroup
+        constexpr int NT = kSmallThreads;
+        constexpr int UN = kSmallUnitsPerWG;
+        const int64_t gx = (rows + UN * (NT / 2) - 1) / (UN * (NT / 2));
+        hipLaunchKernelGGL(q1_gemv_grouped_small2_kernel<UN>,
+                           dim3(static_cast<uint32_t>(gx), static_cast<uint32_t>(count)), dim3(NT), 0,
+                           as_stream(stream), problems, rows);
+        return check_launch("q1_q8_gemv_grouped");
+    }
     if (nb <= kSmallBlocks) {   // one group of blocks per row
         constexpr int NT = kSmallThreads;
         const int64_t gx = (rows + NT / 2 - 1) / (NT / 2);
