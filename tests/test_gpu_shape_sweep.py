@@ -100,7 +100,23 @@ def _q1_group_case(rng, i):
             return R, K, tuple(rows), shared, 7100 + i
 
 
-Q1_GROUP_CASES = draw(12, 10, _q1_group_case)
+def _q1_group_case_at(K):
+    def f(rng, i):
+        while True:
+            R = log_uniform(rng, 300, 6000)
+            count = int(rng.integers(2, 41))
+            rows = [R if rng.random() < 0.3 else int(rng.integers(1, R + 1)) for _ in range(count)]
+            rows[int(rng.integers(0, count))] = R
+            shared = bool(rng.random() < 0.5)
+            if sum(rows) * K <= 8e7:
+                return R, K, tuple(rows), shared, 7150 + i + K
+    return f
+
+
+# random problem sets, plus one at each K whose rows run several 256- or
+# 128-row units per workgroup (whole groups of eight blocks in one table chunk)
+Q1_GROUP_CASES = draw(12, 10, _q1_group_case) + [draw(20 + K // 1024, 1, _q1_group_case_at(K))[0]
+                                                  for K in (1024, 2048, 3072, 4096)]
 
 
 @pytest.mark.parametrize("R,K,rows,shared,seed", Q1_GROUP_CASES,
