@@ -616,7 +616,9 @@ def bench_q1_mm(args, gd, torch):
             "gemv_equivalent_GBps": _r(M * q1_gemv_bytes(rows, K) / per / 1e9, 1),
             "roofline": roofline(launch_bytes / per / 1e9, HBM_PEAK_GBPS, "GB/s", "hbm",
                                  None if mt is None else mt[f"m{M}"],
-                                 kernel="q1_gemv_kernel (one grid row per column)", bytes_per_launch=launch_bytes),
+                                 kernel=("q1_gemv_kernel<256> (128-row workgroups, one grid row per column)"
+                                         if M == 2 else "q1_gemv_kernel<512> (one grid row per column)"),
+                                 bytes_per_launch=launch_bytes),
             "parity_mismatches": mism,
             "cpu_baseline": {"value": _r(M * q1_gemv_bytes(rows, K) / t_cpu / 1e9, 4),
                              "unit": "GB/s (GEMV-equivalent)", "cores": threads, "kind": "oracle",

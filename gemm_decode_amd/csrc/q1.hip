@@ -41,6 +41,9 @@ constexpr int64_t kLatWideRows = 8192;
 // column; above it each column runs the 256-row kernel (both re-read the
 // weights per column, mostly from cache).
 constexpr int64_t kLatMaxColumnRows = 16384;
+// Up to this many 256-row workgroups (half the CUs), the per-column launch
+// takes 128-row workgroups instead.
+constexpr int64_t kNarrowMaxWGs = 128;
 // Threads per workgroup of the grouped launch (two per row of a 64-row tile).
 constexpr int kGroupedThreads = 512;
 // 256-row units per workgroup of the grouped launch when K is 16, 24 or 32
@@ -410,13 +413,15 @@ __device__ __forceinline__ void q1_gemv_body(const Q1Args &p, float *tab, int64_
     }
 }
 
-__global__ __launch_bounds__(kThreads) void q1_gemv_kernel(const uint32_t *bits, const uint4 *scales,
-                                                           const uint16_t *a, float *y, int64_t rows, int64_t nb,
-                                                           int64_t nb8) {
+// NT threads: NT/2 rows per workgroup (256, or 128 when the 256-row grid
+// would leave at least half the CUs without a workgroup).
+template <int NT>
+__global__ __launch_bounds__(NT) void q1_gemv_kernel(const uint32_t *bits, const uint4 *scales, const uint16_t *a,
+                                                     float *y, int64_t rows, int64_t nb, int64_t nb8) {
     __shared__ float tab[kTableFloats];
     const int64_t c = blockIdx.y;   // activation column
     Q1Args p{bits, scales, a + c * (nb * 4) * 17, y + c * rows};
-    q1_gemv_body<kThreads>(p, tab, rows, nb, nb8);
+    q1_gemv_body<NT>(p, tab, rows, nb, nb8);
 }
 
 template <int NT>
@@ -924,10 +929,17 @@ extern "C" int q1_q8_gemv(const void *bits_plane, const void *scale_plane, const
     // (P1's Q1_MM4) measured slower at every n_act from 2 to 32: they halve
     // the independent chains per column group, and these launches are bound
     // by VALU latency, not by the weight stream (the re-reads hit L2 / MALL).
-    hipLaunchKernelGGL(q1_gemv_kernel, dim3(static_cast<uint32_t>(gx), static_cast<uint32_t>(n_act)),
-                       dim3(kThreads), 0, as_stream(stream), static_cast<const uint32_t *>(bits_plane),
-                       static_cast<const uint4 *>(scale_plane), static_cast<const uint16_t *>(a_q8), y, rows, nb,
-                       nb8);
+    // While the 256-row grid would give at most half the CUs a workgroup,
+    // 128-row workgroups put twice as many CUs to work (each builds the
+    // whole table for half the rows).
+    if (gx * n_act <= kNarrowMaxWGs) {
+        const int64_t gx2 = (rows + kRowsPerWG / 2 - 1) / (kRowsPerWG / 2);
+        hipLaunchKernelGGL(q1_gemv_kernel<kThreads / 2>, dim3(static_cast<uint32_t>(gx2), static_cast<uint32_t>(n_act)),
+                           dim3(kThreads / 2), 0, hs, bp, sp, ap, y, rows, nb, nb8);
+        return check_launch("q1_q8_gemv");
+    }
+    hipLaunchKernelGGL(q1_gemv_kernel<kThreads>, dim3(static_cast<uint32_t>(gx), static_cast<uint32_t>(n_act)),
+                       dim3(kThreads), 0, hs, bp, sp, ap, y, rows, nb, nb8);
     return check_launch("q1_q8_gemv");
 }
 

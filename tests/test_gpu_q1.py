@@ -135,12 +135,15 @@ def test_multi_column_wide_groups(gd, rows, K, n_act):
     (8192, 8192),     # 64-row workgroups, two full chunks
     (14336, 4096),    # 64-row workgroups
     (16384, 1152),    # the largest row count on the one-chain-per-thread kernel
-    (16385, 256),     # the first on the 256-row kernel
+    (16385, 256),     # the first on the four-chain kernel (128-row workgroups)
     (20000, 4224),
+    (32768, 256),     # 128 row blocks of 256: the last 128-row grid
+    (32769, 256),     # the first 256-row grid
 ])
 def test_single_gemv_paths(gd, rows, K):
-    """Batch-1 GEMVs across both single-GEMV mappings (one chain per thread
-    for up to 64 row blocks of 256, four per thread above), bit-exact, and
+    """Batch-1 GEMVs across the single-GEMV mappings (one chain per thread
+    for up to 64 row blocks of 256, four per thread above: 128-row
+    workgroups up to 128 row blocks, 256-row ones beyond), bit-exact, and
     nothing written past the last row."""
     W = wl.q1_weights_aos(rows, K, rows % 97 + K)
     A = wl.q8_acts_aos(K, 31 * rows + K)
@@ -159,13 +162,17 @@ def test_single_gemv_paths(gd, rows, K):
     (4096, 4096, 5),     # just past it: the 256-row kernel per column
     (8192, 8192, 2),     # at it with 64-row workgroups and two full chunks
     (2049, 1152, 8),     # just past it, short chunks
-    (14336, 4096, 2),    # the decode weight, two columns
+    (14336, 4096, 2),    # the decode weight, two columns: 128-row workgroups
     (300, 4224, 3),      # a chunk of one block
+    (16384, 256, 2),     # 64 row blocks x 2 columns = 128: the last 128-row grid
+    (16385, 256, 2),     # 65 x 2 = 130: the first 256-row grid
 ])
 def test_columns_across_the_dispatch_boundary(gd, rows, K, n_act):
-    """Several columns on either side of the switch between the
-    one-chain-per-thread and the 256-row kernel: every column bit-exact with its own
-    batch-1 GEMV, nothing written past the last column."""
+    """Several columns on either side of the switches between the
+    one-chain-per-thread kernel, 128-row workgroups (while 256-row ones would
+    fill at most half the CUs) and 256-row workgroups: every column
+    bit-exact with its own batch-1 GEMV, nothing written past the last
+    column."""
     W = wl.q1_weights_aos(rows, K, rows + 3 * n_act)
     A = np.concatenate([wl.q8_acts_aos(K, 500 + 17 * c + rows) for c in range(n_act)])
     b, s = planes_on_gpu(gd, W, rows, K)
