@@ -911,12 +911,21 @@ extern "C" int q1_q8_gemv(const void *bits_plane, const void *scale_plane, const
     const uint16_t *ap = static_cast<const uint16_t *>(a_q8);
     if (gx <= kLatMaxRowBlocks && (n_act == 1 || n_act * rows <= kLatMaxColumnRows)) {
         // One chain per thread, each column its own GEMV (blockIdx.y). A
-        // wave is 16 rows whatever the workgroup, so 32-row workgroups (one
-        // wave per SIMD) until they would stack on the CUs, then 64-row ones,
-        // which build half as many tables.
+        // wave is 16 rows whatever the workgroup, so 16-row workgroups (two
+        // waves) while 32-row ones would fill at most half the CUs, 32-row
+        // workgroups (one wave per SIMD) until they would stack on the CUs,
+        // then 64-row ones, which build half as many tables.
         const uint32_t cols = static_cast<uint32_t>(n_act);
         if (rows >= kLatWideRows) {
             hipLaunchKernelGGL(q1_gemv_lat_kernel<8>, dim3(static_cast<uint32_t>((rows + 63) / 64), cols), dim3(512),
+                               0, hs, bp, sp, ap, y, rows, nb, nb8);
+        } else if ((rows + 31) / 32 * n_act <= kNarrowMaxWGs && nb <= kChunkBlocks) {
+            // 32-row workgroups would leave at least half the CUs idle: 16-row
+            // ones (two waves) use all of them. Each builds the whole table
+            // with half the threads, which pays for one table (K <= 4096) and
+            // not for several rebuilt along K (4096 x 11008: 13.5 -> 14.2 us);
+            // 2560 x 2560 5.92 -> 5.56 us, 4096 x 4096 6.05 -> 5.92 us.
+            hipLaunchKernelGGL(q1_gemv_lat_kernel<2>, dim3(static_cast<uint32_t>((rows + 15) / 16), cols), dim3(128),
                                0, hs, bp, sp, ap, y, rows, nb, nb8);
         } else {
             hipLaunchKernelGGL(q1_gemv_lat_kernel<4>, dim3(static_cast<uint32_t>((rows + 31) / 32), cols), dim3(256),

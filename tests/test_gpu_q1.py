@@ -130,7 +130,9 @@ def test_multi_column_wide_groups(gd, rows, K, n_act):
 
 
 @pytest.mark.parametrize("rows,K", [
-    (4096, 4096),     # one chunk of 32 blocks, 32-row workgroups
+    (4096, 4096),     # one chunk of 32 blocks, 16-row workgroups (128 x 32 rows fill half the CUs)
+    (4097, 1024),     # 129 x 32 rows: 32-row workgroups
+    (2000, 4224),     # two chunks: 32-row workgroups (16-row ones only for one chunk)
     (8191, 4224),     # a full chunk whose next chunk is one block long
     (8192, 8192),     # 64-row workgroups, two full chunks
     (14336, 4096),    # 64-row workgroups
@@ -142,9 +144,9 @@ def test_multi_column_wide_groups(gd, rows, K, n_act):
 ])
 def test_single_gemv_paths(gd, rows, K):
     """Batch-1 GEMVs across the single-GEMV mappings (one chain per thread
-    for up to 64 row blocks of 256, four per thread above: 128-row
-    workgroups up to 128 row blocks, 256-row ones beyond), bit-exact, and
-    nothing written past the last row."""
+    for up to 64 row blocks of 256, in 16-, 32- or 64-row workgroups; four
+    per thread above: 128-row workgroups up to 128 row blocks, 256-row ones
+    beyond), bit-exact, and nothing written past the last row."""
     W = wl.q1_weights_aos(rows, K, rows % 97 + K)
     A = wl.q8_acts_aos(K, 31 * rows + K)
     b, s = planes_on_gpu(gd, W, rows, K)
