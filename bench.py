@@ -55,12 +55,12 @@ MIN_BATCH_S = 0.02     # GPU time per timed batch of the other paths
 # valid for the kernel source they were measured on: reported only while its
 # hash matches, null after any change to it.
 _TRAFFIC = {
-    "q1": ("q1.hip", "4150668f051c481d", {"step": (170182.1, 2304.0)}),
-    "q1_small": ("q1.hip", "4150668f051c481d", {"7646 x 256x1024": (138463.9, 7646.0)}),
-    "q1mm": ("q1.hip", "4150668f051c481d", {"m2": (4307.5, 112.0), "m4": (4329.5, 224.0), "m8": (4397.5, 448.0)}),
+    "q1": ("q1.hip", "6594bcff4a7b6f83", {"step": (170022.2, 2304.0)}),
+    "q1_small": ("q1.hip", "6594bcff4a7b6f83", {"7646 x 256x1024": (138464.3, 7646.0)}),
+    "q1mm": ("q1.hip", "6594bcff4a7b6f83", {"m2": (4307.5, 112.0), "m4": (4329.5, 224.0), "m8": (4397.5, 448.0)}),
     "ternary": ("ternary.hip", "126a8cf5dd046c1e",
-                {"2560x2560": (102223.7, 1200.0), "6912x2560": (137569.2, 1620.0), "2560x6912": (65814.0, 300.0)}),
-    "blockq8": ("blockq8.hip", "f40db311846149b4", {"m1": (26836.1, 192.6), "m16": (27509.4, 3072.0)}),
+                {"2560x2560": (101698.1, 1200.0), "6912x2560": (137148.8, 1620.0), "2560x6912": (65832.9, 300.0)}),
+    "blockq8": ("blockq8.hip", "f40db311846149b4", {"m1": (26849.6, 192.5), "m16": (27505.1, 3072.0)}),
     # per call on the caller's words: prep (split + weight regroup) + gemm
     "sign": ("sign_gemm.hip", "65273486dc365ea0",
              {"prep": (6189.5, 12432.0), "gemm": (20668.0, 8192.0)}),
@@ -69,7 +69,7 @@ _TRAFFIC = {
     "quant": ("quantize.hip", "43e80662c6c5dcbe",
               {"q8_0_decode": (266.5, 136.0), "q8_0_batch_256MiB": (131082.9, 69632.0),
                "int8_planes_decode_step": (488.5 + 480.8, 227.8 + 203.4),
-               "int8_planes_batch_256MiB": (131110.9, 66073.2)}),
+               "int8_planes_batch_256MiB": (131110.9, 66066.3)}),
     # per call: split kernel + merge kernel
     "attention": ("attention.hip", "849b98fd33aa133e",
                   {"kv4096": (16453.1 + 605.0, 1040.0 + 16.0),
@@ -79,8 +79,8 @@ _TRAFFIC = {
 # Hardware MFMA busy fraction (rocprofv3 SQ_VALU_MFMA_BUSY_CYCLES over the
 # dispatch's duration x 1024 SIMDs at 2.4 GHz), for the kernel source measured.
 _MFMA_BUSY = {
-    "sign_gemm_kernel": ("sign_gemm.hip", "65273486dc365ea0", 0.453),
-    "blockq8_mfma_kernel": ("blockq8.hip", "f40db311846149b4", 0.078),
+    "sign_gemm_kernel": ("sign_gemm.hip", "65273486dc365ea0", 0.474),
+    "blockq8_mfma_kernel": ("blockq8.hip", "f40db311846149b4", 0.077),
 }
 
 

@@ -33,16 +33,17 @@ constexpr int kRowsPerWG = 256;
 constexpr int kChunkBlocks = 32;          // blocks whose tables fit in LDS
 constexpr int kTableFloats = kChunkBlocks * 32 * 16;   // 64 KiB
 // A single GEMV of up to this many 256-row blocks takes the one-chain-per-
-// thread kernel (latency); larger ones fill the chip with 256-row blocks.
+// thread kernel (latency); larger ones take the four-chain kernel.
 constexpr int64_t kLatMaxRowBlocks = 64;
 constexpr int64_t kLatWideRows = 8192;
 // While n_act * rows stays within this (about two waves per SIMD in all), a
 // few-row product runs as independent one-chain-per-thread GEMVs, one per
-// column; above it each column runs the 256-row kernel (both re-read the
+// column; above it each column runs the four-chain kernel (both re-read the
 // weights per column, mostly from cache).
+// Up to this many workgroups (half the CUs), a launch takes workgroups of
+// half the rows: 128 instead of 256 on the four-chain kernel, 16 instead of
+// 32 on the one-chain kernel (there only while K is one table chunk).
 constexpr int64_t kLatMaxColumnRows = 16384;
-// Up to this many 256-row workgroups (half the CUs), the per-column launch
-// takes 128-row workgroups instead.
 constexpr int64_t kNarrowMaxWGs = 128;
 // Threads per workgroup of the grouped launch (two per row of a 64-row tile).
 constexpr int kGroupedThreads = 512;
@@ -933,7 +934,7 @@ extern "C" int q1_q8_gemv(const void *bits_plane, const void *scale_plane, const
         }
         return check_launch("q1_q8_gemv");
     }
-    // Each column its own 256-row GEMV (blockIdx.y). Groups of columns that
+    // Each column its own four-chain GEMV (blockIdx.y). Groups of columns that
     // share one read of the weights through LDS tables of several columns
     // (P1's Q1_MM4) measured slower at every n_act from 2 to 32: they halve
     // the independent chains per column group, and these launches are bound
